@@ -1,0 +1,54 @@
+"""Plant plausible mistakes in copies of the oracle and check that the pins
+catch every one of them.  CPU only: each mutant is compiled with gcc into a
+temporary directory and the pin suite runs against it in a subprocess."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "slot_kv_oracle.c")
+
+MUTANTS = {
+    "offset_uses_32bit": ("return row * (uint64_t)kv_dim * (uint64_t)sizeof(float);",
+                          "return (uint32_t)(row * kv_dim * sizeof(float));"),
+    "norm_sum_not_mean": ("sqrt(ss / (double)n + eps)", "sqrt(ss + eps)"),
+    "norm_drops_eps": ("sqrt(ss / (double)n + eps)", "sqrt(ss / (double)n)"),
+    "norm_drops_weight": ("y[i] = (double)x[i] * r * (double)w[i];", "y[i] = (double)x[i] * r;"),
+    "rope_minus_theta": ("x[i] = a * c - b * s;", "x[i] = a * c + b * s;"),
+    "rope_second_sign": ("x[i + half] = b * c + a * s;", "x[i + half] = b * c - a * s;"),
+    "rope_f64_angle": ("double th = (double)ang_f;", "double th = (double)pos * (double)inv_freq[i];"),
+    "rope_pos_plus_one": ("volatile float ang_f = (float)pos * inv_freq[i];",
+                          "volatile float ang_f = (float)(pos + 1) * inv_freq[i];"),
+    "range_exclusive": ("for (uint32_t t = 0; t <= pos; ++t) {\n            const float *vrow",
+                        "for (uint32_t t = 0; t < pos + (pos == 0); ++t) {\n            const float *vrow"),
+    "gqa_modulo": ("const uint32_t j = h / G;", "const uint32_t j = h % n_kv_heads;"),
+    "no_scale": ("sc[t] = (double)scale * dot;", "sc[t] = dot;"),
+    "sink_dropped": ("if (has_sink && sink != -INFINITY) den += exp(sink - m);", ";"),
+    "sink_scaled": ("den += exp(sink - m);", "den += exp((double)scale * sink - m);"),
+    "no_max_subtraction": ("double e = exp(sc[t] - m);", "double e = exp(sc[t]);"),
+    "v_not_verbatim": ("v_written[(size_t)j * D + d] = v_new_row[(size_t)j * D + d];",
+                       "v_written[(size_t)j * D + d] = (float)tmp[d];"),
+    "new_key_unrotated": ("oracle_rope(tmp, inv_freq, pos, D);\n        for",
+                          "for"),
+    "dup_slots_allowed": ("if (slots[c] == slots[b]) return ORACLE_EDUP;", "continue;"),
+    "pos_bound_off_by_one": ("positions[b] >= slot_ctx", "positions[b] > slot_ctx"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor for {name} not found"
+    mut_src = tmp_path / "mutant.c"
+    mut_src.write_text(src.replace(old, new, 1))
+    lib = oracle.build(force=True, src=str(mut_src), out=str(tmp_path / "libmutant.so"))
+    env = dict(os.environ, SLOT_KV_ORACLE_LIB=lib)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
