@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Benchmark of the batched slot-KV decode-attention step on one MI355X.
+
+One "step" is one pass of the whole hot path over one batch: host validation
+and staging, the fused norm + RoPE + KV-write + split-K attention kernel, and
+the merge of split rows (``slot_decode_attn``), for every layer of the
+workload.  Default workload: 1 layer, 32 query / 8 kv heads of 128, 64 slots
+x 4096 positions, B = 64 rows at seeded positions U{1..4095}.
+
+Prints ONE JSON line on stdout:
+  value        rows/s (B / step time), inputs resident in HBM
+  kv_gbps      algorithmic KV bytes per step / step time, where the KV bytes
+               are sum_b (pos_b + 1) * kv_dim * 4 for K and again for V
+  roofline     the fused kernel's achieved GB/s (KV bytes per launch / mean
+               launch time from HIP events on the launch stream) vs 8 TB/s,
+               with the HBM traffic measured by rocprofv3 counters when the
+               committed counter record matches the current kernel source
+  cpu_baseline the CPU oracle on the host cores over the same rows
+
+    python bench.py [--steps K] [--warmup W] [--workload mid]
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn rows/sec and achieved KV HBM GB/s (% of peak) at B=64, ctx 4096"
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "sequence_slot_kv_amd", "csrc", "slot_kv_kernels.hip")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the fused kernel from the committed rocprofv3
+    counter record, or None when there is none for this workload or the
+    kernel source changed since it was taken."""
+    try:
+        rec = json.load(open(TRAFFIC_RECORD))
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload)
+    if not entry or entry.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, hist, target_cpu_s: float = 12.0):
+    import oracle
+    threads = max(1, min(len(os.sched_getaffinity(0)), 16))
+    rows = list(range(w.B))
+
+    def one(bi):
+        L, li = w.layers[0], w.inputs[0]
+        hk, hv = hist[bi]
+        oracle.decode_row(L, int(w.positions[bi]), li.q[bi], li.k_new[bi], li.v_new[bi], hk, hv)
+
+    done, t0 = 0, time.perf_counter()
+    with cf.ThreadPoolExecutor(threads) as ex:
+        while True:
+            list(ex.map(one, rows))
+            done += len(rows)
+            wall = time.perf_counter() - t0
+            if wall * threads >= target_cpu_s or done >= 40 * len(rows):
+                break
+    rows_per_s = done / wall
+    return {"value": rows_per_s, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": f"all {w.B} rows of the step (layer 0), {done // w.B} passes, "
+                      f"{wall:.1f} s wall on {threads} threads",
+            "kv_gbps": rows_per_s / w.B * w.kv_bytes(0) / 1e9}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mid",
+                    choices=["tiny", "mid", "long", "many", "layer_stack"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the step shards by "
+              "slot with no exchange, so more GPUs are not exercised here", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from sequence_slot_kv_amd import binding as b
+    from sequence_slot_kv_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    w = wl.WORKLOADS[args.workload]()
+    n_layers = len(w.layers)
+    log(f"[bench] workload {w.name}: B={w.B} n_slots={w.n_slots} slot_ctx={w.slot_ctx} "
+        f"layers={n_layers} kv_bytes/step={w.kv_bytes()}")
+
+    kv = b.SlotKV()
+    kv.alloc(w.n_slots, w.slot_ctx, w.kv_dims)
+    for l, P in enumerate(w.layers):
+        kv.set_layer(l, P)
+    for l, P in enumerate(w.layers):  # N(0,1) history from seeded device generators
+        for which in (0, 1):
+            g = torch.Generator(device="cuda")
+            g.manual_seed(wl.device_history_seed(w, l, which))
+            for s in range(w.n_slots):
+                rows = torch.randn((w.slot_ctx, P.kv_dim), generator=g, device="cuda")
+                if which == 0:
+                    kv.write_rows(l, s, 0, k_src=rows)
+                else:
+                    kv.write_rows(l, s, 0, v_src=rows)
+    torch.cuda.synchronize()
+    log("[bench] history filled")
+
+    hist = None
+    if not args.no_cpu_baseline:  # snapshot layer-0 history before any step runs
+        hist = {}
+        for bi in range(w.B):
+            p = int(w.positions[bi])
+            if p == 0:
+                z = np.zeros((0, w.layers[0].kv_dim), np.float32)
+                hist[bi] = (z, z)
+            else:
+                k, v = kv.read_rows(0, int(w.slots[bi]), 0, p)
+                hist[bi] = (k.cpu().numpy(), v.cpu().numpy())
+
+    ins = [tuple(torch.from_numpy(a).cuda() for a in (li.q, li.k_new, li.v_new)) for li in w.inputs]
+    outs = [torch.empty_like(x[0]) for x in ins]
+    positions, slots = w.positions, w.slots
+
+    def step():
+        for l in range(n_layers):
+            q, kn, vn = ins[l]
+            kv.decode_attn(l, q, kn, vn, positions, slots, out=outs[l])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    rc = b.slot_kv_profile_begin(kv.h)
+    assert rc == 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    rc, kernel_ms, launches = b.slot_kv_profile_end(kv.h)
+    assert rc == 0 and launches == args.steps * n_layers
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    kv_bytes = w.kv_bytes()
+    rows_per_s = w.B / (ms_per_step / 1e3)
+    kv_gbps = kv_bytes / (ms_per_step / 1e3) / 1e9
+    mean_launch_ms = kernel_ms / launches
+    bytes_per_launch = kv_bytes / n_layers
+    achieved = bytes_per_launch / (mean_launch_ms / 1e3) / 1e9
+    traffic = measured_traffic(w.name)
+    log(f"[bench] {ms_per_step * 1e3:.1f} us/step, fused kernel {mean_launch_ms * 1e3:.1f} us/launch, "
+        f"{achieved:.0f} GB/s in-kernel")
+
+    cpu = None
+    if hist is not None:
+        log("[bench] timing the CPU oracle")
+        cpu = cpu_baseline(w, hist)
+
+    res = {
+        "metric": METRIC, "value": rows_per_s, "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "n_slots": w.n_slots, "slot_ctx": w.slot_ctx,
+                   "layers": n_layers, "n_heads": w.layers[0].n_heads,
+                   "n_kv_heads": w.layers[0].n_kv_heads,
+                   "head_dims": sorted({L.head_dim for L in w.layers}), "seed": w.seed,
+                   "chunk_keys": b.slot_kv_chunk_keys()},
+        "kv_bytes_per_step": kv_bytes, "kv_gbps": kv_gbps,
+        "kv_pct_of_hbm_peak": 100.0 * kv_gbps / HBM_PEAK_GBPS,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "kernel": "decode_attn_kernel", "kernel_us": mean_launch_ms * 1e3,
+                     "algorithmic_bytes_per_launch": bytes_per_launch},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    kv.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,177 @@
+/*
+ * slot_kv.h -- C ABI of the slot-indexed KV cache and its batched decode step
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow two pages of the ZINC engine documentation:
+ *   "Forward Cuda Gemma" (Zig API of ForwardGemma): sections decodeBatch,
+ *       allocSlotKv, slotKvOffsetBytes, slotKvSmoke;
+ *   "Forward Cuda" (Zig API of ForwardCuda): sections on init (upload of the
+ *       inv_freq table and the sinks, zeroed KV cache), the slot K/V byte
+ *       offset, and the reset of a reused slot on admit.
+ *
+ * Conventions shared by every entry point
+ *   - Status codes: 0 on success, a negative SLOT_KV_E* value on failure;
+ *     slot_kv_strerror() names them.  Every argument is validated before any
+ *     device work is enqueued: a call that fails writes nothing.
+ *   - "device" pointers are HIP device allocations (for example the data
+ *     pointer of a torch tensor on the GPU); "host" pointers are ordinary
+ *     process memory, read before the call returns.
+ *   - All floating-point data is IEEE float32, C-contiguous, row-major.
+ *   - A handle is not thread-safe.  Calls that enqueue work (decode, row
+ *     copies) are asynchronous on the stream passed in; a handle keeps one
+ *     set of device scratch buffers, so two calls on one handle that run
+ *     concurrently on different streams race.  Serialise them on one stream
+ *     (or synchronise between them).
+ *   - The handle binds to the HIP device that is current when
+ *     slot_kv_alloc() is called.
+ */
+#ifndef SLOT_KV_H
+#define SLOT_KV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SLOT_KV_OK 0
+#define SLOT_KV_EINVAL (-1)    /* bad argument, unconfigured layer, shape mismatch  */
+#define SLOT_KV_ERANGE (-2)    /* slot >= n_slots or pos >= slot_ctx                 */
+#define SLOT_KV_ENOTALLOC (-3) /* the slot KV has not been allocated                 */
+#define SLOT_KV_ENOMEM (-4)    /* a device or pinned-host allocation failed          */
+#define SLOT_KV_EDUP (-5)      /* one slot named by two rows of a batch              */
+#define SLOT_KV_EDEVICE (-6)   /* HIP runtime or launch error                        */
+
+typedef struct slot_kv slot_kv; /* opaque; owns all slot KV device memory */
+
+/* Create an empty handle (no device memory yet).  *out receives it.
+ * Makes no HIP call.  Returns SLOT_KV_EINVAL if out is NULL. */
+int slot_kv_create(slot_kv **out);
+
+/* Free every device and host allocation of the handle, then the handle.
+ * NULL is accepted.  Synchronises the device first. */
+void slot_kv_destroy(slot_kv *h);
+
+/* "Forward Cuda Gemma", allocSlotKv; "Forward Cuda", allocation of the
+ * per-sequence slot state.
+ * Allocates, per layer L < n_layers, one K and one V buffer of
+ * n_slots * slot_ctx * kv_dims[L] floats each, laid out [slot][pos][kv_dim],
+ * and fills them with zeros.  kv_dims is a host array of n_layers counts of
+ * floats per KV row.  Idempotent: any previous allocation of this handle is
+ * freed first (layer configurations are dropped with it).
+ * Errors: EINVAL (zero sizes, NULL kv_dims, size overflow), ENOMEM, EDEVICE. */
+int slot_kv_alloc(slot_kv *h, uint32_t n_slots, uint32_t slot_ctx,
+                  const uint32_t *kv_dims, uint32_t n_layers);
+
+/* "Forward Cuda", init: upload of inv_freq and sinks.
+ * Configures attention layer `layer`: n_heads query heads and n_kv_heads KV
+ * heads of head_dim floats (n_kv_heads * head_dim must equal kv_dims[layer];
+ * n_heads must be a multiple of n_kv_heads; head_dim one of 64, 128, 256;
+ * n_heads / n_kv_heads one of 1, 2, 4, 8).
+ * Host arrays, copied to the device: q_norm_w[head_dim] and k_norm_w[head_dim]
+ * (RMSNorm weights shared by all query heads, resp. all key heads),
+ * inv_freq[head_dim/2] (RoPE frequencies), sinks[n_heads] (one extra softmax
+ * logit per query head; NULL for none).  eps is the RMSNorm epsilon and
+ * scale multiplies q.k (not the sink).
+ * Errors: ENOTALLOC, EINVAL, EDEVICE. */
+int slot_kv_set_layer(slot_kv *h, uint32_t layer, uint32_t n_heads,
+                      uint32_t n_kv_heads, uint32_t head_dim,
+                      const float *q_norm_w, const float *k_norm_w,
+                      const float *inv_freq, const float *sinks, float eps,
+                      float scale);
+
+/* "Forward Cuda Gemma", slotKvOffsetBytes; "Forward Cuda", slot K/V offset.
+ * *out_bytes = (slot * slot_ctx + pos) * kv_dims[layer] * 4, in 64 bits: the
+ * byte offset of the row (slot, pos) inside layer `layer`'s K buffer (the V
+ * buffer uses the same offset).  Errors: ENOTALLOC, EINVAL (layer or
+ * out_bytes), ERANGE (slot or pos out of range). */
+int slot_kv_offset_bytes(const slot_kv *h, uint32_t layer, uint32_t slot,
+                         uint32_t pos, uint64_t *out_bytes);
+
+/* "Forward Cuda", reset of a reused slot on admit.
+ * The attention slot KV needs no clearing: it is indexed by position, each
+ * sequence overwrites from position 0 and reads only what it wrote.  So this
+ * validates `slot` and does nothing else.  Returns OK when nothing is
+ * allocated (no-op), ERANGE when slot >= n_slots. */
+int slot_reset(slot_kv *h, uint32_t slot);
+
+/* "Forward Cuda Gemma", decodeBatch (its attention part).
+ * Advances B independent sequences by one token each.  Row b uses its own
+ * slot slots[b] at its own position positions[b]:
+ *   1. RMSNorm each query head of q[b] (weights q_norm_w) and each key head
+ *      of k_new[b] (weights k_norm_w), then rotate both with RoPE at
+ *      positions[b] (pairs (i, i + head_dim/2), angle float(pos)*inv_freq[i]);
+ *   2. store the rotated key row and v_new[b] unchanged at byte offset
+ *      (slots[b]*slot_ctx + positions[b]) * kv_dim * 4 of the layer's K / V;
+ *   3. out[b] = causal softmax attention of each query head h over keys
+ *      0..positions[b] (inclusive) of that slot, against kv head
+ *      h / (n_heads / n_kv_heads), scores scale*q.k, plus the head's sink
+ *      logit in the denominator when sinks are set.
+ * Requires history rows 0..positions[b]-1 of the slot to hold that sequence's
+ * keys and values (written by earlier calls or slot_kv_write_rows).
+ *   q      device [B][n_heads*head_dim]        k_new, v_new  device [B][kv_dim]
+ *   out    device [B][n_heads*head_dim]; must not overlap q, k_new or v_new
+ *   positions, slots  host [B]; copied before the call returns
+ *   stream hipStream_t (NULL = the null stream)
+ * B == 0 is a no-op.  Errors: ENOTALLOC, EINVAL (layer unconfigured, NULL
+ * pointer), ERANGE (slots[b] >= n_slots or positions[b] >= slot_ctx), EDUP
+ * (a slot repeated in the batch), ENOMEM, EDEVICE (launch failure).  Faults
+ * inside the kernels surface at the caller's next synchronisation. */
+int slot_decode_attn(slot_kv *h, uint32_t layer, const float *q,
+                     const float *k_new, const float *v_new,
+                     const uint32_t *positions, const uint32_t *slots,
+                     uint32_t B, float *out, void *stream);
+
+/* Device pointers of layer `layer`'s K and V buffers ([n_slots][slot_ctx]
+ * [kv_dim] floats each; owned by the handle, valid until the next
+ * slot_kv_alloc or slot_kv_destroy).  Errors: ENOTALLOC, EINVAL. */
+int slot_kv_layer_ptrs(const slot_kv *h, uint32_t layer, float **k, float **v);
+
+/* Copy n_rows consecutive K and V rows (kv_dim floats each) from device
+ * buffers k_src / v_src into slot `slot` at positions pos0 .. pos0+n_rows-1
+ * of layer `layer` (a prefill by copy; either source may be NULL to skip
+ * it).  Asynchronous on `stream`.  Errors: ENOTALLOC, EINVAL, ERANGE, EDEVICE. */
+int slot_kv_write_rows(slot_kv *h, uint32_t layer, uint32_t slot, uint32_t pos0,
+                       uint32_t n_rows, const float *k_src, const float *v_src,
+                       void *stream);
+
+/* The reverse copy: rows pos0 .. pos0+n_rows-1 of slot `slot` into device
+ * buffers k_dst / v_dst (either may be NULL).  Same errors. */
+int slot_kv_read_rows(const slot_kv *h, uint32_t layer, uint32_t slot,
+                      uint32_t pos0, uint32_t n_rows, float *k_dst, float *v_dst,
+                      void *stream);
+
+/* "Forward Cuda Gemma", decodeBatch preconditions, checked on the host only
+ * (no device access, usable without a GPU): every slots[b] < n_slots, every
+ * positions[b] < slot_ctx, no slot twice.  On success, when the pointers are
+ * non-NULL, *n_items receives the number of split-K work items the decode
+ * step launches per kv head (a row at position p is cut into
+ * ceil((p+1)/chunk_keys) chunks of chunk_keys keys) and *n_split_rows the
+ * number of rows cut into more than one chunk.  Errors: EINVAL, ERANGE, EDUP. */
+int slot_kv_check_batch(uint32_t n_slots, uint32_t slot_ctx,
+                        const uint32_t *positions, const uint32_t *slots,
+                        uint32_t B, uint32_t chunk_keys, uint32_t *n_items,
+                        uint32_t *n_split_rows);
+
+/* Keys per split-K chunk used by slot_decode_attn (a build constant; chunk
+ * boundaries depend only on each row's position, never on the batch). */
+uint32_t slot_kv_chunk_keys(void);
+
+/* Profiling of the fused decode kernel.  Between slot_kv_profile_begin and
+ * slot_kv_profile_end the handle records a HIP event pair on the call's
+ * stream immediately around each launch of the fused split-K decode kernel
+ * (the partial-merge kernel, when a batch needs it, runs after the second
+ * event).  slot_kv_profile_end waits for the recorded launches and returns
+ * their summed duration in milliseconds and their count (either pointer may
+ * be NULL), then stops recording.  Errors: EINVAL, ENOMEM, EDEVICE. */
+int slot_kv_profile_begin(slot_kv *h);
+int slot_kv_profile_end(slot_kv *h, double *kernel_ms, uint32_t *launches);
+
+/* Static text for a status code. */
+const char *slot_kv_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SLOT_KV_H */

@@ -1,0 +1,471 @@
+// slot_kv_api.hip -- the C ABI of include/slot_kv.h: handle, slot-KV
+// allocator, 64-bit offsets, host validation, per-call staging of the row
+// table and work list, and the kernel launches.
+//
+// "Forward Cuda Gemma": allocSlotKv (idempotent, frees first), slotKvOffsetBytes
+// ((slot*slot_ctx + pos)*kv_dim*4), decodeBatch (preconditions, per-row
+// slot and position); "Forward Cuda": init (zeroed cache, inv_freq and sinks
+// uploaded), reset of a reused slot (nothing to clear for attention KV).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "slot_kv.h"
+#include "slot_kv_internal.h"
+
+using slotkv::AttnParams;
+using slotkv::Plan;
+using slotkv::RowInfo;
+using slotkv::WorkItem;
+
+namespace {
+
+constexpr int kStages = 16;  // staging ring depth (calls in flight per handle)
+
+struct LayerState {
+  uint32_t kv_dim = 0;
+  float* k = nullptr;
+  float* v = nullptr;
+  bool configured = false;
+  uint32_t n_heads = 0, n_kv_heads = 0, head_dim = 0;
+  float* params = nullptr;  // q_norm_w[D] | k_norm_w[D] | inv_freq[D/2] | sinks[n_heads]
+  bool has_sinks = false;
+  float eps = 0.f, scale = 0.f;
+};
+
+struct Stage {
+  void* host = nullptr;   // pinned
+  void* dev = nullptr;
+  size_t cap = 0;
+  hipEvent_t done = nullptr;
+  bool used = false;
+};
+
+}  // namespace
+
+struct slot_kv {
+  int device = -1;
+  uint32_t n_slots = 0, slot_ctx = 0;
+  std::vector<LayerState> layers;
+  Stage stages[kStages];
+  unsigned next_stage = 0;
+  float* part = nullptr;  // partial results (acc then m/l)
+  size_t part_cap = 0;    // floats
+  std::vector<RowInfo> rows;
+  std::vector<WorkItem> items;
+  bool profiling = false;
+  std::vector<hipEvent_t> prof_events;  // start/end pairs
+  size_t prof_used = 0;                 // pairs recorded since profile_begin
+  bool allocated() const { return !layers.empty(); }
+};
+
+namespace {
+
+void free_layers(slot_kv* h) {
+  for (auto& L : h->layers) {
+    if (L.k) (void)hipFree(L.k);
+    if (L.v) (void)hipFree(L.v);
+    if (L.params) (void)hipFree(L.params);
+  }
+  h->layers.clear();
+}
+
+void free_scratch(slot_kv* h) {
+  for (auto& s : h->stages) {
+    if (s.host) (void)hipHostFree(s.host);
+    if (s.dev) (void)hipFree(s.dev);
+    if (s.done) (void)hipEventDestroy(s.done);
+    s = Stage{};
+  }
+  if (h->part) (void)hipFree(h->part);
+  h->part = nullptr;
+  h->part_cap = 0;
+  for (hipEvent_t e : h->prof_events) (void)hipEventDestroy(e);
+  h->prof_events.clear();
+  h->prof_used = 0;
+  h->profiling = false;
+}
+
+int check_layer(const slot_kv* h, uint32_t layer) {
+  if (!h) return SLOT_KV_EINVAL;
+  if (!h->allocated()) return SLOT_KV_ENOTALLOC;
+  if (layer >= h->layers.size()) return SLOT_KV_EINVAL;
+  return SLOT_KV_OK;
+}
+
+// Make sure the ring stage has `bytes` of pinned and device memory and that
+// the device is done with its previous contents.
+int prepare_stage(Stage& s, size_t bytes) {
+  if (s.used) {
+    if (hipEventSynchronize(s.done) != hipSuccess) return SLOT_KV_EDEVICE;
+  }
+  if (!s.done) {
+    if (hipEventCreateWithFlags(&s.done, hipEventDisableTiming) != hipSuccess)
+      return SLOT_KV_EDEVICE;
+  }
+  if (s.cap < bytes) {
+    size_t cap = 4096;
+    while (cap < bytes) cap *= 2;
+    if (s.host) (void)hipHostFree(s.host);
+    if (s.dev) (void)hipFree(s.dev);
+    s.host = s.dev = nullptr;
+    s.cap = 0;
+    if (hipHostMalloc(&s.host, cap, hipHostMallocDefault) != hipSuccess) {
+      s.host = nullptr;
+      return SLOT_KV_ENOMEM;
+    }
+    if (hipMalloc(&s.dev, cap) != hipSuccess) {
+      (void)hipHostFree(s.host);
+      s.host = s.dev = nullptr;
+      return SLOT_KV_ENOMEM;
+    }
+    s.cap = cap;
+  }
+  return SLOT_KV_OK;
+}
+
+int ensure_partials(slot_kv* h, size_t floats) {
+  if (h->part_cap >= floats) return SLOT_KV_OK;
+  // Kernels of earlier calls may still read the old buffer.
+  if (hipDeviceSynchronize() != hipSuccess) return SLOT_KV_EDEVICE;
+  if (h->part) (void)hipFree(h->part);
+  h->part = nullptr;
+  h->part_cap = 0;
+  size_t cap = 1 << 20;
+  while (cap < floats) cap *= 2;
+  if (hipMalloc(&h->part, cap * sizeof(float)) != hipSuccess) {
+    h->part = nullptr;
+    return SLOT_KV_ENOMEM;
+  }
+  h->part_cap = cap;
+  return SLOT_KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int slot_kv_create(slot_kv** out) {
+  if (!out) return SLOT_KV_EINVAL;
+  *out = new (std::nothrow) slot_kv();
+  return *out ? SLOT_KV_OK : SLOT_KV_ENOMEM;
+}
+
+void slot_kv_destroy(slot_kv* h) {
+  if (!h) return;
+  if (h->device >= 0) (void)hipDeviceSynchronize();
+  free_layers(h);
+  free_scratch(h);
+  delete h;
+}
+
+int slot_kv_alloc(slot_kv* h, uint32_t n_slots, uint32_t slot_ctx, const uint32_t* kv_dims,
+                  uint32_t n_layers) {
+  if (!h || !kv_dims || n_slots == 0 || slot_ctx == 0 || n_layers == 0) return SLOT_KV_EINVAL;
+  for (uint32_t L = 0; L < n_layers; ++L) {
+    if (kv_dims[L] == 0) return SLOT_KV_EINVAL;
+    // bytes = n_slots*slot_ctx*kv_dim*4 must fit 64 bits (it always does for
+    // 32-bit factors below 2^62 / 4); rows must also fit the u32 kernel math
+    // of positions, which they do by type.
+  }
+  // Idempotent: drop any earlier allocation (and its layer configurations).
+  if (h->device >= 0) (void)hipDeviceSynchronize();
+  free_layers(h);
+  free_scratch(h);
+  h->n_slots = h->slot_ctx = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SLOT_KV_EDEVICE;
+  h->device = dev;
+  std::vector<LayerState> layers(n_layers);
+  const uint64_t rows = static_cast<uint64_t>(n_slots) * slot_ctx;
+  for (uint32_t L = 0; L < n_layers; ++L) {
+    const uint64_t bytes = rows * kv_dims[L] * sizeof(float);
+    layers[L].kv_dim = kv_dims[L];
+    void* k = nullptr;
+    void* v = nullptr;
+    if (hipMalloc(&k, bytes) != hipSuccess) k = nullptr;
+    if (k && hipMalloc(&v, bytes) != hipSuccess) v = nullptr;
+    layers[L].k = static_cast<float*>(k);
+    layers[L].v = static_cast<float*>(v);
+    if (!k || !v) {
+      h->layers.swap(layers);
+      free_layers(h);
+      (void)hipGetLastError();
+      return SLOT_KV_ENOMEM;
+    }
+    // "Forward Cuda", init: the KV cache starts zeroed.
+    if (hipMemset(k, 0, bytes) != hipSuccess || hipMemset(v, 0, bytes) != hipSuccess) {
+      h->layers.swap(layers);
+      free_layers(h);
+      return SLOT_KV_EDEVICE;
+    }
+  }
+  if (hipDeviceSynchronize() != hipSuccess) {
+    h->layers.swap(layers);
+    free_layers(h);
+    return SLOT_KV_EDEVICE;
+  }
+  h->layers.swap(layers);
+  h->n_slots = n_slots;
+  h->slot_ctx = slot_ctx;
+  return SLOT_KV_OK;
+}
+
+int slot_kv_set_layer(slot_kv* h, uint32_t layer, uint32_t n_heads, uint32_t n_kv_heads,
+                      uint32_t head_dim, const float* q_norm_w, const float* k_norm_w,
+                      const float* inv_freq, const float* sinks, float eps, float scale) {
+  int rc = check_layer(h, layer);
+  if (rc) return rc;
+  LayerState& L = h->layers[layer];
+  if (!q_norm_w || !k_norm_w || !inv_freq) return SLOT_KV_EINVAL;
+  if (n_heads == 0 || n_kv_heads == 0 || head_dim == 0 || n_heads % n_kv_heads != 0)
+    return SLOT_KV_EINVAL;
+  if (static_cast<uint64_t>(n_kv_heads) * head_dim != L.kv_dim) return SLOT_KV_EINVAL;
+  if (!slotkv::decode_shape_supported(head_dim, n_heads / n_kv_heads)) return SLOT_KV_EINVAL;
+  if (!std::isfinite(eps) || eps < 0.f || !std::isfinite(scale)) return SLOT_KV_EINVAL;
+  const size_t D = head_dim;
+  const size_t n = 2 * D + D / 2 + n_heads;
+  std::vector<float> host(n, 0.f);
+  std::memcpy(host.data(), q_norm_w, D * sizeof(float));
+  std::memcpy(host.data() + D, k_norm_w, D * sizeof(float));
+  std::memcpy(host.data() + 2 * D, inv_freq, D / 2 * sizeof(float));
+  if (sinks) std::memcpy(host.data() + 2 * D + D / 2, sinks, n_heads * sizeof(float));
+  float* dev = nullptr;
+  if (L.params) {
+    if (hipDeviceSynchronize() != hipSuccess) return SLOT_KV_EDEVICE;
+    (void)hipFree(L.params);
+    L.params = nullptr;
+    L.configured = false;
+  }
+  if (hipMalloc(&dev, n * sizeof(float)) != hipSuccess) return SLOT_KV_ENOMEM;
+  if (hipMemcpy(dev, host.data(), n * sizeof(float), hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(dev);
+    return SLOT_KV_EDEVICE;
+  }
+  L.params = dev;
+  L.n_heads = n_heads;
+  L.n_kv_heads = n_kv_heads;
+  L.head_dim = head_dim;
+  L.has_sinks = sinks != nullptr;
+  L.eps = eps;
+  L.scale = scale;
+  L.configured = true;
+  return SLOT_KV_OK;
+}
+
+int slot_kv_offset_bytes(const slot_kv* h, uint32_t layer, uint32_t slot, uint32_t pos,
+                         uint64_t* out_bytes) {
+  int rc = check_layer(h, layer);
+  if (rc) return rc;
+  if (!out_bytes) return SLOT_KV_EINVAL;
+  if (slot >= h->n_slots || pos >= h->slot_ctx) return SLOT_KV_ERANGE;
+  *out_bytes = (static_cast<uint64_t>(slot) * h->slot_ctx + pos) *
+               static_cast<uint64_t>(h->layers[layer].kv_dim) * sizeof(float);
+  return SLOT_KV_OK;
+}
+
+int slot_reset(slot_kv* h, uint32_t slot) {
+  if (!h) return SLOT_KV_EINVAL;
+  if (!h->allocated()) return SLOT_KV_OK;  // no-op when nothing is allocated
+  return slot < h->n_slots ? SLOT_KV_OK : SLOT_KV_ERANGE;
+}
+
+int slot_kv_check_batch(uint32_t n_slots, uint32_t slot_ctx, const uint32_t* positions,
+                        const uint32_t* slots, uint32_t B, uint32_t chunk_keys,
+                        uint32_t* n_items, uint32_t* n_split_rows) {
+  if (chunk_keys == 0) return SLOT_KV_EINVAL;
+  int rc = slotkv::check_batch(n_slots, slot_ctx, positions, slots, B);
+  if (rc) return rc;
+  uint32_t items = 0, split = 0;
+  for (uint32_t b = 0; b < B; ++b) {
+    const uint32_t nc = static_cast<uint32_t>((uint64_t(positions[b]) + chunk_keys) / chunk_keys);
+    items += nc;
+    split += nc > 1;
+  }
+  if (n_items) *n_items = items;
+  if (n_split_rows) *n_split_rows = split;
+  return SLOT_KV_OK;
+}
+
+uint32_t slot_kv_chunk_keys(void) { return SLOT_KV_CHUNK; }
+
+int slot_decode_attn(slot_kv* h, uint32_t layer, const float* q, const float* k_new,
+                     const float* v_new, const uint32_t* positions, const uint32_t* slots,
+                     uint32_t B, float* out, void* stream) {
+  int rc = check_layer(h, layer);
+  if (rc) return rc;
+  LayerState& L = h->layers[layer];
+  if (!L.configured) return SLOT_KV_EINVAL;
+  if (B == 0) return SLOT_KV_OK;
+  if (!q || !k_new || !v_new || !out) return SLOT_KV_EINVAL;
+  rc = slotkv::check_batch(h->n_slots, h->slot_ctx, positions, slots, B);
+  if (rc) return rc;
+  const uint32_t C = SLOT_KV_CHUNK;
+  const uint64_t n_items64 = [&] {
+    uint64_t n = 0;
+    for (uint32_t b = 0; b < B; ++b) n += (uint64_t(positions[b]) + C) / C;
+    return n;
+  }();
+  if (n_items64 * L.n_kv_heads >= (uint64_t(1) << 31)) return SLOT_KV_EINVAL;
+
+  h->rows.resize(B);
+  h->items.resize(n_items64);
+  const Plan plan = slotkv::build_plan(positions, slots, B, C, h->rows.data(), h->items.data());
+
+  const size_t D = L.head_dim;
+  if (plan.n_parts) {
+    rc = ensure_partials(h, static_cast<size_t>(plan.n_parts) * L.n_heads * (D + 2));
+    if (rc) return rc;
+  }
+  const size_t rows_bytes = B * sizeof(RowInfo);
+  const size_t bytes = rows_bytes + plan.n_items * sizeof(WorkItem);
+  Stage& st = h->stages[h->next_stage];
+  rc = prepare_stage(st, bytes);
+  if (rc) return rc;
+  h->next_stage = (h->next_stage + 1) % kStages;
+  std::memcpy(st.host, h->rows.data(), rows_bytes);
+  std::memcpy(static_cast<char*>(st.host) + rows_bytes, h->items.data(),
+              plan.n_items * sizeof(WorkItem));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(st.dev, st.host, bytes, hipMemcpyHostToDevice, s) != hipSuccess)
+    return SLOT_KV_EDEVICE;
+
+  AttnParams p{};
+  p.k_cache = L.k;
+  p.v_cache = L.v;
+  p.q = q;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.out = out;
+  p.part_acc = h->part;
+  p.part_ml = h->part ? h->part + static_cast<size_t>(plan.n_parts) * L.n_heads * D : nullptr;
+  p.rows = static_cast<const RowInfo*>(st.dev);
+  p.items = reinterpret_cast<const WorkItem*>(static_cast<const char*>(st.dev) + rows_bytes);
+  p.q_norm_w = L.params;
+  p.k_norm_w = L.params + D;
+  p.inv_freq = L.params + 2 * D;
+  p.sinks = L.has_sinks ? L.params + 2 * D + D / 2 : nullptr;
+  p.slot_stride = static_cast<uint64_t>(h->slot_ctx) * L.kv_dim;
+  p.kv_dim = L.kv_dim;
+  p.n_kv_heads = L.n_kv_heads;
+  p.n_heads = L.n_heads;
+  p.n_waves = plan.n_items * L.n_kv_heads;
+  p.chunk = C;
+  p.B = B;
+  p.eps = L.eps;
+  p.qk_scale_log2 = L.scale * 1.4426950408889634f;
+  hipEvent_t ev_end = nullptr;
+  if (h->profiling) {
+    if (h->prof_events.size() < 2 * (h->prof_used + 1)) {
+      hipEvent_t a = nullptr, b = nullptr;
+      if (hipEventCreate(&a) != hipSuccess) return SLOT_KV_EDEVICE;
+      if (hipEventCreate(&b) != hipSuccess) {
+        (void)hipEventDestroy(a);
+        return SLOT_KV_EDEVICE;
+      }
+      h->prof_events.push_back(a);
+      h->prof_events.push_back(b);
+    }
+    if (hipEventRecord(h->prof_events[2 * h->prof_used], s) != hipSuccess) return SLOT_KV_EDEVICE;
+    ev_end = h->prof_events[2 * h->prof_used + 1];
+    ++h->prof_used;
+  }
+  const int e = slotkv::launch_decode(p, L.head_dim, L.n_heads / L.n_kv_heads,
+                                      plan.n_split_rows > 0, stream, ev_end);
+  // The stage may be reused once everything enqueued so far has run.
+  const bool rec = hipEventRecord(st.done, s) == hipSuccess;
+  st.used = rec;
+  if (e != hipSuccess || !rec) return SLOT_KV_EDEVICE;
+  return SLOT_KV_OK;
+}
+
+int slot_kv_layer_ptrs(const slot_kv* h, uint32_t layer, float** k, float** v) {
+  int rc = check_layer(h, layer);
+  if (rc) return rc;
+  if (k) *k = h->layers[layer].k;
+  if (v) *v = h->layers[layer].v;
+  return SLOT_KV_OK;
+}
+
+static int copy_rows(const slot_kv* h, uint32_t layer, uint32_t slot, uint32_t pos0,
+                     uint32_t n_rows, float* dst_k, const float* src_k, float* dst_v,
+                     const float* src_v, bool into_cache, void* stream) {
+  int rc = check_layer(h, layer);
+  if (rc) return rc;
+  if (slot >= h->n_slots || pos0 >= h->slot_ctx ||
+      static_cast<uint64_t>(pos0) + n_rows > h->slot_ctx)
+    return SLOT_KV_ERANGE;
+  if (n_rows == 0) return SLOT_KV_OK;
+  const LayerState& L = h->layers[layer];
+  const uint64_t off = (static_cast<uint64_t>(slot) * h->slot_ctx + pos0) * L.kv_dim;
+  const size_t bytes = static_cast<size_t>(n_rows) * L.kv_dim * sizeof(float);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int which = 0; which < 2; ++which) {
+    float* cache = which == 0 ? L.k : L.v;
+    const void* src = into_cache ? (which == 0 ? static_cast<const void*>(src_k)
+                                               : static_cast<const void*>(src_v))
+                                 : cache + off;
+    void* dst = into_cache ? static_cast<void*>(cache + off)
+                           : (which == 0 ? static_cast<void*>(dst_k) : static_cast<void*>(dst_v));
+    if (!(into_cache ? src : dst)) continue;  // that side skipped
+    if (hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
+      return SLOT_KV_EDEVICE;
+  }
+  return SLOT_KV_OK;
+}
+
+int slot_kv_write_rows(slot_kv* h, uint32_t layer, uint32_t slot, uint32_t pos0, uint32_t n_rows,
+                       const float* k_src, const float* v_src, void* stream) {
+  return copy_rows(h, layer, slot, pos0, n_rows, nullptr, k_src, nullptr, v_src, true, stream);
+}
+
+int slot_kv_read_rows(const slot_kv* h, uint32_t layer, uint32_t slot, uint32_t pos0,
+                      uint32_t n_rows, float* k_dst, float* v_dst, void* stream) {
+  return copy_rows(h, layer, slot, pos0, n_rows, k_dst, nullptr, v_dst, nullptr, false, stream);
+}
+
+int slot_kv_profile_begin(slot_kv* h) {
+  if (!h) return SLOT_KV_EINVAL;
+  h->profiling = true;
+  h->prof_used = 0;
+  return SLOT_KV_OK;
+}
+
+int slot_kv_profile_end(slot_kv* h, double* kernel_ms, uint32_t* launches) {
+  if (!h) return SLOT_KV_EINVAL;
+  double total = 0.0;
+  int rc = SLOT_KV_OK;
+  for (size_t i = 0; i < h->prof_used; ++i) {
+    float ms = 0.f;
+    if (hipEventSynchronize(h->prof_events[2 * i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&ms, h->prof_events[2 * i], h->prof_events[2 * i + 1]) != hipSuccess) {
+      rc = SLOT_KV_EDEVICE;
+      break;
+    }
+    total += ms;
+  }
+  if (kernel_ms) *kernel_ms = total;
+  if (launches) *launches = static_cast<uint32_t>(h->prof_used);
+  h->profiling = false;
+  h->prof_used = 0;
+  return rc;
+}
+
+const char* slot_kv_strerror(int status) {
+  switch (status) {
+    case SLOT_KV_OK: return "ok";
+    case SLOT_KV_EINVAL: return "invalid argument or unconfigured layer";
+    case SLOT_KV_ERANGE: return "slot or position out of range";
+    case SLOT_KV_ENOTALLOC: return "slot KV not allocated";
+    case SLOT_KV_ENOMEM: return "out of memory";
+    case SLOT_KV_EDUP: return "slot used by two rows of one batch";
+    case SLOT_KV_EDEVICE: return "HIP device error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"
