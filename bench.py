@@ -94,6 +94,9 @@ def main():
     ap.add_argument("--workload", default="mid",
                     choices=["tiny", "mid", "long", "many", "layer_stack"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (the reference "
+                         "kernel that scales the rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the step shards by "
@@ -108,6 +111,14 @@ def main():
     if not torch.cuda.is_available():
         log("no GPU visible")
         sys.exit(1)
+    if args.calibrate_copy:
+        src = torch.ones(2**28, device="cuda")  # 1 GiB of f32
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copied 1 GiB x 5")
+        return
     w = wl.WORKLOADS[args.workload]()
     n_layers = len(w.layers)
     log(f"[bench] workload {w.name}: B={w.B} n_slots={w.n_slots} slot_ctx={w.slot_ctx} "

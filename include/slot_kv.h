@@ -159,11 +159,11 @@ uint32_t slot_kv_chunk_keys(void);
 
 /* Profiling of the fused decode kernel.  Between slot_kv_profile_begin and
  * slot_kv_profile_end the handle records a HIP event pair on the call's
- * stream immediately around each launch of the fused split-K decode kernel
- * (the partial-merge kernel, when a batch needs it, runs after the second
- * event).  slot_kv_profile_end waits for the recorded launches and returns
- * their summed duration in milliseconds and their count (either pointer may
- * be NULL), then stops recording.  Errors: EINVAL, ENOMEM, EDEVICE. */
+ * stream immediately around each launch of the fused decode kernel (one
+ * launch per 256 rows of a slot_decode_attn call; it does the whole step).
+ * slot_kv_profile_end waits for the recorded launches and returns their
+ * summed duration in milliseconds and their count (either pointer may be
+ * NULL), then stops recording.  Errors: EINVAL, EDEVICE. */
 int slot_kv_profile_begin(slot_kv *h);
 int slot_kv_profile_end(slot_kv *h, double *kernel_ms, uint32_t *launches);
 

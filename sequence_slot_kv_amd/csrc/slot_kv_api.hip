@@ -1,6 +1,7 @@
 // slot_kv_api.hip -- the C ABI of include/slot_kv.h: handle, slot-KV
-// allocator, 64-bit offsets, host validation, per-call staging of the row
-// table and work list, and the kernel launches.
+// allocator, 64-bit offsets, host validation, and the decode launches (the
+// row table of each launch travels in the kernel arguments, so a decode
+// call enqueues exactly one kernel per 256 rows and no copies).
 //
 // "Forward Cuda Gemma": allocSlotKv (idempotent, frees first), slotKvOffsetBytes
 // ((slot*slot_ctx + pos)*kv_dim*4), decodeBatch (preconditions, per-row
@@ -11,20 +12,17 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <algorithm>
 #include <new>
 #include <vector>
 
 #include "slot_kv.h"
 #include "slot_kv_internal.h"
 
+using slotkv::AttnArgs;
 using slotkv::AttnParams;
-using slotkv::Plan;
-using slotkv::RowInfo;
-using slotkv::WorkItem;
 
 namespace {
-
-constexpr int kStages = 16;  // staging ring depth (calls in flight per handle)
 
 struct LayerState {
   uint32_t kv_dim = 0;
@@ -37,26 +35,18 @@ struct LayerState {
   float eps = 0.f, scale = 0.f;
 };
 
-struct Stage {
-  void* host = nullptr;   // pinned
-  void* dev = nullptr;
-  size_t cap = 0;
-  hipEvent_t done = nullptr;
-  bool used = false;
-};
-
 }  // namespace
 
 struct slot_kv {
   int device = -1;
   uint32_t n_slots = 0, slot_ctx = 0;
   std::vector<LayerState> layers;
-  Stage stages[kStages];
-  unsigned next_stage = 0;
-  float* part = nullptr;  // partial results (acc then m/l)
-  size_t part_cap = 0;    // floats
-  std::vector<RowInfo> rows;
-  std::vector<WorkItem> items;
+  float* part = nullptr;         // partial results of split rows (acc, then max/sum)
+  size_t part_cap = 0;           // floats
+  uint32_t* counters = nullptr;  // work queue [2], then per (row, kv head) chunk counters;
+                                 // all zero between launches
+  size_t counters_cap = 0;       // entries
+  AttnArgs args;                 // kernel arguments of the launch being built
   bool profiling = false;
   std::vector<hipEvent_t> prof_events;  // start/end pairs
   size_t prof_used = 0;                 // pairs recorded since profile_begin
@@ -75,15 +65,12 @@ void free_layers(slot_kv* h) {
 }
 
 void free_scratch(slot_kv* h) {
-  for (auto& s : h->stages) {
-    if (s.host) (void)hipHostFree(s.host);
-    if (s.dev) (void)hipFree(s.dev);
-    if (s.done) (void)hipEventDestroy(s.done);
-    s = Stage{};
-  }
   if (h->part) (void)hipFree(h->part);
   h->part = nullptr;
   h->part_cap = 0;
+  if (h->counters) (void)hipFree(h->counters);
+  h->counters = nullptr;
+  h->counters_cap = 0;
   for (hipEvent_t e : h->prof_events) (void)hipEventDestroy(e);
   h->prof_events.clear();
   h->prof_used = 0;
@@ -94,37 +81,6 @@ int check_layer(const slot_kv* h, uint32_t layer) {
   if (!h) return SLOT_KV_EINVAL;
   if (!h->allocated()) return SLOT_KV_ENOTALLOC;
   if (layer >= h->layers.size()) return SLOT_KV_EINVAL;
-  return SLOT_KV_OK;
-}
-
-// Make sure the ring stage has `bytes` of pinned and device memory and that
-// the device is done with its previous contents.
-int prepare_stage(Stage& s, size_t bytes) {
-  if (s.used) {
-    if (hipEventSynchronize(s.done) != hipSuccess) return SLOT_KV_EDEVICE;
-  }
-  if (!s.done) {
-    if (hipEventCreateWithFlags(&s.done, hipEventDisableTiming) != hipSuccess)
-      return SLOT_KV_EDEVICE;
-  }
-  if (s.cap < bytes) {
-    size_t cap = 4096;
-    while (cap < bytes) cap *= 2;
-    if (s.host) (void)hipHostFree(s.host);
-    if (s.dev) (void)hipFree(s.dev);
-    s.host = s.dev = nullptr;
-    s.cap = 0;
-    if (hipHostMalloc(&s.host, cap, hipHostMallocDefault) != hipSuccess) {
-      s.host = nullptr;
-      return SLOT_KV_ENOMEM;
-    }
-    if (hipMalloc(&s.dev, cap) != hipSuccess) {
-      (void)hipHostFree(s.host);
-      s.host = s.dev = nullptr;
-      return SLOT_KV_ENOMEM;
-    }
-    s.cap = cap;
-  }
   return SLOT_KV_OK;
 }
 
@@ -142,6 +98,26 @@ int ensure_partials(slot_kv* h, size_t floats) {
     return SLOT_KV_ENOMEM;
   }
   h->part_cap = cap;
+  return SLOT_KV_OK;
+}
+
+// The work-queue counters start at zero; the kernel returns them to zero, so
+// they are cleared only when (re)allocated.
+int ensure_counters(slot_kv* h, size_t entries) {
+  if (h->counters_cap >= entries) return SLOT_KV_OK;
+  if (hipDeviceSynchronize() != hipSuccess) return SLOT_KV_EDEVICE;
+  if (h->counters) (void)hipFree(h->counters);
+  h->counters = nullptr;
+  h->counters_cap = 0;
+  void* c = nullptr;
+  if (hipMalloc(&c, entries * sizeof(uint32_t)) != hipSuccess) return SLOT_KV_ENOMEM;
+  if (hipMemset(c, 0, entries * sizeof(uint32_t)) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess) {
+    (void)hipFree(c);
+    return SLOT_KV_EDEVICE;
+  }
+  h->counters = static_cast<uint32_t*>(c);
+  h->counters_cap = entries;
   return SLOT_KV_OK;
 }
 
@@ -305,46 +281,38 @@ int slot_decode_attn(slot_kv* h, uint32_t layer, const float* q, const float* k_
   rc = slotkv::check_batch(h->n_slots, h->slot_ctx, positions, slots, B);
   if (rc) return rc;
   const uint32_t C = SLOT_KV_CHUNK;
-  const uint64_t n_items64 = [&] {
-    uint64_t n = 0;
-    for (uint32_t b = 0; b < B; ++b) n += (uint64_t(positions[b]) + C) / C;
-    return n;
-  }();
-  if (n_items64 * L.n_kv_heads >= (uint64_t(1) << 31)) return SLOT_KV_EINVAL;
-
-  h->rows.resize(B);
-  h->items.resize(n_items64);
-  const Plan plan = slotkv::build_plan(positions, slots, B, C, h->rows.data(), h->items.data());
-
   const size_t D = L.head_dim;
-  if (plan.n_parts) {
-    rc = ensure_partials(h, static_cast<size_t>(plan.n_parts) * L.n_heads * (D + 2));
-    if (rc) return rc;
-  }
-  const size_t rows_bytes = B * sizeof(RowInfo);
-  const size_t bytes = rows_bytes + plan.n_items * sizeof(WorkItem);
-  Stage& st = h->stages[h->next_stage];
-  rc = prepare_stage(st, bytes);
-  if (rc) return rc;
-  h->next_stage = (h->next_stage + 1) % kStages;
-  std::memcpy(st.host, h->rows.data(), rows_bytes);
-  std::memcpy(static_cast<char*>(st.host) + rows_bytes, h->items.data(),
-              plan.n_items * sizeof(WorkItem));
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (hipMemcpyAsync(st.dev, st.host, bytes, hipMemcpyHostToDevice, s) != hipSuccess)
-    return SLOT_KV_EDEVICE;
+  const uint32_t R = slotkv::kMaxRowsPerLaunch;
+  const uint32_t G = L.n_heads / L.n_kv_heads;
 
-  AttnParams p{};
+  // Size the scratch for the largest launch before enqueueing anything.
+  size_t part_floats = 0;
+  for (uint32_t r0 = 0; r0 < B; r0 += R) {
+    const uint32_t n = std::min(B - r0, R);
+    uint64_t items = 0, max_chunks = 0;
+    for (uint32_t b = r0; b < r0 + n; ++b) {
+      const uint64_t nc = (uint64_t(positions[b]) + C) / C;
+      items += nc;
+      max_chunks = std::max(max_chunks, nc);
+    }
+    if (items * L.n_kv_heads >= (uint64_t(1) << 31)) return SLOT_KV_EINVAL;
+    part_floats = std::max(part_floats, static_cast<size_t>(n * max_chunks) * L.n_heads * (D + 2));
+  }
+  rc = ensure_partials(h, part_floats);
+  if (rc) return rc;
+  rc = ensure_counters(h, 2 + static_cast<size_t>(R) * L.n_kv_heads);
+  if (rc) return rc;
+  const uint32_t resident = slotkv::resident_blocks(L.head_dim, G);
+  if (resident == 0) return SLOT_KV_EDEVICE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  AttnArgs& a = h->args;
+  a.magic = slotkv::kArgsMagic;
+  AttnParams& p = a.p;
   p.k_cache = L.k;
   p.v_cache = L.v;
-  p.q = q;
-  p.k_new = k_new;
-  p.v_new = v_new;
-  p.out = out;
-  p.part_acc = h->part;
-  p.part_ml = h->part ? h->part + static_cast<size_t>(plan.n_parts) * L.n_heads * D : nullptr;
-  p.rows = static_cast<const RowInfo*>(st.dev);
-  p.items = reinterpret_cast<const WorkItem*>(static_cast<const char*>(st.dev) + rows_bytes);
+  p.sched = h->counters;
+  p.counters = h->counters + 2;
   p.q_norm_w = L.params;
   p.k_norm_w = L.params + D;
   p.inv_freq = L.params + 2 * D;
@@ -353,33 +321,45 @@ int slot_decode_attn(slot_kv* h, uint32_t layer, const float* q, const float* k_
   p.kv_dim = L.kv_dim;
   p.n_kv_heads = L.n_kv_heads;
   p.n_heads = L.n_heads;
-  p.n_waves = plan.n_items * L.n_kv_heads;
   p.chunk = C;
-  p.B = B;
   p.eps = L.eps;
   p.qk_scale_log2 = L.scale * 1.4426950408889634f;
-  hipEvent_t ev_end = nullptr;
-  if (h->profiling) {
-    if (h->prof_events.size() < 2 * (h->prof_used + 1)) {
-      hipEvent_t a = nullptr, b = nullptr;
-      if (hipEventCreate(&a) != hipSuccess) return SLOT_KV_EDEVICE;
-      if (hipEventCreate(&b) != hipSuccess) {
-        (void)hipEventDestroy(a);
-        return SLOT_KV_EDEVICE;
+  const size_t qd = static_cast<size_t>(L.n_heads) * D;
+  for (uint32_t r0 = 0; r0 < B; r0 += R) {  // rows are independent: launch in slices
+    const uint32_t n = std::min(B - r0, R);
+    const slotkv::LaunchWork work = slotkv::fill_rows(a.rows, positions + r0, slots + r0, n, C);
+    p.n_rows = n;
+    p.n_full = work.n_full;
+    p.n_units = work.n_items * L.n_kv_heads;
+    p.max_chunks = work.max_chunks;
+    p.q = q + r0 * qd;
+    p.k_new = k_new + static_cast<size_t>(r0) * L.kv_dim;
+    p.v_new = v_new + static_cast<size_t>(r0) * L.kv_dim;
+    p.out = out + r0 * qd;
+    p.part_acc = h->part;
+    p.part_ml = h->part + static_cast<size_t>(n) * work.max_chunks * L.n_heads * D;
+
+    hipEvent_t ev_end = nullptr;
+    if (h->profiling) {
+      if (h->prof_events.size() < 2 * (h->prof_used + 1)) {
+        hipEvent_t e0 = nullptr, e1 = nullptr;
+        if (hipEventCreate(&e0) != hipSuccess) return SLOT_KV_EDEVICE;
+        if (hipEventCreate(&e1) != hipSuccess) {
+          (void)hipEventDestroy(e0);
+          return SLOT_KV_EDEVICE;
+        }
+        h->prof_events.push_back(e0);
+        h->prof_events.push_back(e1);
       }
-      h->prof_events.push_back(a);
-      h->prof_events.push_back(b);
+      if (hipEventRecord(h->prof_events[2 * h->prof_used], s) != hipSuccess)
+        return SLOT_KV_EDEVICE;
+      ev_end = h->prof_events[2 * h->prof_used + 1];
+      ++h->prof_used;
     }
-    if (hipEventRecord(h->prof_events[2 * h->prof_used], s) != hipSuccess) return SLOT_KV_EDEVICE;
-    ev_end = h->prof_events[2 * h->prof_used + 1];
-    ++h->prof_used;
+    const uint32_t blocks = std::min(p.n_units, resident);
+    if (slotkv::launch_decode(a, L.head_dim, G, blocks, stream, ev_end) != hipSuccess)
+      return SLOT_KV_EDEVICE;
   }
-  const int e = slotkv::launch_decode(p, L.head_dim, L.n_heads / L.n_kv_heads,
-                                      plan.n_split_rows > 0, stream, ev_end);
-  // The stage may be reused once everything enqueued so far has run.
-  const bool rec = hipEventRecord(st.done, s) == hipSuccess;
-  st.used = rec;
-  if (e != hipSuccess || !rec) return SLOT_KV_EDEVICE;
   return SLOT_KV_OK;
 }
 

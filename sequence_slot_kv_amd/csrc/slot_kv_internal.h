@@ -6,55 +6,38 @@
 #include <stdint.h>
 
 #ifndef SLOT_KV_CHUNK
-#define SLOT_KV_CHUNK 256  // keys per split-K chunk (multiple of 64)
+#define SLOT_KV_CHUNK 512  // keys per split-K chunk (a multiple of 64)
+#endif
+#ifndef SLOT_KV_WG_WAVES
+#define SLOT_KV_WG_WAVES 4  // waves of one workgroup sharing a chunk
 #endif
 
 namespace slotkv {
 
-// One batch row as the kernels see it (16 bytes, one vector load).
-struct RowInfo {
-  uint32_t pos;        // position written and attended up to (inclusive)
-  uint32_t slot;       // slot index
-  uint32_t part_base;  // first partial-result index of this row (split rows)
-  uint32_t n_chunks;   // ceil((pos + 1) / chunk)
+// Rows of one launch travel inside the kernel arguments (no staging copy).
+constexpr uint32_t kMaxRowsPerLaunch = 256;
+
+// The launch's work items are the (row, chunk) pairs: first every full chunk
+// (row-major), then each row's shorter last chunk, longest first.
+struct LaunchRows {
+  uint32_t pos[kMaxRowsPerLaunch];    // position written and attended up to (inclusive)
+  uint32_t slot[kMaxRowsPerLaunch];   // slot index
+  uint32_t full_prefix[kMaxRowsPerLaunch + 1];  // full chunks of the rows before b
+  uint8_t tail_row[kMaxRowsPerLaunch];          // rows owning a partial chunk, longest first
 };
 
-// One split-K work item: keys [chunk*C, min((chunk+1)*C, pos+1)) of one row.
-struct WorkItem {
-  uint32_t row;
-  uint32_t chunk;
-};
-
-// Host-side plan of one decode call.
-struct Plan {
-  uint32_t n_items = 0;       // work items (per kv head)
-  uint32_t n_split_rows = 0;  // rows with more than one chunk
-  uint32_t n_parts = 0;       // partial results per head (sum of chunks of split rows)
-};
-
-// Validation of one batch (no device access).  Returns a SLOT_KV_* status.
-int check_batch(uint32_t n_slots, uint32_t slot_ctx, const uint32_t* positions,
-                const uint32_t* slots, uint32_t B);
-
-// Build the row table and the work list (full chunks first, then the partial
-// last chunks, longest first).  rows must hold B entries and items at least
-// count_items(...) entries.
-Plan build_plan(const uint32_t* positions, const uint32_t* slots, uint32_t B,
-                uint32_t chunk, RowInfo* rows, WorkItem* items);
-uint32_t count_items(const uint32_t* positions, uint32_t B, uint32_t chunk);
-
-// Kernel-side parameters of one decode launch.
+// Kernel-side parameters of one decode launch (rows 0..n_rows-1 of it).
 struct AttnParams {
   float* k_cache;          // layer K buffer [n_slots][slot_ctx][kv_dim]
   float* v_cache;          // layer V buffer
-  const float* q;          // [B][n_heads*D]
-  const float* k_new;      // [B][kv_dim]
-  const float* v_new;      // [B][kv_dim]
-  float* out;              // [B][n_heads*D]
-  float* part_acc;         // [n_parts][n_heads][D]   unnormalised partial outputs
-  float* part_ml;          // [n_parts][n_heads][2]   running max (log2 units), sum
-  const RowInfo* rows;     // [B]
-  const WorkItem* items;   // [n_items]
+  const float* q;          // [n_rows][n_heads*D]
+  const float* k_new;      // [n_rows][kv_dim]
+  const float* v_new;      // [n_rows][kv_dim]
+  float* out;              // [n_rows][n_heads*D]
+  float* part_acc;         // [n_rows][max_chunks][n_heads][D]  unnormalised partial outputs
+  float* part_ml;          // [n_rows][max_chunks][n_heads][2]  max (log2 units), sum
+  uint32_t* sched;         // [2]: next dynamic work unit, exited workgroups; zero between launches
+  uint32_t* counters;      // [n_rows][n_kv_heads] chunks finished; zero between launches
   const float* q_norm_w;   // [D]
   const float* k_norm_w;   // [D]
   const float* inv_freq;   // [D/2]
@@ -63,18 +46,46 @@ struct AttnParams {
   uint32_t kv_dim;
   uint32_t n_kv_heads;
   uint32_t n_heads;
-  uint32_t n_waves;        // n_items * n_kv_heads
+  uint32_t n_rows;
+  uint32_t n_full;         // full-chunk items
+  uint32_t n_units;        // (full + partial items) * n_kv_heads
+  uint32_t max_chunks;     // largest chunk count of a row (partial-result stride)
   uint32_t chunk;
-  uint32_t B;
   float eps;
   float qk_scale_log2;     // scale * log2(e)
 };
 
-// Launches (defined with the kernels).  Return a hipError_t value.
-// `after_attn` (may be null) is a hipEvent_t recorded right after the fused
-// kernel, before the merge kernel.
-int launch_decode(const AttnParams& p, uint32_t head_dim, uint32_t group,
-                  bool any_split, void* stream, void* after_attn);
+constexpr uint32_t kArgsMagic = 0x534c4b56u;  // last word of the kernel arguments
+
+struct AttnArgs {
+  AttnParams p;
+  LaunchRows rows;
+  uint32_t magic;  // kArgsMagic; the kernel does nothing if it reads another value
+};
+static_assert(sizeof(AttnArgs) < 4000, "kernel arguments must stay below 4 KiB");
+
+// Validation of one batch (no device access).  Returns a SLOT_KV_* status.
+int check_batch(uint32_t n_slots, uint32_t slot_ctx, const uint32_t* positions,
+                const uint32_t* slots, uint32_t B);
+
+// Work of one launch over rows [0, n) of positions / slots.
+struct LaunchWork {
+  uint32_t n_full = 0;      // full-chunk items
+  uint32_t n_items = 0;     // full + partial items
+  uint32_t max_chunks = 0;  // largest chunk count of a row
+};
+// Fill the row table of one launch (n <= kMaxRowsPerLaunch).
+LaunchWork fill_rows(LaunchRows& rows, const uint32_t* positions, const uint32_t* slots,
+                     uint32_t n, uint32_t chunk);
+
+// Launch of the fused decode kernel with `blocks` persistent workgroups, then
+// (when a row spans several chunks) of the partial merge.  `after_decode` (a
+// hipEvent_t or null) is recorded between the two.  Returns a hipError_t value.
+int launch_decode(const AttnArgs& a, uint32_t head_dim, uint32_t group, uint32_t blocks,
+                  void* stream, void* after_decode);
+// Workgroups of the decode kernel for this shape that are resident at once
+// on the current device (0 on error).
+uint32_t resident_blocks(uint32_t head_dim, uint32_t group);
 bool decode_shape_supported(uint32_t head_dim, uint32_t group);
 
 }  // namespace slotkv

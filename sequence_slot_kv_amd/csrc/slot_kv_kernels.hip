@@ -1,28 +1,31 @@
-// slot_kv_kernels.hip -- gfx950 kernels of the batched decode step over a
+// slot_kv_kernels.hip -- gfx950 kernel of the batched decode step over a
 // slot-indexed KV cache ("Forward Cuda Gemma", decodeBatch: per-head Q/K
 // norm, RoPE, KV write and causal softmax attention of every row against its
 // own slot; "Forward Cuda", init: inv_freq and sinks).
 //
-// One fused split-K kernel does the whole step for one (row, key chunk, kv
-// head) per 64-lane wave:
-//   prologue  RMSNorm + RoPE of the row's G query heads of this kv head
-//             (kept in registers, pre-multiplied by scale*log2(e));
-//             the wave that owns the row's last chunk also normalises and
-//             rotates the new key, stores it and v_new at
-//             (slot*slot_ctx + pos)*kv_dim, and seeds its softmax state with
-//             that key straight from registers (no read-after-write);
-//   body      streams the chunk's history rows of K and V once, with 128-bit
-//             non-temporal loads: LPK lanes own one key row (each lane four
-//             floats per 4*LPK-float slice), 64/LPK keys per wave in flight,
-//             dot products reduced over the LPK lanes with DPP, one online
-//             softmax state per key group;
-//   epilogue  the key groups of the wave are merged with cross-lane
-//             shuffles; a row that fits one chunk is normalised (with its
-//             sink) and written out, a longer row leaves an unnormalised
-//             partial (acc, max, sum) per query head.
-// A second kernel merges the partials of split rows in chunk order.  Chunk
-// boundaries depend only on the row's position and the merge order is
-// fixed, so a row's result does not depend on the rest of the batch.
+// One persistent launch does the whole step.  The work is cut into units
+// (row b, chunk c of C keys, kv head j); the NW waves of a workgroup split a
+// unit's keys, wave w taking [c*C + w*C/NW, c*C + (w+1)*C/NW).  Workgroups
+// pull units from an agent-scope queue (full chunks first, then partial
+// chunks longest first) and keep it one unit ahead, so that:
+//   - the next unit's query heads (and new key) are normalised, rotated and
+//     staged in LDS while the current unit streams; the unit that holds a
+//     row's last chunk also writes the row's KV entry -- rotated key and
+//     v_new at (slot*slot_ctx + pos)*kv_dim -- from that staging step;
+//   - the next unit's first K stage is in flight while the current unit
+//     finishes.
+// Per unit and wave, two passes stream the history rows once each with
+// 128-bit non-temporal loads, double-buffered: pass 1 reads K, computes the
+// scores (LPK lanes per key row, DPP reductions) into LDS and the running
+// max; pass 2 reads V and accumulates exp2(score - max) * v.  No accumulator
+// is ever rescaled inside a wave.  Key groups, then the NW waves (through
+// LDS), merge; a row of one chunk is finished with its sink; a longer row's
+// chunk leaves an unnormalised partial (acc, max, sum) through agent-coherent
+// stores and the last workgroup of that (row, kv head) -- an agent-scope
+// counter decides -- merges the row's partials in chunk order.
+// Chunk boundaries depend only on the row's position, every merge runs in a
+// fixed order and no result depends on which workgroup ran a unit, so a
+// row's result does not depend on the rest of the batch.
 #include <hip/hip_runtime.h>
 
 #include "slot_kv_internal.h"
@@ -33,24 +36,35 @@ namespace {
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
-constexpr int kWavesPerBlock = 4;
+constexpr int NW = SLOT_KV_WG_WAVES;
+constexpr int kThreads = kWave * NW;
 constexpr float kLog2e = 1.4426950408889634f;
+#ifndef SLOT_KV_WAVES_PER_EU
+#define SLOT_KV_WAVES_PER_EU 2  // occupancy the register budget is fitted to
+#endif
+static_assert(SLOT_KV_CHUNK % NW == 0, "a chunk splits evenly over the waves");
 
-// Lanes per key row: enough that each lane holds about 64 floats of query
+// Lanes per key row: enough that each lane holds about 32 floats of query
 // (G heads) and as many of accumulator.  The lane's elements of a head
 // vector are d = i*4*LPK + 4*r + c (slice i, lane r of the key group,
 // component c), so the RoPE partner d + D/2 sits in the same lane, slice
 // i + NV4/2.
+#ifndef SLOT_KV_LPK
+#define SLOT_KV_LPK 0  // 0: derive from the shape
+#endif
+#ifndef SLOT_KV_UNROLL
+#define SLOT_KV_UNROLL 0  // 0: derive from the shape
+#endif
 constexpr int pick_lpk(int D, int G) {
-  int want = G * D / 64;
+  int want = SLOT_KV_LPK ? SLOT_KV_LPK : G * D / 32;
   int lpk = want < 4 ? 4 : (want > 16 ? 16 : want);
   while (D / (4 * lpk) < 2) lpk /= 2;
   return lpk;
 }
-// Keys per key group per loop trip: about 16 float4 loads per lane in flight.
+// Keys per key group per pipeline stage: about 8 float4 loads per lane.
 constexpr int pick_unroll(int D, int LPK) {
   int nv4 = D / (4 * LPK);
-  return nv4 >= 8 ? 1 : 8 / nv4;
+  return SLOT_KV_UNROLL ? SLOT_KV_UNROLL : (nv4 >= 8 ? 1 : 8 / nv4);
 }
 
 template <int CTRL>
@@ -65,8 +79,8 @@ __device__ __forceinline__ float dpp_mov(float v) {
 template <int LPK>
 __device__ __forceinline__ float group_sum(float v) {
   static_assert(LPK == 4 || LPK == 8 || LPK == 16, "lanes per key");
-  v += dpp_mov<0xB1>(v);                         // quad_perm [1,0,3,2]: lane ^ 1
-  v += dpp_mov<0x4E>(v);                         // quad_perm [2,3,0,1]: lane ^ 2
+  v += dpp_mov<0xB1>(v);                            // quad_perm [1,0,3,2]: lane ^ 1
+  v += dpp_mov<0x4E>(v);                            // quad_perm [2,3,0,1]: lane ^ 2
   if constexpr (LPK >= 8) v += dpp_mov<0x141>(v);   // row_half_mirror: i <-> 7-i
   if constexpr (LPK >= 16) v += dpp_mov<0x140>(v);  // row_mirror: i <-> 15-i
   return v;
@@ -77,330 +91,675 @@ __device__ __forceinline__ float dot4(f4 a, f4 b) {
 }
 
 __device__ __forceinline__ f4 ld4(const float* p) { return *reinterpret_cast<const f4*>(p); }
+#ifndef SLOT_KV_FUSED_MERGE
+#define SLOT_KV_FUSED_MERGE 1  // merge split rows inside the decode kernel
+#endif
+#ifndef SLOT_KV_NT_LOADS
+#define SLOT_KV_NT_LOADS 1  // stream history rows past the caches
+#endif
 __device__ __forceinline__ f4 ld4_stream(const float* p) {
+#if SLOT_KV_NT_LOADS
   return __builtin_nontemporal_load(reinterpret_cast<const f4*>(p));
+#else
+  return *reinterpret_cast<const f4*>(p);
+#endif
 }
 __device__ __forceinline__ void st4(float* p, f4 v) { *reinterpret_cast<f4*>(p) = v; }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Rescale factor exp2(m_old - m_new) for a state that may still be empty.
-__device__ __forceinline__ float rescale(float m_old, float m_new) {
-  return m_old == -INFINITY ? 0.f : fast_exp2(m_old - m_new);
+
+// Agent-scope (all XCDs) coherent store / load of one float: split-row
+// partials that another workgroup merges within the same launch.
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int D, int LPK>
-__device__ __forceinline__ void rms_norm_lane(f4 (&x)[D / (4 * LPK)], const f4 (&w)[D / (4 * LPK)],
-                                              float eps) {
-  constexpr int NV4 = D / (4 * LPK);
-  float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < NV4; ++i) ss += dot4(x[i], x[i]);
-  ss = group_sum<LPK>(ss);
-  const float rn = 1.0f / sqrtf(ss * (1.0f / D) + eps);
-#pragma unroll
-  for (int i = 0; i < NV4; ++i) x[i] = x[i] * rn * w[i];
+// max without the NaN canonicalisation of fmaxf (inputs are never NaN here).
+__device__ __forceinline__ float max_nc(float a, float b) { return a > b ? a : b; }
+
+// Weight exp2(m - m_new) of a state with max m; an empty state (m = -inf)
+// weighs 0.
+__device__ __forceinline__ float rescale(float m, float m_new) {
+  return m == -INFINITY ? 0.f : fast_exp2(m - m_new);
 }
 
-template <int D, int LPK>
-__device__ __forceinline__ void rope_lane(f4 (&x)[D / (4 * LPK)],
-                                          const float (&cs)[D / (8 * LPK)][4],
-                                          const float (&sn)[D / (8 * LPK)][4]) {
-  constexpr int HALF = D / (8 * LPK);
+template <int D, int G>
+struct alignas(16) Lds {
+  float acc[NW][G][D];
+  float m[NW][G];
+  float l[NW][G];
+  uint32_t last;
+};
+
+// Occupancy the register allocation targets: shapes whose lanes hold 64
+// floats of query and 64 of accumulator get the whole register file.
+template <int D, int G>
+constexpr int waves_per_eu() {
+  return G * D / pick_lpk(D, G) >= 64 ? 1 : SLOT_KV_WAVES_PER_EU;
+}
+
+template <int D, int G>
+struct Shape {
+  static constexpr int LPK = pick_lpk(D, G);
+  static constexpr int U = pick_unroll(D, LPK);
+  static constexpr int NV4 = D / (4 * LPK);                  // float4 per lane per head vector
+  static constexpr int NG = kWave / LPK;                     // key groups per wave
+  static constexpr int SL = 4 * LPK;                         // floats per slice
+  static constexpr int STEP = NG * U;                        // keys per wave per stage
+  static constexpr int KPW = SLOT_KV_CHUNK / NW;             // history keys per wave, at most
+  static constexpr int NST = (KPW + STEP - 1) / STEP;        // stages per pass, at most
+  static constexpr int SCORES = NST * NG * G * U;            // score slots per wave
+  static_assert(NV4 >= 2 && NV4 % 2 == 0, "lane layout needs an even slice count");
+};
+
+// One work unit as one wave sees it: chunk `chunk` of row b against kv head
+// j; the wave owns history keys [k_begin, k_begin + len) of that chunk.
+struct UnitPlan {
+  uint32_t b, j, chunk, pos, slot, n_chunks;
+  uint32_t k_begin, len, n_full, n_st;  // n_st = stages per pass (last may be partial)
+  bool new_key;                         // this wave also owns the row's new key
+};
+
+// Row, kv head and chunk of a unit (the binary search is done once per unit).
+struct UnitId {
+  uint32_t b, j, chunk;
+};
+
+__device__ __forceinline__ UnitId locate_unit(const AttnArgs& a, uint32_t unit) {
+  const AttnParams& p = a.p;
+  UnitId id;
+  id.j = unit % p.n_kv_heads;
+  const uint32_t item = unit / p.n_kv_heads;
+  if (item < p.n_full) {
+    // full chunk: the last row whose first full chunk is <= item
+    uint32_t blo = 0, bhi = p.n_rows;
+    while (bhi - blo > 1) {
+      const uint32_t mid = (blo + bhi) / 2;
+      if (a.rows.full_prefix[mid] <= item) blo = mid; else bhi = mid;
+    }
+    id.b = blo;
+    id.chunk = item - a.rows.full_prefix[id.b];
+  } else {
+    id.b = a.rows.tail_row[item - p.n_full];
+    id.chunk = a.rows.pos[id.b] / p.chunk;  // the partial last chunk
+  }
+  return id;
+}
+
+template <int D, int G>
+__device__ __forceinline__ UnitPlan plan_unit(const AttnArgs& a, const UnitId& id, uint32_t w) {
+  using S = Shape<D, G>;
+  const AttnParams& p = a.p;
+  UnitPlan u;
+  u.b = id.b;
+  u.j = id.j;
+  u.chunk = id.chunk;
+  u.pos = a.rows.pos[u.b];
+  u.slot = a.rows.slot[u.b];
+  u.n_chunks = u.pos / p.chunk + 1;
+  const uint32_t c0 = u.chunk * p.chunk;
+  const uint32_t t_end = min(c0 + p.chunk, u.pos);
+  const uint32_t per_wave = p.chunk / NW;
+  u.k_begin = min(c0 + w * per_wave, t_end);
+  u.len = min(c0 + (w + 1) * per_wave, t_end) - u.k_begin;
+  u.n_full = u.len / S::STEP;
+  u.n_st = u.n_full + (u.len % S::STEP != 0 ? 1u : 0u);
+  u.new_key = (w == 0) && (u.chunk == u.n_chunks - 1);
+  return u;
+}
+
+template <int D, int G>
+struct Stage {
+  f4 x[Shape<D, G>::U][Shape<D, G>::NV4];
+};
+
+// Stage qi of a unit: K stage qi for qi < n_st, else V stage qi - n_st.
+template <int D, int G>
+__device__ __forceinline__ void load_stage(const AttnParams& p, const UnitPlan& u, uint32_t gi,
+                                           uint32_t lo, Stage<D, G>& sg, uint32_t qi) {
+  using S = Shape<D, G>;
+  const bool is_v = qi >= u.n_st;
+  const uint32_t st = is_v ? qi - u.n_st : qi;
+  const uint64_t row = static_cast<uint64_t>(u.k_begin + st * S::STEP + gi);
+  const float* base = (is_v ? p.v_cache : p.k_cache) + static_cast<uint64_t>(u.slot) * p.slot_stride +
+                      row * p.kv_dim + u.j * D + lo;
+  if (st < u.n_full) {
 #pragma unroll
-  for (int i = 0; i < HALF; ++i) {
+    for (int uu = 0; uu < S::U; ++uu)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float a = x[i][c], b = x[i + HALF][c];
-      x[i][c] = a * cs[i][c] - b * sn[i][c];
-      x[i + HALF][c] = b * cs[i][c] + a * sn[i][c];
+      for (int i = 0; i < S::NV4; ++i)
+        sg.x[uu][i] = ld4_stream(base + static_cast<uint64_t>(S::NG * uu) * p.kv_dim + i * S::SL);
+  } else {
+#pragma unroll
+    for (int uu = 0; uu < S::U; ++uu) {
+      if (st * S::STEP + gi + S::NG * uu < u.len) {
+#pragma unroll
+        for (int i = 0; i < S::NV4; ++i)
+          sg.x[uu][i] = ld4_stream(base + static_cast<uint64_t>(S::NG * uu) * p.kv_dim + i * S::SL);
+      } else {
+#pragma unroll
+        for (int i = 0; i < S::NV4; ++i) sg.x[uu][i] = f4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  }
+}
+
+// The next unit's query heads (and its new key) are normalised and rotated
+// while the current unit streams, and staged in LDS in two parity buffers.
+// Vector v < G is query head j*G + v; v == G is the new key, present only
+// for the unit that holds the row's last chunk.  Wave w takes vectors
+// w, w + NW, ...; lane l holds elements l*EPL .. l*EPL + EPL-1, so the RoPE
+// partner of element d (d +- D/2) sits in lane l ^ 32.
+template <int D, int G>
+struct alignas(16) PrepLds {
+  float q[2][G][D];  // normalised, rotated, times scale*log2(e)
+  float kn[2][D];    // normalised, rotated new key
+};
+template <int D, int G>
+struct PrepRaw {
+  static constexpr int EPL = D / kWave;
+  static constexpr int SLOTS = (G + 1 + NW - 1) / NW;
+  float x[SLOTS][EPL];
+};
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v = group_sum<16>(v);
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+template <int D, int G>
+__device__ __forceinline__ bool prep_has(const AttnArgs& a, const UnitId& id, uint32_t v) {
+  return v < G || (v == G && id.chunk == a.rows.pos[id.b] / a.p.chunk);
+}
+
+template <int D, int G>
+__device__ __forceinline__ void prep_issue(const AttnArgs& a, const UnitId& id, uint32_t w,
+                                           uint32_t lane, PrepRaw<D, G>& raw) {
+  using R = PrepRaw<D, G>;
+  const AttnParams& p = a.p;
+#pragma unroll
+  for (int s = 0; s < R::SLOTS; ++s) {
+    const uint32_t v = w + s * NW;
+    if (!prep_has<D, G>(a, id, v)) continue;  // wave-uniform
+    const float* src = v < G ? p.q + (static_cast<size_t>(id.b) * p.n_heads + id.j * G + v) * D
+                             : p.k_new + static_cast<size_t>(id.b) * p.kv_dim + id.j * D;
+#pragma unroll
+    for (int e = 0; e < R::EPL; ++e) raw.x[s][e] = src[lane * R::EPL + e];
+  }
+}
+
+template <int D, int G>
+__device__ __forceinline__ void prep_finish(const AttnArgs& a, const UnitId& id, uint32_t w,
+                                            uint32_t lane, PrepRaw<D, G>& raw,
+                                            PrepLds<D, G>& prep, uint32_t par) {
+  using R = PrepRaw<D, G>;
+  const AttnParams& p = a.p;
+  const uint32_t pos = a.rows.pos[id.b];
+  const float fpos = static_cast<float>(pos);
+#pragma unroll
+  for (int s = 0; s < R::SLOTS; ++s) {
+    const uint32_t v = w + s * NW;
+    if (!prep_has<D, G>(a, id, v)) continue;  // wave-uniform
+    const float* wts = v < G ? p.q_norm_w : p.k_norm_w;
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < R::EPL; ++e) ss += raw.x[s][e] * raw.x[s][e];
+    ss = wave_sum(ss);
+    const float rn = 1.0f / sqrtf(ss * (1.0f / D) + p.eps);
+    float y[R::EPL];
+#pragma unroll
+    for (int e = 0; e < R::EPL; ++e) {
+      const uint32_t d = lane * R::EPL + e;
+      const float x = raw.x[s][e] * rn * wts[d];
+      const float partner = __shfl_xor(x, 32);
+      const float ang = fpos * p.inv_freq[(lane & 31) * R::EPL + e];  // one f32 multiply
+      float sn, cs;
+      sincosf(ang, &sn, &cs);
+      y[e] = lane < 32 ? x * cs - partner * sn : x * cs + partner * sn;
+    }
+    if (v < G) {
+#pragma unroll
+      for (int e = 0; e < R::EPL; ++e) prep.q[par][v][lane * R::EPL + e] = y[e] * p.qk_scale_log2;
+    } else {
+      // the step's KV write: rotated key and v_new at (slot*slot_ctx + pos)*kv_dim
+      const uint64_t at = static_cast<uint64_t>(a.rows.slot[id.b]) * p.slot_stride +
+                          static_cast<uint64_t>(pos) * p.kv_dim + id.j * D + lane * R::EPL;
+      const float* vsrc = p.v_new + static_cast<size_t>(id.b) * p.kv_dim + id.j * D + lane * R::EPL;
+#pragma unroll
+      for (int e = 0; e < R::EPL; ++e) {
+        prep.kn[par][lane * R::EPL + e] = y[e];
+        p.k_cache[at + e] = y[e];
+        p.v_cache[at + e] = vsrc[e];
+      }
     }
   }
 }
 
 template <int D, int G>
-__global__ void __launch_bounds__(kWave* kWavesPerBlock)
-    decode_attn_kernel(const AttnParams p) {
-  constexpr int LPK = pick_lpk(D, G);
-  constexpr int U = pick_unroll(D, LPK);
-  constexpr int NV4 = D / (4 * LPK);  // float4 per lane per head vector
-  constexpr int HALF = NV4 / 2;
-  constexpr int NG = kWave / LPK;     // key groups per wave
-  constexpr int SL = 4 * LPK;         // floats per slice
-  static_assert(NV4 >= 2 && NV4 % 2 == 0, "lane layout needs an even slice count");
+__device__ __forceinline__ void merge_row(const AttnParams& p, uint32_t b, uint32_t j,
+                                          uint32_t n_chunks, uint32_t tid, uint32_t n_threads);
 
-  const uint32_t lane = threadIdx.x % kWave;
-  const uint32_t wave = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
-  if (wave >= p.n_waves) return;  // wave-uniform
-  const uint32_t j = wave % p.n_kv_heads;
-  const WorkItem it = p.items[wave / p.n_kv_heads];
-  const RowInfo row = p.rows[it.row];
+// Persistent decode kernel: as many workgroups as are resident at once.
+// Workgroup g starts with unit g, then takes units from an agent-scope queue
+// that it reads one unit ahead, so the next unit's first loads are in flight
+// while the current unit finishes.  Units are ordered full chunks first, then
+// partial chunks longest first, so the work left at the end is short.  The
+// last workgroup to exit returns the queue to zero for the next launch.  No
+// workgroup ever waits for another.  A row of one chunk is finished here; a
+// longer row leaves one unnormalised partial per chunk for merge_kernel.
+template <int D, int G>
+__global__ void __launch_bounds__(kThreads)
+    __attribute__((amdgpu_waves_per_eu(waves_per_eu<D, G>()))) decode_attn_kernel(const AttnArgs a) {
+  using S = Shape<D, G>;
+  constexpr int LPK = S::LPK, U = S::U, NV4 = S::NV4, NG = S::NG, SL = S::SL, STEP = S::STEP;
+  __shared__ Lds<D, G> sh;
+  __shared__ __attribute__((aligned(16))) float sc_lds[NW][S::SCORES];
+  __shared__ uint32_t queue_slot[2];
+  __shared__ PrepLds<D, G> prep;
+  if (a.magic != kArgsMagic) return;  // argument block not delivered whole
+  const AttnParams& p = a.p;
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid % kWave;
+  const uint32_t w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
   const uint32_t gi = lane / LPK;
   const uint32_t lo = 4 * (lane % LPK);  // lane's float offset inside a slice
+  const uint32_t n_blocks = gridDim.x;
 
-  // ---- prologue: RoPE angles of this lane's first-half elements --------
-  float cs[HALF][4], sn[HALF][4];
-  {
-    const float fpos = static_cast<float>(row.pos);
-#pragma unroll
-    for (int i = 0; i < HALF; ++i) {
-      const f4 f = ld4(p.inv_freq + i * SL + lo);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float ang = fpos * f[c];  // one f32 multiply
-        sincosf(ang, &sn[i][c], &cs[i][c]);
-      }
-    }
-  }
+  if (tid == 0)
+    queue_slot[0] = __hip_atomic_fetch_add(&p.sched[0], 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT) + n_blocks;
+  __syncthreads();
+  uint32_t nxt = __builtin_amdgcn_readfirstlane(queue_slot[0]);
+  const UnitId first = locate_unit(a, blockIdx.x);  // blocks <= n_units
+  UnitPlan u = plan_unit<D, G>(a, first, w);
+  Stage<D, G> A, B;
+  if (u.n_st > 0) load_stage<D, G>(p, u, gi, lo, A, 0);  // A always holds the next stage
+  PrepRaw<D, G> praw;
+  prep_issue<D, G>(a, first, w, lane, praw);
+  prep_finish<D, G>(a, first, w, lane, praw, prep, 0);
+  __syncthreads();
 
-  // ---- query heads j*G .. j*G+G-1: norm, RoPE, fold in scale*log2(e) ----
-  f4 q[G][NV4];
-  {
-    f4 w[NV4];
-#pragma unroll
-    for (int i = 0; i < NV4; ++i) w[i] = ld4(p.q_norm_w + i * SL + lo);
-    const float* qrow = p.q + static_cast<size_t>(it.row) * p.n_heads * D +
-                        static_cast<size_t>(j) * G * D + lo;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-#pragma unroll
-      for (int i = 0; i < NV4; ++i) q[g][i] = ld4(qrow + g * D + i * SL);
-      rms_norm_lane<D, LPK>(q[g], w, p.eps);
-      rope_lane<D, LPK>(q[g], cs, sn);
-#pragma unroll
-      for (int i = 0; i < NV4; ++i) q[g][i] *= p.qk_scale_log2;
-    }
-  }
+  for (uint32_t it = 0;; ++it) {  // workgroup-uniform
+    const bool has_next = nxt < p.n_units;
+    if (tid == 0 && has_next)
+      queue_slot[(it + 1) & 1] = __hip_atomic_fetch_add(&p.sched[0], 1u, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT) + n_blocks;
+    UnitId un{};
+    if (has_next) un = locate_unit(a, nxt);
 
-  float m[G], l[G];
-  f4 acc[G][NV4];
+    // ---- prologue: queries and new key from LDS ------------------------------
+    const uint32_t par = it & 1;
+    f4 q[G][NV4];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = -INFINITY;
-    l[g] = 0.f;
+    for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int i = 0; i < NV4; ++i) acc[g][i] = f4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  const uint64_t slot_base = static_cast<uint64_t>(row.slot) * p.slot_stride + j * D + lo;
-
-  // ---- the new key (last chunk of the row only) ---------------------------
-  if (it.chunk == row.n_chunks - 1) {
-    f4 kn[NV4], vn[NV4], w[NV4];
-    const size_t nb = static_cast<size_t>(it.row) * p.kv_dim + j * D + lo;
+      for (int i = 0; i < NV4; ++i) q[g][i] = ld4(&prep.q[par][g][i * SL + lo]);
+    float mx[G];  // running max of this lane's key group, per head
+    float s_new[G];
+    f4 vn[NV4];
 #pragma unroll
-    for (int i = 0; i < NV4; ++i) {
-      kn[i] = ld4(p.k_new + nb + i * SL);
-      vn[i] = ld4(p.v_new + nb + i * SL);
-      w[i] = ld4(p.k_norm_w + i * SL + lo);
-    }
-    rms_norm_lane<D, LPK>(kn, w, p.eps);
-    rope_lane<D, LPK>(kn, cs, sn);
-    if (gi == 0) {
-      const uint64_t at = slot_base + static_cast<uint64_t>(row.pos) * p.kv_dim;
+    for (int g = 0; g < G; ++g) mx[g] = -INFINITY;
+    if (u.new_key) {  // wave 0 of the row's last chunk scores the new key
+      f4 kn[NV4];
+      const size_t nb = static_cast<size_t>(u.b) * p.kv_dim + u.j * D + lo;
 #pragma unroll
       for (int i = 0; i < NV4; ++i) {
-        st4(p.k_cache + at + i * SL, kn[i]);
-        st4(p.v_cache + at + i * SL, vn[i]);
+        kn[i] = ld4(&prep.kn[par][i * SL + lo]);
+        vn[i] = ld4(p.v_new + nb + i * SL);
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float sdot = dot4(q[g][0], kn[0]);
+#pragma unroll
+        for (int i = 1; i < NV4; ++i) sdot += dot4(q[g][i], kn[i]);
+        s_new[g] = group_sum<LPK>(sdot);
+        mx[g] = s_new[g];
       }
     }
-    // Key group 0 starts its state from the new key: weight exp2(0) = 1.
+    if (has_next) prep_issue<D, G>(a, un, w, lane, praw);  // consumed after pass 1
+
+    // ---- two passes over this wave's history keys ------------------------
+    // Pass 1 streams the K rows, keeps each key's scores (log2 units) in LDS
+    // and the running max per head; pass 2 streams the V rows and
+    // accumulates exp2(score - max) * v against the wave's final max, so no
+    // accumulator is ever rescaled.  Both passes form one double-buffered
+    // sequence of 2 * n_st stages; stage s of a pass holds key
+    // k_begin + s*STEP + gi + NG*u for u < U.
+    float* sc_w = &sc_lds[w][0];  // [stage][key group][G][U]
+    auto score = [&](const Stage<D, G>& sg, uint32_t st) {
+      const bool tail = st >= u.n_full;
+      float sc[G * U];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+#pragma unroll
+        for (int uu = 0; uu < U; ++uu) {
+          float d = dot4(q[g][0], sg.x[uu][0]);
+#pragma unroll
+          for (int i = 1; i < NV4; ++i) d += dot4(q[g][i], sg.x[uu][i]);
+          d = group_sum<LPK>(d);
+          if (tail && st * STEP + gi + NG * uu >= u.len) d = -INFINITY;
+          sc[g * U + uu] = d;
+          mx[g] = max_nc(mx[g], d);
+        }
+      }
+      if (lane % LPK == 0) {
+        float* dst = sc_w + (st * NG + gi) * (G * U);
+        if constexpr ((G * U) % 4 == 0) {
+#pragma unroll
+          for (int e = 0; e < G * U; e += 4)
+            st4(dst + e, f4{sc[e], sc[e + 1], sc[e + 2], sc[e + 3]});
+        } else {
+#pragma unroll
+          for (int e = 0; e < G * U; ++e) dst[e] = sc[e];
+        }
+      }
+    };
+    float m[G];  // wave max per head: all key groups (and the new key) share it
+    auto finish_max = [&]() {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float v = mx[g];
+#pragma unroll
+        for (int off = LPK; off < kWave; off <<= 1) v = max_nc(v, __shfl_xor(v, off));
+        m[g] = v;
+      }
+    };
+    float l[G];
+    f4 acc[G][NV4];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float s = 0.f;
+      l[g] = 0.f;
 #pragma unroll
-      for (int i = 0; i < NV4; ++i) s += dot4(q[g][i], kn[i]);
-      s = group_sum<LPK>(s);
-      if (gi == 0) {
-        m[g] = s;
-        l[g] = 1.f;
-#pragma unroll
-        for (int i = 0; i < NV4; ++i) acc[g][i] = vn[i];
-      }
+      for (int i = 0; i < NV4; ++i) acc[g][i] = f4{0.f, 0.f, 0.f, 0.f};
     }
-  }
-
-  // ---- history keys [t0, min(t0 + C, pos)) --------------------------------
-  const uint32_t t0 = it.chunk * p.chunk;
-  const uint32_t t_end = min(t0 + p.chunk, row.pos);
-  const float* kb = p.k_cache + slot_base;
-  const float* vb = p.v_cache + slot_base;
-  for (uint32_t base = t0; base < t_end; base += NG * U) {  // wave-uniform trip count
-    f4 kr[U][NV4], vr[U][NV4];
-    bool valid[U];
+    auto accumulate = [&](const Stage<D, G>& sg, uint32_t st) {
+      const float* src = sc_w + (st * NG + gi) * (G * U);
+      float sc[G * U];
+      if constexpr ((G * U) % 4 == 0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t t = base + gi + NG * u;
-      valid[u] = t < t_end;
-      if (valid[u]) {
-        const uint64_t o = static_cast<uint64_t>(t) * p.kv_dim;
-#pragma unroll
-        for (int i = 0; i < NV4; ++i) {
-          kr[u][i] = ld4_stream(kb + o + i * SL);
-          vr[u][i] = ld4_stream(vb + o + i * SL);
+        for (int e = 0; e < G * U; e += 4) {
+          const f4 v = ld4(src + e);
+          sc[e] = v[0];
+          sc[e + 1] = v[1];
+          sc[e + 2] = v[2];
+          sc[e + 3] = v[3];
         }
       } else {
 #pragma unroll
+        for (int e = 0; e < G * U; ++e) sc[e] = src[e];
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+#pragma unroll
+        for (int uu = 0; uu < U; ++uu) {
+          const float pu = fast_exp2(sc[g * U + uu] - m[g]);  // masked keys: exp2(-inf) = 0
+          l[g] += pu;
+#pragma unroll
+          for (int i = 0; i < NV4; ++i) acc[g][i] += pu * sg.x[uu][i];
+        }
+      }
+    };
+    // Stage loads run one ahead of use in two buffers: K stages, then V
+    // stages, then the next unit's first K stage (while this unit finishes).
+    // Stage index qi < n_st is K stage qi, qi >= n_st is V stage qi - n_st.
+    const uint32_t n_st = u.n_st;
+    auto prefetch = [&](Stage<D, G>& dst, uint32_t qi) {
+      if (qi < 2 * n_st) load_stage<D, G>(p, u, gi, lo, dst, qi);
+      else if (has_next) {
+        const UnitPlan nu = plan_unit<D, G>(a, un, w);
+        if (nu.n_st > 0) load_stage<D, G>(p, nu, gi, lo, dst, 0);
+      }
+    };
+    uint32_t st = 0;
+    for (; st + 1 < n_st; st += 2) {  // pass 1, two stages per trip
+      prefetch(B, st + 1);
+      score(A, st);
+      prefetch(A, st + 2);
+      score(B, st + 1);
+    }
+    if (st < n_st) {  // odd stage count: the last K stage is in A
+      prefetch(B, st + 1);
+      score(A, st);
+      A = B;
+    }
+    finish_max();
+    if (has_next) prep_finish<D, G>(a, un, w, lane, praw, prep, par ^ 1u);
+    for (st = 0; st + 1 < n_st; st += 2) {  // pass 2
+      prefetch(B, n_st + st + 1);
+      accumulate(A, st);
+      prefetch(A, n_st + st + 2);
+      accumulate(B, st + 1);
+    }
+    if (st < n_st) {
+      prefetch(B, n_st + st + 1);
+      accumulate(A, st);
+      A = B;
+    }
+    if (n_st == 0) prefetch(A, 0);
+    if (u.new_key && gi == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float pn = fast_exp2(s_new[g] - m[g]);
+        l[g] += pn;
+#pragma unroll
+        for (int i = 0; i < NV4; ++i) acc[g][i] += pn * vn[i];
+      }
+    }
+
+    // ---- sum the wave's key groups (they share m) ------------------------
+#pragma unroll
+    for (int off = LPK; off < kWave; off <<= 1) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        l[g] += __shfl_xor(l[g], off);
+#pragma unroll
         for (int i = 0; i < NV4; ++i) {
-          kr[u][i] = f4{0.f, 0.f, 0.f, 0.f};
-          vr[u][i] = f4{0.f, 0.f, 0.f, 0.f};
+          f4 other;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) other[c] = __shfl_xor(acc[g][i][c], off);
+          acc[g][i] += other;
         }
       }
     }
+
+    // ---- merge the NW waves through LDS -----------------------------------
+    if (gi == 0) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float s[U];
+      for (int g = 0; g < G; ++g) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float d = 0.f;
-#pragma unroll
-        for (int i = 0; i < NV4; ++i) d += dot4(q[g][i], kr[u][i]);
-        s[u] = group_sum<LPK>(d);
+        for (int i = 0; i < NV4; ++i) st4(&sh.acc[w][g][i * SL + lo], acc[g][i]);
       }
-      float mx = m[g];
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (valid[u]) mx = fmaxf(mx, s[u]);
-      const float corr = rescale(m[g], mx);
-      float pu[U];
-      float psum = 0.f;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        pu[u] = valid[u] ? fast_exp2(s[u] - mx) : 0.f;
-        psum += pu[u];
-      }
-      l[g] = l[g] * corr + psum;
-#pragma unroll
-      for (int i = 0; i < NV4; ++i) {
-        f4 a = acc[g][i] * corr;
-#pragma unroll
-        for (int u = 0; u < U; ++u) a += pu[u] * vr[u][i];
-        acc[g][i] = a;
-      }
-      m[g] = mx;
     }
+    if (lane == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        sh.m[w][g] = m[g];
+        sh.l[w][g] = l[g];
+      }
+    }
+    __syncthreads();
+    const uint32_t h0 = u.j * G;
+    const bool split = u.n_chunks > 1;
+    for (uint32_t e = tid; e < G * D; e += kThreads) {
+      const uint32_t g = e / D, d = e % D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < NW; ++v) M = fmaxf(M, sh.m[v][g]);
+      float L = 0.f, Acc = 0.f;
+#pragma unroll
+      for (int v = 0; v < NW; ++v) {
+        const float wv = rescale(sh.m[v][g], M);
+        L += sh.l[v][g] * wv;
+        Acc += sh.acc[v][g][d] * wv;
+      }
+      if (!split) {
+        // the whole row lives in this unit: add the sink and normalise
+        float sa = 1.f;
+        if (p.sinks) {
+          const float sk = p.sinks[h0 + g] * kLog2e;
+          const float mn = fmaxf(M, sk);
+          sa = fast_exp2(M - mn);
+          L = L * sa + (sk == -INFINITY ? 0.f : fast_exp2(sk - mn));
+        }
+        p.out[(static_cast<size_t>(u.b) * p.n_heads + h0 + g) * D + d] = Acc * (sa / L);
+      } else {
+        const size_t ph = (static_cast<size_t>(u.b) * p.max_chunks + u.chunk) * p.n_heads + h0 + g;
+#if SLOT_KV_FUSED_MERGE
+        store_agent(&p.part_acc[ph * D + d], Acc);
+        if (d == 0) {
+          store_agent(&p.part_ml[ph * 2 + 0], M);
+          store_agent(&p.part_ml[ph * 2 + 1], L);
+        }
+#else
+        p.part_acc[ph * D + d] = Acc;
+        if (d == 0) {
+          p.part_ml[ph * 2 + 0] = M;
+          p.part_ml[ph * 2 + 1] = L;
+        }
+#endif
+      }
+    }
+#if SLOT_KV_FUSED_MERGE
+    if (split) {  // workgroup-uniform
+      // The partials above are agent-coherent stores; once every wave's
+      // stores have completed (waitcnt) they are visible on every XCD, so
+      // the counter increment after the barrier publishes them.  The last
+      // workgroup of the (row, kv head) merges the row's chunks in order.
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0) {
+        const uint32_t done = __hip_atomic_fetch_add(&p.counters[u.b * p.n_kv_heads + u.j], 1u,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sh.last = (done == u.n_chunks - 1) ? 1u : 0u;
+      }
+      __syncthreads();
+      if (sh.last) {
+        merge_row<D, G>(p, u.b, u.j, u.n_chunks, tid, kThreads);
+        if (tid == 0)  // ready for the next launch
+          __hip_atomic_store(&p.counters[u.b * p.n_kv_heads + u.j], 0u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+#endif
+    __syncthreads();  // LDS free for the next unit; queue_slot visible
+    if (!has_next) break;
+    u = plan_unit<D, G>(a, un, w);
+    nxt = __builtin_amdgcn_readfirstlane(queue_slot[(it + 1) & 1]);
   }
 
-  // ---- merge the wave's key groups (butterfly over lane ^ LPK .. ^ 32) ----
-#pragma unroll
-  for (int off = LPK; off < kWave; off <<= 1) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float mo = __shfl_xor(m[g], off);
-      const float lo_ = __shfl_xor(l[g], off);
-      const float mn = fmaxf(m[g], mo);
-      const float c1 = rescale(m[g], mn), c2 = rescale(mo, mn);
-      l[g] = l[g] * c1 + lo_ * c2;
-#pragma unroll
-      for (int i = 0; i < NV4; ++i) {
-        f4 other;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) other[c] = __shfl_xor(acc[g][i][c], off);
-        acc[g][i] = acc[g][i] * c1 + other * c2;
-      }
-      m[g] = mn;
-    }
-  }
-
-  // ---- epilogue ------------------------------------------------------------
-  const uint32_t h0 = j * G;
-  if (row.n_chunks == 1) {
-    // the whole row lives in this item: add the sink and normalise
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float mf = m[g], lf = l[g], sa = 1.f;
-      if (p.sinks) {
-        const float sk = p.sinks[h0 + g] * kLog2e;
-        const float mn = fmaxf(mf, sk);
-        sa = fast_exp2(mf - mn);
-        lf = lf * sa + (sk == -INFINITY ? 0.f : fast_exp2(sk - mn));
-      }
-      const float inv = sa / lf;
-      if (gi == 0) {
-        float* o = p.out + (static_cast<size_t>(it.row) * p.n_heads + h0 + g) * D + lo;
-#pragma unroll
-        for (int i = 0; i < NV4; ++i) st4(o + i * SL, acc[g][i] * inv);
-      }
-    }
-  } else {
-    const size_t part = static_cast<size_t>(row.part_base) + it.chunk;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const size_t ph = part * p.n_heads + h0 + g;
-      if (gi == 0) {
-        float* o = p.part_acc + ph * D + lo;
-#pragma unroll
-        for (int i = 0; i < NV4; ++i) st4(o + i * SL, acc[g][i]);
-      }
-      if (lane == 0) {
-        p.part_ml[ph * 2 + 0] = m[g];
-        p.part_ml[ph * 2 + 1] = l[g];
-      }
+  if (tid == 0) {
+    // Every queue fetch of this workgroup has returned (its value ended the
+    // loop), so it is complete before this increment is issued.
+    const uint32_t exited = __hip_atomic_fetch_add(&p.sched[1], 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+    if (exited == n_blocks - 1) {
+      __hip_atomic_store(&p.sched[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&p.sched[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
 
-// Merge of the partial results of rows cut into several chunks: one wave per
-// (row, query head), chunks combined in index order.
-template <int D>
-__global__ void __launch_bounds__(kWave* kWavesPerBlock) merge_kernel(const AttnParams p) {
-  constexpr int EPL = D / kWave;  // elements per lane
-  const uint32_t lane = threadIdx.x % kWave;
-  const uint32_t wave = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
-  const uint32_t b = wave / p.n_heads, h = wave % p.n_heads;
-  if (b >= p.B) return;
-  const RowInfo row = p.rows[b];
-  if (row.n_chunks <= 1) return;
-  const size_t first = static_cast<size_t>(row.part_base) * p.n_heads + h;
-  float M = -INFINITY;
-  for (uint32_t c = 0; c < row.n_chunks; ++c)
-    M = fmaxf(M, p.part_ml[(first + static_cast<size_t>(c) * p.n_heads) * 2]);
-  float sk = -INFINITY;
-  if (p.sinks) {
-    sk = p.sinks[h] * kLog2e;
-    M = fmaxf(M, sk);
+// Merge of the partials of a row cut into several chunks, for the G query
+// heads of kv head j: chunks combined in index order (one online pass, eight
+// chunks' loads in flight at a time); the sink joins the denominator.
+template <int D, int G>
+__device__ __forceinline__ void merge_row(const AttnParams& p, uint32_t b, uint32_t j,
+                                          uint32_t n_chunks, uint32_t tid, uint32_t n_threads) {
+  const size_t first = static_cast<size_t>(b) * p.max_chunks;
+  for (uint32_t e = tid; e < G * D; e += n_threads) {
+    const uint32_t g = e / D, d = e % D;
+    const uint32_t h = j * G + g;
+    float M = -INFINITY, L = 0.f, Acc = 0.f;
+#pragma unroll 8
+    for (uint32_t c = 0; c < n_chunks; ++c) {
+      const size_t ph = (first + c) * p.n_heads + h;
+      const float mc = load_agent(&p.part_ml[ph * 2]);
+      const float lc = load_agent(&p.part_ml[ph * 2 + 1]);
+      const float ac = load_agent(&p.part_acc[ph * D + d]);
+      const float mn = fmaxf(M, mc);
+      const float s_old = rescale(M, mn), s_new = fast_exp2(mc - mn);
+      L = L * s_old + lc * s_new;
+      Acc = Acc * s_old + ac * s_new;
+      M = mn;
+    }
+    if (p.sinks) {
+      const float sk = p.sinks[h] * kLog2e;
+      if (sk != -INFINITY) {
+        const float mn = fmaxf(M, sk);
+        const float s_old = fast_exp2(M - mn);
+        L = L * s_old + fast_exp2(sk - mn);
+        Acc *= s_old;
+      }
+    }
+    p.out[(static_cast<size_t>(b) * p.n_heads + h) * D + d] = Acc / L;
   }
-  float L = 0.f, o[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) o[e] = 0.f;
-  for (uint32_t c = 0; c < row.n_chunks; ++c) {
-    const size_t ph = first + static_cast<size_t>(c) * p.n_heads;
-    const float w = fast_exp2(p.part_ml[ph * 2] - M);
-    L += p.part_ml[ph * 2 + 1] * w;
-    const float* a = p.part_acc + ph * D + lane * EPL;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] += a[e] * w;
-  }
-  if (sk != -INFINITY) L += fast_exp2(sk - M);
-  const float inv = 1.0f / L;
-  float* dst = p.out + (static_cast<size_t>(b) * p.n_heads + h) * D + lane * EPL;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) dst[e] = o[e] * inv;
+}
+
+// Stand-alone merge (when the decode kernel does not merge): one workgroup
+// per (row, kv head).
+template <int D, int G>
+__global__ void __launch_bounds__(256) merge_kernel(const AttnArgs a) {
+  if (a.magic != kArgsMagic) return;
+  const AttnParams& p = a.p;
+  const uint32_t b = blockIdx.x / p.n_kv_heads, j = blockIdx.x % p.n_kv_heads;
+  if (b >= p.n_rows) return;
+  const uint32_t n_chunks = a.rows.pos[b] / p.chunk + 1;
+  if (n_chunks == 1) return;  // finished by the decode kernel
+  merge_row<D, G>(p, b, j, n_chunks, threadIdx.x, 256);
 }
 
 template <int D, int G>
-hipError_t launch_shape(const AttnParams& p, bool any_split, hipStream_t s, hipEvent_t mark) {
-  const uint32_t blocks = (p.n_waves + kWavesPerBlock - 1) / kWavesPerBlock;
-  hipLaunchKernelGGL((decode_attn_kernel<D, G>), dim3(blocks), dim3(kWave * kWavesPerBlock), 0, s,
-                     p);
+hipError_t launch_shape(const AttnArgs& a, uint32_t blocks, hipStream_t s, hipEvent_t mark) {
+  hipLaunchKernelGGL((decode_attn_kernel<D, G>), dim3(blocks), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && mark) e = hipEventRecord(mark, s);
-  if (e != hipSuccess || !any_split) return e;
-  const uint32_t mwaves = p.B * p.n_heads;
-  const uint32_t mblocks = (mwaves + kWavesPerBlock - 1) / kWavesPerBlock;
-  hipLaunchKernelGGL((merge_kernel<D>), dim3(mblocks), dim3(kWave * kWavesPerBlock), 0, s, p);
+  if (e != hipSuccess || a.p.max_chunks <= 1 || SLOT_KV_FUSED_MERGE) return e;
+  hipLaunchKernelGGL((merge_kernel<D, G>), dim3(a.p.n_rows * a.p.n_kv_heads), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
+template <int D, int G>
+uint32_t resident_shape() {
+  static uint32_t cached = 0;  // one device per process is the supported setup
+  if (!cached) {
+    int per_cu = 0, cus = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_attn_kernel<D, G>,
+                                                     kThreads, 0) != hipSuccess)
+      return 0;
+    cached = static_cast<uint32_t>(per_cu > 0 ? per_cu : 1) * static_cast<uint32_t>(cus);
+  }
+  return cached;
+}
+
 template <int D>
-hipError_t launch_d(const AttnParams& p, uint32_t G, bool any_split, hipStream_t s,
+hipError_t launch_d(const AttnArgs& a, uint32_t G, uint32_t blocks, hipStream_t s,
                     hipEvent_t mark) {
   switch (G) {
-    case 1: return launch_shape<D, 1>(p, any_split, s, mark);
-    case 2: return launch_shape<D, 2>(p, any_split, s, mark);
-    case 4: return launch_shape<D, 4>(p, any_split, s, mark);
-    case 8: return launch_shape<D, 8>(p, any_split, s, mark);
+    case 1: return launch_shape<D, 1>(a, blocks, s, mark);
+    case 2: return launch_shape<D, 2>(a, blocks, s, mark);
+    case 4: return launch_shape<D, 4>(a, blocks, s, mark);
+    case 8: return launch_shape<D, 8>(a, blocks, s, mark);
     default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D>
+uint32_t resident_d(uint32_t G) {
+  switch (G) {
+    case 1: return resident_shape<D, 1>();
+    case 2: return resident_shape<D, 2>();
+    case 4: return resident_shape<D, 4>();
+    case 8: return resident_shape<D, 8>();
+    default: return 0;
   }
 }
 
@@ -412,15 +771,24 @@ bool decode_shape_supported(uint32_t head_dim, uint32_t group) {
   return d_ok && g_ok;
 }
 
-int launch_decode(const AttnParams& p, uint32_t head_dim, uint32_t group, bool any_split,
-                  void* stream, void* after_attn) {
+int launch_decode(const AttnArgs& a, uint32_t head_dim, uint32_t group, uint32_t blocks,
+                  void* stream, void* after_decode) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipEvent_t mark = static_cast<hipEvent_t>(after_attn);
+  hipEvent_t mark = static_cast<hipEvent_t>(after_decode);
   switch (head_dim) {
-    case 64: return launch_d<64>(p, group, any_split, s, mark);
-    case 128: return launch_d<128>(p, group, any_split, s, mark);
-    case 256: return launch_d<256>(p, group, any_split, s, mark);
+    case 64: return launch_d<64>(a, group, blocks, s, mark);
+    case 128: return launch_d<128>(a, group, blocks, s, mark);
+    case 256: return launch_d<256>(a, group, blocks, s, mark);
     default: return hipErrorInvalidValue;
+  }
+}
+
+uint32_t resident_blocks(uint32_t head_dim, uint32_t group) {
+  switch (head_dim) {
+    case 64: return resident_d<64>(group);
+    case 128: return resident_d<128>(group);
+    case 256: return resident_d<256>(group);
+    default: return 0;
   }
 }
 

@@ -1,4 +1,4 @@
-// slot_kv_plan.cpp -- host-side validation and split-K planning of one
+// slot_kv_plan.cpp -- host-side validation and split-K row tables of one
 // decode call.  Plain C++ (no HIP), so it also runs where no GPU is present.
 //
 // Preconditions follow "Forward Cuda Gemma", decodeBatch: n_slots >
@@ -29,40 +29,28 @@ int check_batch(uint32_t n_slots, uint32_t slot_ctx, const uint32_t* positions,
   return SLOT_KV_OK;
 }
 
-uint32_t count_items(const uint32_t* positions, uint32_t B, uint32_t chunk) {
-  uint64_t n = 0;
-  for (uint32_t b = 0; b < B; ++b) n += (uint64_t(positions[b]) + chunk) / chunk;
-  return static_cast<uint32_t>(n);
-}
-
-Plan build_plan(const uint32_t* positions, const uint32_t* slots, uint32_t B,
-                uint32_t chunk, RowInfo* rows, WorkItem* items) {
-  Plan plan;
-  uint32_t part = 0;
-  for (uint32_t b = 0; b < B; ++b) {
-    const uint32_t nc = (positions[b] + chunk) / chunk;  // ceil((pos+1)/chunk)
-    rows[b] = RowInfo{positions[b], slots[b], nc > 1 ? part : 0u, nc};
-    if (nc > 1) {
-      part += nc;
-      ++plan.n_split_rows;
-    }
-  }
-  plan.n_parts = part;
-  // Full chunks first (row order), then each row's shorter last chunk, the
-  // longest first: equal-cost items fill the machine, short ones close the tail.
-  uint32_t n = 0;
-  std::vector<std::pair<uint32_t, uint32_t>> tails;  // (keys, row)
-  for (uint32_t b = 0; b < B; ++b) {
+LaunchWork fill_rows(LaunchRows& rows, const uint32_t* positions, const uint32_t* slots,
+                     uint32_t n, uint32_t chunk) {
+  LaunchWork work;
+  uint32_t tails[kMaxRowsPerLaunch];
+  uint32_t n_tails = 0;
+  for (uint32_t b = 0; b < n; ++b) {
     const uint32_t keys = positions[b] + 1;
-    const uint32_t full = keys / chunk;
-    for (uint32_t c = 0; c < full; ++c) items[n++] = WorkItem{b, c};
-    if (keys % chunk) tails.emplace_back(keys % chunk, b);
+    rows.pos[b] = positions[b];
+    rows.slot[b] = slots[b];
+    rows.full_prefix[b] = work.n_full;
+    work.n_full += keys / chunk;
+    if (keys % chunk) tails[n_tails++] = b;
+    work.max_chunks = std::max(work.max_chunks, (keys + chunk - 1) / chunk);
   }
-  std::stable_sort(tails.begin(), tails.end(),
-                   [](const auto& a, const auto& b) { return a.first > b.first; });
-  for (const auto& t : tails) items[n++] = WorkItem{t.second, rows[t.second].n_chunks - 1};
-  plan.n_items = n;
-  return plan;
+  rows.full_prefix[n] = work.n_full;
+  // longest partial chunk first; ties keep row order
+  std::stable_sort(tails, tails + n_tails, [&](uint32_t x, uint32_t y) {
+    return (positions[x] + 1) % chunk > (positions[y] + 1) % chunk;
+  });
+  for (uint32_t t = 0; t < n_tails; ++t) rows.tail_row[t] = static_cast<uint8_t>(tails[t]);
+  work.n_items = work.n_full + n_tails;
+  return work;
 }
 
 }  // namespace slotkv
