@@ -25,6 +25,9 @@ SOURCES = ["slot_kv_api.hip", "slot_kv_kernels.hip", "slot_kv_plan.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # every atomic in the kernels is issued by a single lane; the
+          # wave-aggregating rewrite would read each result at once
+          "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
           "-I", INCLUDE, "-I", CSRC]
 
 

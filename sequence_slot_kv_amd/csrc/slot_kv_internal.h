@@ -25,6 +25,7 @@ struct LaunchRows {
   uint32_t full_prefix[kMaxRowsPerLaunch + 1];  // full chunks of the rows before b
   uint8_t tail_row[kMaxRowsPerLaunch];          // rows owning a partial chunk, longest first
 };
+static_assert(offsetof(LaunchRows, tail_row) % 4 == 0, "tail_row is read through 32-bit words");
 
 // Kernel-side parameters of one decode launch (rows 0..n_rows-1 of it).
 struct AttnParams {

@@ -13,7 +13,7 @@
 //     row's last chunk also writes the row's KV entry -- rotated key and
 //     v_new at (slot*slot_ctx + pos)*kv_dim -- from that staging step;
 //   - the next unit's first K stage is in flight while the current unit
-//     finishes.
+//     waits for its split-row counter.
 // Per unit and wave, two passes stream the history rows once each with
 // 128-bit non-temporal loads, double-buffered: pass 1 reads K, computes the
 // scores (LPK lanes per key row, DPP reductions) into LDS and the running
@@ -127,6 +127,16 @@ __device__ __forceinline__ float rescale(float m, float m_new) {
   return m == -INFINITY ? 0.f : fast_exp2(m - m_new);
 }
 
+constexpr uint32_t kNoUnit = 0xffffffffu;  // mailbox empty
+
+// Wait for another wave of the workgroup to post a value in LDS.
+__device__ __forceinline__ uint32_t mbox_wait(const uint32_t* slot) {
+  uint32_t v;
+  while ((v = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) == kNoUnit)
+    __builtin_amdgcn_s_sleep(1);
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
 template <int D, int G>
 struct alignas(16) Lds {
   float acc[NW][G][D];
@@ -160,7 +170,7 @@ struct Shape {
 // j; the wave owns history keys [k_begin, k_begin + len) of that chunk.
 struct UnitPlan {
   uint32_t b, j, chunk, pos, slot, n_chunks;
-  uint32_t k_begin, len, n_full, n_st;  // n_st = stages per pass (last may be partial)
+  uint32_t k_begin, len, n_full, n_st;  // n_st = stages per pass, even; those past n_full masked
   bool new_key;                         // this wave also owns the row's new key
 };
 
@@ -184,7 +194,10 @@ __device__ __forceinline__ UnitId locate_unit(const AttnArgs& a, uint32_t unit) 
     id.b = blo;
     id.chunk = item - a.rows.full_prefix[id.b];
   } else {
-    id.b = a.rows.tail_row[item - p.n_full];
+    // the byte through its aligned word, so that the read stays a scalar load
+    const uint32_t t = item - p.n_full;
+    const uint32_t word = reinterpret_cast<const uint32_t*>(a.rows.tail_row)[t / 4];
+    id.b = (word >> (8 * (t % 4))) & 0xffu;
     id.chunk = a.rows.pos[id.b] / p.chunk;  // the partial last chunk
   }
   return id;
@@ -207,7 +220,10 @@ __device__ __forceinline__ UnitPlan plan_unit(const AttnArgs& a, const UnitId& i
   u.k_begin = min(c0 + w * per_wave, t_end);
   u.len = min(c0 + (w + 1) * per_wave, t_end) - u.k_begin;
   u.n_full = u.len / S::STEP;
-  u.n_st = u.n_full + (u.len % S::STEP != 0 ? 1u : 0u);
+  // stages per pass, rounded up to an even count (the stages past the keys
+  // are masked) so that each pass ends in the same buffer
+  const uint32_t n_st = u.n_full + (u.len % S::STEP != 0 ? 1u : 0u);
+  u.n_st = (n_st + 1) & ~1u;
   u.new_key = (w == 0) && (u.chunk == u.n_chunks - 1);
   return u;
 }
@@ -217,35 +233,31 @@ struct Stage {
   f4 x[Shape<D, G>::U][Shape<D, G>::NV4];
 };
 
-// Stage qi of a unit: K stage qi for qi < n_st, else V stage qi - n_st.
+// Stage qi of a unit (n_st >= 1): K stage qi for qi < n_st, else V stage
+// qi - n_st.  Every call issues the same U*NV4 loads whatever the stage: a
+// key past the wave's range re-reads the wave's last key row (pass 1 masks
+// its score to -inf, so pass 2 gives it weight 0).  The count of loads in
+// flight therefore never depends on the data, and the compiler can leave one
+// stage in flight while the other is consumed.
 template <int D, int G>
 __device__ __forceinline__ void load_stage(const AttnParams& p, const UnitPlan& u, uint32_t gi,
                                            uint32_t lo, Stage<D, G>& sg, uint32_t qi) {
   using S = Shape<D, G>;
   const bool is_v = qi >= u.n_st;
   const uint32_t st = is_v ? qi - u.n_st : qi;
-  const uint64_t row = static_cast<uint64_t>(u.k_begin + st * S::STEP + gi);
   const float* base = (is_v ? p.v_cache : p.k_cache) + static_cast<uint64_t>(u.slot) * p.slot_stride +
-                      row * p.kv_dim + u.j * D + lo;
-  if (st < u.n_full) {
+                      u.j * D + lo;
+  const uint32_t first = u.k_begin + st * S::STEP + gi;
+  const uint32_t last = u.k_begin + u.len - 1;
 #pragma unroll
-    for (int uu = 0; uu < S::U; ++uu)
+  for (int uu = 0; uu < S::U; ++uu) {
+    const uint32_t row = min(first + S::NG * uu, last);
+    const float* r = base + static_cast<uint64_t>(row) * p.kv_dim;
 #pragma unroll
-      for (int i = 0; i < S::NV4; ++i)
-        sg.x[uu][i] = ld4_stream(base + static_cast<uint64_t>(S::NG * uu) * p.kv_dim + i * S::SL);
-  } else {
-#pragma unroll
-    for (int uu = 0; uu < S::U; ++uu) {
-      if (st * S::STEP + gi + S::NG * uu < u.len) {
-#pragma unroll
-        for (int i = 0; i < S::NV4; ++i)
-          sg.x[uu][i] = ld4_stream(base + static_cast<uint64_t>(S::NG * uu) * p.kv_dim + i * S::SL);
-      } else {
-#pragma unroll
-        for (int i = 0; i < S::NV4; ++i) sg.x[uu][i] = f4{0.f, 0.f, 0.f, 0.f};
-      }
-    }
+    for (int i = 0; i < S::NV4; ++i) sg.x[uu][i] = ld4_stream(r + i * S::SL);
   }
+  // keep the loads ahead of the work on the other buffer
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // The next unit's query heads (and its new key) are normalised and rotated
@@ -264,7 +276,25 @@ struct PrepRaw {
   static constexpr int EPL = D / kWave;
   static constexpr int SLOTS = (G + 1 + NW - 1) / NW;
   float x[SLOTS][EPL];
+  float vn[EPL];  // v_new of the row, for the wave that holds the new key
 };
+// The lane's norm weights and RoPE frequencies, the same for every unit.
+template <int D>
+struct PrepConst {
+  static constexpr int EPL = D / kWave;
+  float wq[EPL], wk[EPL], freq[EPL];
+};
+template <int D>
+__device__ __forceinline__ PrepConst<D> prep_const(const AttnParams& p, uint32_t lane) {
+  PrepConst<D> c;
+#pragma unroll
+  for (int e = 0; e < PrepConst<D>::EPL; ++e) {
+    c.wq[e] = p.q_norm_w[lane * PrepConst<D>::EPL + e];
+    c.wk[e] = p.k_norm_w[lane * PrepConst<D>::EPL + e];
+    c.freq[e] = p.inv_freq[(lane & 31) * PrepConst<D>::EPL + e];
+  }
+  return c;
+}
 
 __device__ __forceinline__ float wave_sum(float v) {
   v = group_sum<16>(v);
@@ -291,13 +321,19 @@ __device__ __forceinline__ void prep_issue(const AttnArgs& a, const UnitId& id, 
                              : p.k_new + static_cast<size_t>(id.b) * p.kv_dim + id.j * D;
 #pragma unroll
     for (int e = 0; e < R::EPL; ++e) raw.x[s][e] = src[lane * R::EPL + e];
+    if (v == G) {
+      const float* vsrc = p.v_new + static_cast<size_t>(id.b) * p.kv_dim + id.j * D;
+#pragma unroll
+      for (int e = 0; e < R::EPL; ++e) raw.vn[e] = vsrc[lane * R::EPL + e];
+    }
   }
 }
 
 template <int D, int G>
 __device__ __forceinline__ void prep_finish(const AttnArgs& a, const UnitId& id, uint32_t w,
-                                            uint32_t lane, PrepRaw<D, G>& raw,
-                                            PrepLds<D, G>& prep, uint32_t par) {
+                                            uint32_t lane, const PrepRaw<D, G>& raw,
+                                            const PrepConst<D>& pc, PrepLds<D, G>& prep,
+                                            uint32_t par) {
   using R = PrepRaw<D, G>;
   const AttnParams& p = a.p;
   const uint32_t pos = a.rows.pos[id.b];
@@ -306,23 +342,26 @@ __device__ __forceinline__ void prep_finish(const AttnArgs& a, const UnitId& id,
   for (int s = 0; s < R::SLOTS; ++s) {
     const uint32_t v = w + s * NW;
     if (!prep_has<D, G>(a, id, v)) continue;  // wave-uniform
-    const float* wts = v < G ? p.q_norm_w : p.k_norm_w;
-    float ss = 0.f;
+    // norm with weights wts, then RoPE at pos (two inlined copies, so that
+    // each reads its weights straight from registers)
+    auto norm_rope = [&](const float (&wts)[R::EPL], float (&y)[R::EPL]) {
+      float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < R::EPL; ++e) ss += raw.x[s][e] * raw.x[s][e];
-    ss = wave_sum(ss);
-    const float rn = 1.0f / sqrtf(ss * (1.0f / D) + p.eps);
+      for (int e = 0; e < R::EPL; ++e) ss += raw.x[s][e] * raw.x[s][e];
+      ss = wave_sum(ss);
+      const float rn = 1.0f / sqrtf(ss * (1.0f / D) + p.eps);
+#pragma unroll
+      for (int e = 0; e < R::EPL; ++e) {
+        const float x = raw.x[s][e] * rn * wts[e];
+        const float partner = __shfl_xor(x, 32);
+        const float ang = fpos * pc.freq[e];  // one f32 multiply
+        float sn, cs;
+        sincosf(ang, &sn, &cs);
+        y[e] = lane < 32 ? x * cs - partner * sn : x * cs + partner * sn;
+      }
+    };
     float y[R::EPL];
-#pragma unroll
-    for (int e = 0; e < R::EPL; ++e) {
-      const uint32_t d = lane * R::EPL + e;
-      const float x = raw.x[s][e] * rn * wts[d];
-      const float partner = __shfl_xor(x, 32);
-      const float ang = fpos * p.inv_freq[(lane & 31) * R::EPL + e];  // one f32 multiply
-      float sn, cs;
-      sincosf(ang, &sn, &cs);
-      y[e] = lane < 32 ? x * cs - partner * sn : x * cs + partner * sn;
-    }
+    if (v < G) norm_rope(pc.wq, y); else norm_rope(pc.wk, y);
     if (v < G) {
 #pragma unroll
       for (int e = 0; e < R::EPL; ++e) prep.q[par][v][lane * R::EPL + e] = y[e] * p.qk_scale_log2;
@@ -330,12 +369,11 @@ __device__ __forceinline__ void prep_finish(const AttnArgs& a, const UnitId& id,
       // the step's KV write: rotated key and v_new at (slot*slot_ctx + pos)*kv_dim
       const uint64_t at = static_cast<uint64_t>(a.rows.slot[id.b]) * p.slot_stride +
                           static_cast<uint64_t>(pos) * p.kv_dim + id.j * D + lane * R::EPL;
-      const float* vsrc = p.v_new + static_cast<size_t>(id.b) * p.kv_dim + id.j * D + lane * R::EPL;
 #pragma unroll
       for (int e = 0; e < R::EPL; ++e) {
         prep.kn[par][lane * R::EPL + e] = y[e];
         p.k_cache[at + e] = y[e];
-        p.v_cache[at + e] = vsrc[e];
+        p.v_cache[at + e] = raw.vn[e];
       }
     }
   }
@@ -346,13 +384,16 @@ __device__ __forceinline__ void merge_row(const AttnParams& p, uint32_t b, uint3
                                           uint32_t n_chunks, uint32_t tid, uint32_t n_threads);
 
 // Persistent decode kernel: as many workgroups as are resident at once.
-// Workgroup g starts with unit g, then takes units from an agent-scope queue
-// that it reads one unit ahead, so the next unit's first loads are in flight
-// while the current unit finishes.  Units are ordered full chunks first, then
-// partial chunks longest first, so the work left at the end is short.  The
-// last workgroup to exit returns the queue to zero for the next launch.  No
-// workgroup ever waits for another.  A row of one chunk is finished here; a
-// longer row leaves one unnormalised partial per chunk for merge_kernel.
+// Workgroup g starts with unit g, then takes units from an agent-scope queue.
+// Each unit asks the queue for the one after it as it starts; wave 0 posts
+// the answer in an LDS mailbox after its first K stages and the other waves
+// read it there, so every workgroup holds at most one unit it has not begun,
+// and only for the second half of a unit.  Units are ordered full chunks
+// first, then partial chunks longest first, so the work left at the end is
+// short.  The last workgroup to exit returns the queue to zero for the next
+// launch.  No workgroup ever waits for another.  A row of one chunk is
+// finished here; a longer row leaves one unnormalised partial per chunk,
+// merged by the row's last workgroup (or by merge_kernel).
 template <int D, int G>
 __global__ void __launch_bounds__(kThreads)
     __attribute__((amdgpu_waves_per_eu(waves_per_eu<D, G>()))) decode_attn_kernel(const AttnArgs a) {
@@ -360,7 +401,7 @@ __global__ void __launch_bounds__(kThreads)
   constexpr int LPK = S::LPK, U = S::U, NV4 = S::NV4, NG = S::NG, SL = S::SL, STEP = S::STEP;
   __shared__ Lds<D, G> sh;
   __shared__ __attribute__((aligned(16))) float sc_lds[NW][S::SCORES];
-  __shared__ uint32_t queue_slot[2];
+  __shared__ uint32_t mbox[2];  // next unit, by unit parity; kNoUnit until posted
   __shared__ PrepLds<D, G> prep;
   if (a.magic != kArgsMagic) return;  // argument block not delivered whole
   const AttnParams& p = a.p;
@@ -371,30 +412,48 @@ __global__ void __launch_bounds__(kThreads)
   const uint32_t lo = 4 * (lane % LPK);  // lane's float offset inside a slice
   const uint32_t n_blocks = gridDim.x;
 
-  if (tid == 0)
-    queue_slot[0] = __hip_atomic_fetch_add(&p.sched[0], 1u, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT) + n_blocks;
-  __syncthreads();
-  uint32_t nxt = __builtin_amdgcn_readfirstlane(queue_slot[0]);
+  if (tid == 0) {
+    mbox[0] = kNoUnit;
+    mbox[1] = kNoUnit;
+  }
   const UnitId first = locate_unit(a, blockIdx.x);  // blocks <= n_units
   UnitPlan u = plan_unit<D, G>(a, first, w);
   Stage<D, G> A, B;
   if (u.n_st > 0) load_stage<D, G>(p, u, gi, lo, A, 0);  // A always holds the next stage
+  const PrepConst<D> pconst = prep_const<D>(p, lane);
   PrepRaw<D, G> praw;
   prep_issue<D, G>(a, first, w, lane, praw);
-  prep_finish<D, G>(a, first, w, lane, praw, prep, 0);
+  prep_finish<D, G>(a, first, w, lane, praw, pconst, prep, 0);
   __syncthreads();
 
   for (uint32_t it = 0;; ++it) {  // workgroup-uniform
-    const bool has_next = nxt < p.n_units;
-    if (tid == 0 && has_next)
-      queue_slot[(it + 1) & 1] = __hip_atomic_fetch_add(&p.sched[0], 1u, __ATOMIC_RELAXED,
-                                                        __HIP_MEMORY_SCOPE_AGENT) + n_blocks;
+    const uint32_t par = it & 1;
+    // the unit after this one: asked for now, read after the first K stages
+    uint32_t ticket = 0;
+    if (tid == 0)
+      ticket = __hip_atomic_fetch_add(&p.sched[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t nxt = kNoUnit;
+    bool has_next = false;
     UnitId un{};
-    if (has_next) un = locate_unit(a, nxt);
+    // Wave 0 posts the next unit in the mailbox (every wave of it reads the
+    // ticket register, so that no write to it is outstanding when the next
+    // unit sets it again); the other waves wait for the post, which wave 0
+    // makes before it waits for any other wave.  The raw next queries go out.
+    auto take_next = [&]() {
+      if (w == 0) {
+        nxt = __builtin_amdgcn_readfirstlane(ticket) + n_blocks;
+        if (lane == 0) __hip_atomic_store(&mbox[par], nxt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      } else {
+        nxt = mbox_wait(&mbox[par]);
+      }
+      has_next = nxt < p.n_units;
+      if (has_next) {
+        un = locate_unit(a, nxt);
+        prep_issue<D, G>(a, un, w, lane, praw);  // consumed after pass 1
+      }
+    };
 
     // ---- prologue: queries and new key from LDS ------------------------------
-    const uint32_t par = it & 1;
     f4 q[G][NV4];
 #pragma unroll
     for (int g = 0; g < G; ++g)
@@ -422,7 +481,6 @@ __global__ void __launch_bounds__(kThreads)
         mx[g] = s_new[g];
       }
     }
-    if (has_next) prep_issue<D, G>(a, un, w, lane, praw);  // consumed after pass 1
 
     // ---- two passes over this wave's history keys ------------------------
     // Pass 1 streams the K rows, keeps each key's scores (log2 units) in LDS
@@ -506,42 +564,45 @@ __global__ void __launch_bounds__(kThreads)
       }
     };
     // Stage loads run one ahead of use in two buffers: K stages, then V
-    // stages, then the next unit's first K stage (while this unit finishes).
-    // Stage index qi < n_st is K stage qi, qi >= n_st is V stage qi - n_st.
+    // stages; stage index qi < n_st is K stage qi, qi >= n_st is V stage
+    // qi - n_st.  n_st is even, so each pass starts in A.  The last V stage
+    // is consumed with nothing behind it; the next unit's first K stage goes
+    // out once this unit's results are stored.  The staging of the next
+    // unit's queries sits on both sides of the branch so that its wait for
+    // their loads only covers the loads issued before them.
     const uint32_t n_st = u.n_st;
-    auto prefetch = [&](Stage<D, G>& dst, uint32_t qi) {
-      if (qi < 2 * n_st) load_stage<D, G>(p, u, gi, lo, dst, qi);
-      else if (has_next) {
-        const UnitPlan nu = plan_unit<D, G>(a, un, w);
-        if (nu.n_st > 0) load_stage<D, G>(p, nu, gi, lo, dst, 0);
+    if (n_st > 0) {  // wave-uniform
+      // pass 1; the next unit is taken between the first two stages (loads
+      // follow it on every path, so that its wait for the raw queries later
+      // leaves the stage in flight alone)
+      load_stage<D, G>(p, u, gi, lo, B, 1);
+      score(A, 0);
+      take_next();
+      load_stage<D, G>(p, u, gi, lo, A, 2);  // V stage 0 when n_st == 2
+      score(B, 1);
+      for (uint32_t st = 2; st < n_st; st += 2) {
+        load_stage<D, G>(p, u, gi, lo, B, st + 1);
+        score(A, st);
+        load_stage<D, G>(p, u, gi, lo, A, st + 2);  // the last trip loads V stage 0
+        score(B, st + 1);
       }
-    };
-    uint32_t st = 0;
-    for (; st + 1 < n_st; st += 2) {  // pass 1, two stages per trip
-      prefetch(B, st + 1);
-      score(A, st);
-      prefetch(A, st + 2);
-      score(B, st + 1);
-    }
-    if (st < n_st) {  // odd stage count: the last K stage is in A
-      prefetch(B, st + 1);
-      score(A, st);
-      A = B;
-    }
-    finish_max();
-    if (has_next) prep_finish<D, G>(a, un, w, lane, praw, prep, par ^ 1u);
-    for (st = 0; st + 1 < n_st; st += 2) {  // pass 2
-      prefetch(B, n_st + st + 1);
+      finish_max();
+      if (has_next) prep_finish<D, G>(a, un, w, lane, praw, pconst, prep, par ^ 1u);
+      uint32_t st = 0;
+      for (; st + 2 < n_st; st += 2) {  // pass 2 while two more stages follow
+        load_stage<D, G>(p, u, gi, lo, B, n_st + st + 1);
+        accumulate(A, st);
+        load_stage<D, G>(p, u, gi, lo, A, n_st + st + 2);
+        accumulate(B, st + 1);
+      }
+      load_stage<D, G>(p, u, gi, lo, B, n_st + st + 1);  // the last stage
       accumulate(A, st);
-      prefetch(A, n_st + st + 2);
       accumulate(B, st + 1);
+    } else {
+      take_next();
+      finish_max();
+      if (has_next) prep_finish<D, G>(a, un, w, lane, praw, pconst, prep, par ^ 1u);
     }
-    if (st < n_st) {
-      prefetch(B, n_st + st + 1);
-      accumulate(A, st);
-      A = B;
-    }
-    if (n_st == 0) prefetch(A, 0);
     if (u.new_key && gi == 0) {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -625,20 +686,31 @@ __global__ void __launch_bounds__(kThreads)
 #endif
       }
     }
+    // the next unit's first K stage into A
+    auto prefetch_next = [&]() {
+      if (has_next) {
+        const UnitPlan nu = plan_unit<D, G>(a, un, w);
+        if (nu.n_st > 0) load_stage<D, G>(p, nu, gi, lo, A, 0);
+      }
+    };
 #if SLOT_KV_FUSED_MERGE
     if (split) {  // workgroup-uniform
       // The partials above are agent-coherent stores; once every wave's
       // stores have completed (waitcnt) they are visible on every XCD, so
       // the counter increment after the barrier publishes them.  The last
       // workgroup of the (row, kv head) merges the row's chunks in order.
+      // No history load is in flight here, so the wait costs only the stores.
+      // The next unit's first K stage goes out while the counter's round
+      // trip is pending.
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (tid == 0) {
-        const uint32_t done = __hip_atomic_fetch_add(&p.counters[u.b * p.n_kv_heads + u.j], 1u,
-                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        sh.last = (done == u.n_chunks - 1) ? 1u : 0u;
-      }
+      uint32_t done = 0;
+      if (tid == 0)
+        done = __hip_atomic_fetch_add(&p.counters[u.b * p.n_kv_heads + u.j], 1u,
+                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      prefetch_next();
+      if (tid == 0) sh.last = (done == u.n_chunks - 1) ? 1u : 0u;
       __syncthreads();
       if (sh.last) {
         merge_row<D, G>(p, u.b, u.j, u.n_chunks, tid, kThreads);
@@ -646,12 +718,17 @@ __global__ void __launch_bounds__(kThreads)
           __hip_atomic_store(&p.counters[u.b * p.n_kv_heads + u.j], 0u, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
       }
+    } else {
+      prefetch_next();
     }
+#else
+    prefetch_next();
 #endif
-    __syncthreads();  // LDS free for the next unit; queue_slot visible
+    if (tid == 0)  // every wave read it before the merge barrier
+      __hip_atomic_store(&mbox[par], kNoUnit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __syncthreads();  // LDS free for the next unit
     if (!has_next) break;
     u = plan_unit<D, G>(a, un, w);
-    nxt = __builtin_amdgcn_readfirstlane(queue_slot[(it + 1) & 1]);
   }
 
   if (tid == 0) {
