@@ -68,6 +68,10 @@ def _load():
             u32, u32, u32, f32p, f32p, f32p, f32p, ctypes.c_float, ctypes.c_float,
             f32p, f32p, u32, u32, f32p, f32p, f32p, u32p, u32p, u32, f32p]
         lib.oracle_decode_batch.restype = ctypes.c_int
+        lib.oracle_prefill.argtypes = [
+            u32, u32, u32, f32p, f32p, f32p, f32p, ctypes.c_float, ctypes.c_float,
+            f32p, f32p, u32, u32, f32p, f32p, f32p, u32, u32, u32, f32p]
+        lib.oracle_prefill.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -172,4 +176,26 @@ def decode_batch(layer, cache_k, cache_v, q, k_new, v_new, positions, slots):
         _f32(np.ascontiguousarray(k_new, np.float32), "k_new"),
         _f32(np.ascontiguousarray(v_new, np.float32), "v_new"),
         _u32(positions, "positions"), _u32(slots, "slots"), B, _f32(out, "out"))
+    return rc, out
+
+
+def prefill(layer, cache_k, cache_v, q, k_new, v_new, slot, pos0):
+    """Slot prefill over host mirrors ``cache_k`` / ``cache_v``
+    [n_slots, slot_ctx, kv_dim] float32 (updated in place): the T rows of q,
+    k_new, v_new are tokens at positions pos0 .. pos0+T-1 of ``slot``.
+    Returns (status, out[T, n_heads*head_dim])."""
+    L = layer
+    n_slots, slot_ctx, kv_dim = cache_k.shape
+    if kv_dim != L.n_kv_heads * L.head_dim or cache_v.shape != cache_k.shape:
+        raise ValueError("cache shape does not match the layer")
+    q = np.ascontiguousarray(q, np.float32)
+    T = q.shape[0]
+    out = np.zeros((T, L.n_heads * L.head_dim), np.float32)
+    rc = _load().oracle_prefill(
+        L.n_heads, L.n_kv_heads, L.head_dim, _f32(L.q_norm_w, "q_norm_w"),
+        _f32(L.k_norm_w, "k_norm_w"), _f32(L.inv_freq, "inv_freq"),
+        _opt_f32(L.sinks, "sinks"), float(L.eps), float(L.scale),
+        _f32(cache_k, "cache_k"), _f32(cache_v, "cache_v"), n_slots, slot_ctx,
+        _f32(q, "q"), _f32(np.ascontiguousarray(k_new, np.float32), "k_new"),
+        _f32(np.ascontiguousarray(v_new, np.float32), "v_new"), slot, pos0, T, _f32(out, "out"))
     return rc, out

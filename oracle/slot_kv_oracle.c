@@ -208,3 +208,35 @@ int oracle_decode_batch(uint32_t n_heads, uint32_t n_kv_heads, uint32_t head_dim
     }
     return ORACLE_OK;
 }
+
+/* Slot prefill ("Forward Cuda", batched prefill that writes the KV cache into
+ * the given slot's per-sequence region; "Forward Cuda Gemma", prefillBatched,
+ * which the pages define as equal to running the one-token step on every
+ * prompt token in order): the T tokens of one sequence, at positions
+ * pos0 .. pos0+T-1 of slot `slot`, each written and attended exactly as a
+ * one-row decode step at its position would be, in token order.  Token t
+ * therefore attends over positions 0 .. pos0+t: the slot's earlier history
+ * and the rows of tokens 0..t of this call. */
+int oracle_prefill(uint32_t n_heads, uint32_t n_kv_heads, uint32_t head_dim,
+                   const float *q_norm_w, const float *k_norm_w,
+                   const float *inv_freq, const float *sinks,
+                   float eps, float scale,
+                   float *cache_k, float *cache_v,
+                   uint32_t n_slots, uint32_t slot_ctx,
+                   const float *q, const float *k_new, const float *v_new,
+                   uint32_t slot, uint32_t pos0, uint32_t T, float *out) {
+    if (n_kv_heads == 0 || head_dim == 0) return ORACLE_EINVAL;
+    if (slot >= n_slots || pos0 >= slot_ctx || T > slot_ctx - pos0) return ORACLE_ERANGE;
+    const uint32_t kv_dim = n_kv_heads * head_dim;
+    const size_t qd = (size_t)n_heads * head_dim;
+    for (uint32_t t = 0; t < T; ++t) {
+        const uint32_t p = pos0 + t;
+        int rc = oracle_decode_batch(n_heads, n_kv_heads, head_dim, q_norm_w, k_norm_w,
+                                     inv_freq, sinks, eps, scale, cache_k, cache_v,
+                                     n_slots, slot_ctx, q + (size_t)t * qd,
+                                     k_new + (size_t)t * kv_dim, v_new + (size_t)t * kv_dim,
+                                     &p, &slot, 1, out + (size_t)t * qd);
+        if (rc != ORACLE_OK) return rc;
+    }
+    return ORACLE_OK;
+}

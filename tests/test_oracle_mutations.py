@@ -36,7 +36,12 @@ MUTANTS = {
                           "for"),
     "dup_slots_allowed": ("if (slots[c] == slots[b]) return ORACLE_EDUP;", "continue;"),
     "pos_bound_off_by_one": ("positions[b] >= slot_ctx", "positions[b] > slot_ctx"),
+    # slot prefill
+    "prefill_ignores_pos0": ("const uint32_t p = pos0 + t;", "const uint32_t p = t;"),
+    "prefill_reverse_order": ("const uint32_t p = pos0 + t;", "const uint32_t p = pos0 + (T - 1 - t);"),
+    "prefill_range_off_by_one": ("T > slot_ctx - pos0", "T > slot_ctx - pos0 + 1"),
 }
+PIN_FILES = ["test_oracle_pins.py", "test_oracle_prefill_pins.py"]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
@@ -49,6 +54,6 @@ def test_pins_catch_mutant(name, tmp_path):
     lib = oracle.build(force=True, src=str(mut_src), out=str(tmp_path / "libmutant.so"))
     env = dict(os.environ, SLOT_KV_ORACLE_LIB=lib)
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        *[os.path.join(ROOT, "tests", f) for f in PIN_FILES]],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"

@@ -1,0 +1,132 @@
+"""Pins of the oracle's slot prefill to facts fixed independently of it.
+
+The pages define batched prefill into a slot as equal to running the
+one-token step on every prompt token in order ("Forward Cuda": batched
+prefill that writes the KV cache into the slot's per-sequence region;
+"Forward Cuda Gemma": prefillBatched).  The oracle implements exactly that
+loop.  These tests pin it to a vectorised float64 causal-attention
+computation written from the mathematics (no loop over tokens, no shared
+code), to causality, to the placement of the rows it writes, and to its range
+checks.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from sequence_slot_kv_amd import workloads as wl
+
+F64 = np.float64
+
+
+def make_layer(rng, H, Hkv, D, *, sinks=False, theta=1e4):
+    return wl.LayerParams(
+        n_heads=H, n_kv_heads=Hkv, head_dim=D,
+        q_norm_w=(1 + 0.1 * rng.standard_normal(D)).astype(np.float32),
+        k_norm_w=(1 + 0.1 * rng.standard_normal(D)).astype(np.float32),
+        inv_freq=wl.rope_inv_freq(theta, D),
+        sinks=rng.standard_normal(H).astype(np.float32) if sinks else None,
+        eps=1e-6, scale=float(np.float32(1 / math.sqrt(D))))
+
+
+def brute_force(L, hist_k, hist_v, q, k_new, v_new, pos0):
+    """Causal softmax attention of T query tokens at positions pos0..pos0+T-1
+    over the slot's history rows and the T new rows, all in one vectorised
+    float64 pass.  Returns (out[T, H*D] f32, written K rows [T, kv_dim] f32)."""
+    H, Hkv, D, G = L.n_heads, L.n_kv_heads, L.head_dim, L.n_heads // L.n_kv_heads
+    T = q.shape[0]
+    pos = pos0 + np.arange(T)
+
+    def norm(x, w):
+        return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + L.eps) * w.astype(F64)
+
+    def rope(x, p):
+        ang = (p.astype(np.float32)[:, None] * L.inv_freq).astype(F64)  # f32 product
+        c, s = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+        a, b = x[..., : D // 2], x[..., D // 2:]
+        return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+
+    k_rot = rope(norm(k_new.reshape(T, Hkv, D).astype(F64), L.k_norm_w), pos)
+    k_written = k_rot.astype(np.float32)
+    K = np.concatenate([hist_k.reshape(pos0, Hkv, D), k_written]).astype(F64)
+    V = np.concatenate([hist_v.reshape(pos0, Hkv, D), v_new.reshape(T, Hkv, D)]).astype(F64)
+    qr = rope(norm(q.reshape(T, H, D).astype(F64), L.q_norm_w), pos)
+    kv_of_head = np.arange(H) // G
+    S = L.scale * np.einsum("thd,nhd->thn", qr, K[:, kv_of_head, :])
+    N = K.shape[0]
+    S = np.where(np.arange(N)[None, None, :] > pos[:, None, None], -np.inf, S)
+    m = S.max(axis=-1)
+    if L.sinks is not None:
+        m = np.maximum(m, L.sinks.astype(F64)[None, :])
+    E = np.exp(S - m[..., None])
+    den = E.sum(axis=-1)
+    if L.sinks is not None:
+        den = den + np.exp(L.sinks.astype(F64)[None, :] - m)
+    out = np.einsum("thn,nhd->thd", E, V[:, kv_of_head, :]) / den[..., None]
+    return out.astype(np.float32).reshape(T, H * D), k_written.reshape(T, Hkv * D)
+
+
+def setup(rng, H, Hkv, D, n_slots, slot_ctx, slot, pos0, T, sinks=False):
+    L = make_layer(rng, H, Hkv, D, sinks=sinks)
+    kv_dim = Hkv * D
+    ck = rng.standard_normal((n_slots, slot_ctx, kv_dim)).astype(np.float32)
+    cv = rng.standard_normal((n_slots, slot_ctx, kv_dim)).astype(np.float32)
+    q = rng.standard_normal((T, H * D)).astype(np.float32)
+    kn = rng.standard_normal((T, kv_dim)).astype(np.float32)
+    vn = rng.standard_normal((T, kv_dim)).astype(np.float32)
+    return L, ck, cv, q, kn, vn
+
+
+@pytest.mark.parametrize("H,Hkv,D,pos0,T,sinks", [
+    (2, 2, 8, 0, 5, False),   # prompt from position 0, no GQA
+    (4, 2, 8, 3, 6, True),    # continuation over history, G = 2, sinks
+    (8, 2, 16, 7, 9, False),  # G = 4
+    (8, 1, 4, 0, 1, True),    # a single token, G = 8
+])
+def test_prefill_matches_vectorised_causal_attention(H, Hkv, D, pos0, T, sinks):
+    rng = np.random.default_rng(100 + H + pos0 + T)
+    n_slots, slot_ctx, slot = 3, 24, 1
+    L, ck, cv, q, kn, vn = setup(rng, H, Hkv, D, n_slots, slot_ctx, slot, pos0, T, sinks)
+    ref_out, ref_k = brute_force(L, ck[slot, :pos0], cv[slot, :pos0], q, kn, vn, pos0)
+    rc, out = oracle.prefill(L, ck, cv, q, kn, vn, slot, pos0)
+    assert rc == 0
+    np.testing.assert_allclose(out, ref_out, rtol=1e-6, atol=1e-7)
+    np.testing.assert_allclose(ck[slot, pos0:pos0 + T], ref_k, rtol=1e-6, atol=1e-7)
+
+
+def test_prefill_is_causal():
+    rng = np.random.default_rng(7)
+    L, ck, cv, q, kn, vn = setup(rng, 4, 2, 8, 2, 16, 0, 2, 6)
+    ck2, cv2 = ck.copy(), cv.copy()
+    _, out = oracle.prefill(L, ck, cv, q, kn, vn, 0, 2)
+    q2, kn2, vn2 = q.copy(), kn.copy(), vn.copy()
+    q2[4:] += 1.0
+    kn2[4:] -= 2.0
+    vn2[4:] *= 3.0
+    _, out2 = oracle.prefill(L, ck2, cv2, q2, kn2, vn2, 0, 2)
+    assert np.array_equal(out[:4], out2[:4])  # tokens 0..3 cannot see tokens 4..5
+    assert not np.array_equal(out[4:], out2[4:])
+
+
+def test_prefill_writes_its_rows_only():
+    rng = np.random.default_rng(8)
+    n_slots, slot_ctx, slot, pos0, T = 3, 12, 2, 4, 5
+    L, ck, cv, q, kn, vn = setup(rng, 4, 2, 8, n_slots, slot_ctx, slot, pos0, T)
+    ck0, cv0 = ck.copy(), cv.copy()
+    rc, _ = oracle.prefill(L, ck, cv, q, kn, vn, slot, pos0)
+    assert rc == 0
+    changed = np.argwhere(np.any(ck != ck0, axis=-1) | np.any(cv != cv0, axis=-1))
+    assert {tuple(x) for x in changed} == {(slot, p) for p in range(pos0, pos0 + T)}
+    assert np.array_equal(cv[slot, pos0:pos0 + T], vn)  # values verbatim
+
+
+def test_prefill_range_checks_write_nothing_on_error():
+    rng = np.random.default_rng(9)
+    L, ck, cv, q, kn, vn = setup(rng, 2, 1, 4, 2, 8, 0, 0, 3)
+    ck0, cv0 = ck.copy(), cv.copy()
+    assert oracle.prefill(L, ck, cv, q, kn, vn, 2, 0)[0] == -2      # slot out of range
+    assert oracle.prefill(L, ck, cv, q, kn, vn, 0, 6)[0] == -2      # 6 + 3 > 8
+    assert oracle.prefill(L, ck, cv, q, kn, vn, 0, 8)[0] == -2      # first position past the end
+    assert np.array_equal(ck, ck0) and np.array_equal(cv, cv0)      # a rejected call writes nothing
+    assert oracle.prefill(L, ck, cv, q, kn, vn, 0, 5)[0] == 0       # 5 + 3 == 8 fits
