@@ -122,6 +122,27 @@ int slot_decode_attn(slot_kv *h, uint32_t layer, const float *q,
                      const uint32_t *positions, const uint32_t *slots,
                      uint32_t B, float *out, void *stream);
 
+/* "Forward Cuda", batched prefill that writes the KV cache into a slot's
+ * per-sequence region; "Forward Cuda Gemma", prefillBatched, defined there as
+ * equal to running the one-token step on every prompt token in order.
+ * T tokens of one sequence, at positions pos0 .. pos0+T-1 of slot `slot`: for
+ * token t the same per-head RMSNorm and RoPE (at pos0+t), KV write and
+ * attention as slot_decode_attn gives a row at that position, with the tokens
+ * taken in order, so token t attends over positions 0 .. pos0+t (the slot's
+ * earlier history and tokens 0..t of this call).
+ *   q      device [T][n_heads*head_dim]        k_new, v_new  device [T][kv_dim]
+ *   out    device [T][n_heads*head_dim]; must not overlap q, k_new or v_new
+ *   stream hipStream_t (NULL = the null stream)
+ * Requires history rows 0..pos0-1 of the slot to hold the sequence's keys and
+ * values.  The handle keeps a scratch buffer of T*n_heads*head_dim floats for
+ * the rotated queries (grown on demand).  T == 0 is a no-op.  Errors:
+ * ENOTALLOC, EINVAL (layer unconfigured or head shape unsupported, NULL
+ * pointer), ERANGE (slot >= n_slots or pos0 + T > slot_ctx), ENOMEM, EDEVICE.
+ * Nothing is written when an error is returned. */
+int slot_prefill_attn(slot_kv *h, uint32_t layer, const float *q,
+                      const float *k_new, const float *v_new, uint32_t slot,
+                      uint32_t pos0, uint32_t T, float *out, void *stream);
+
 /* Device pointers of layer `layer`'s K and V buffers ([n_slots][slot_ctx]
  * [kv_dim] floats each; owned by the handle, valid until the next
  * slot_kv_alloc or slot_kv_destroy).  Errors: ENOTALLOC, EINVAL. */
@@ -157,10 +178,11 @@ int slot_kv_check_batch(uint32_t n_slots, uint32_t slot_ctx,
  * boundaries depend only on each row's position, never on the batch). */
 uint32_t slot_kv_chunk_keys(void);
 
-/* Profiling of the fused decode kernel.  Between slot_kv_profile_begin and
+/* Profiling of the attention kernels.  Between slot_kv_profile_begin and
  * slot_kv_profile_end the handle records a HIP event pair on the call's
  * stream immediately around each launch of the fused decode kernel (one
- * launch per 256 rows of a slot_decode_attn call; it does the whole step).
+ * launch per 256 rows of a slot_decode_attn call; it does the whole step) and
+ * of the prefill attention kernel (one per slot_prefill_attn call).
  * slot_kv_profile_end waits for the recorded launches and returns their
  * summed duration in milliseconds and their count (either pointer may be
  * NULL), then stops recording.  Errors: EINVAL, EDEVICE. */

@@ -27,7 +27,8 @@ SLOT_KV_EDEVICE = -6
 
 # Every symbol include/slot_kv.h declares.
 EXPORTS = ("slot_kv_create", "slot_kv_destroy", "slot_kv_alloc", "slot_kv_set_layer",
-           "slot_kv_offset_bytes", "slot_reset", "slot_decode_attn", "slot_kv_layer_ptrs",
+           "slot_kv_offset_bytes", "slot_reset", "slot_decode_attn", "slot_prefill_attn",
+           "slot_kv_layer_ptrs",
            "slot_kv_write_rows", "slot_kv_read_rows", "slot_kv_check_batch",
            "slot_kv_chunk_keys", "slot_kv_profile_begin", "slot_kv_profile_end",
            "slot_kv_strerror")
@@ -57,6 +58,7 @@ _lib.slot_kv_set_layer.argtypes = [_vp, _u32, _u32, _u32, _u32, _f32p, _f32p, _f
 _lib.slot_kv_offset_bytes.argtypes = [_vp, _u32, _u32, _u32, ctypes.POINTER(ctypes.c_uint64)]
 _lib.slot_reset.argtypes = [_vp, _u32]
 _lib.slot_decode_attn.argtypes = [_vp, _u32, _vp, _vp, _vp, _u32p, _u32p, _u32, _vp, _vp]
+_lib.slot_prefill_attn.argtypes = [_vp, _u32, _vp, _vp, _vp, _u32, _u32, _u32, _vp, _vp]
 _lib.slot_kv_layer_ptrs.argtypes = [_vp, _u32, ctypes.POINTER(_vp), ctypes.POINTER(_vp)]
 _lib.slot_kv_write_rows.argtypes = [_vp, _u32, _u32, _u32, _u32, _vp, _vp, _vp]
 _lib.slot_kv_read_rows.argtypes = [_vp, _u32, _u32, _u32, _u32, _vp, _vp, _vp]
@@ -182,6 +184,15 @@ def slot_decode_attn(h, layer, q, k_new, v_new, positions, slots, out, stream=No
                                  B, ptrs[3], _stream_handle(stream))
 
 
+def slot_prefill_attn(h, layer, q, k_new, v_new, slot, pos0, out, stream=None) -> int:
+    """Raw call: q/k_new/v_new/out are GPU float32 tensors of T rows (T is
+    taken from q's leading dimension).  Returns the status code."""
+    T = int(q.shape[0]) if q.dim() > 0 else 0
+    ptrs = [_dev_ptr(t, n) for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (out, "out"))]
+    return _lib.slot_prefill_attn(h, layer, ptrs[0], ptrs[1], ptrs[2], slot, pos0, T, ptrs[3],
+                                  _stream_handle(stream))
+
+
 def slot_kv_layer_ptrs(h, layer):
     """Returns (status, k_ptr, v_ptr)."""
     k, v = _vp(), _vp()
@@ -292,6 +303,23 @@ class SlotKV:
                     raise ValueError(f"{n}: expected {B}x{w} elements, got {tuple(t.shape)}")
         _check(slot_decode_attn(self.h, layer, q, k_new, v_new, positions, slots, out, stream),
                "slot_decode_attn")
+        return out
+
+    def prefill_attn(self, layer, q, k_new, v_new, slot, pos0, out=None, stream=None):
+        """T tokens (rows of q / k_new / v_new) of one sequence at positions
+        pos0 .. pos0+T-1 of ``slot``; returns out [T, n_heads*head_dim]."""
+        import torch
+        if out is None:
+            out = torch.empty_like(q)
+        P = self.layers.get(layer)
+        if P is not None:
+            T = int(q.shape[0])
+            for t, n, w in ((q, "q", P.n_heads * P.head_dim), (k_new, "k_new", P.kv_dim),
+                            (v_new, "v_new", P.kv_dim), (out, "out", P.n_heads * P.head_dim)):
+                if t.numel() != T * w:
+                    raise ValueError(f"{n}: expected {T}x{w} elements, got {tuple(t.shape)}")
+        _check(slot_prefill_attn(self.h, layer, q, k_new, v_new, slot, pos0, out, stream),
+               "slot_prefill_attn")
         return out
 
     def layer_view(self, layer):

@@ -101,6 +101,27 @@ int ensure_partials(slot_kv* h, size_t floats) {
   return SLOT_KV_OK;
 }
 
+// When profiling, the next HIP event pair of the handle (created on first
+// use); *e0 = *e1 = nullptr otherwise.
+int prof_pair(slot_kv* h, hipEvent_t* e0, hipEvent_t* e1) {
+  *e0 = *e1 = nullptr;
+  if (!h->profiling) return SLOT_KV_OK;
+  if (h->prof_events.size() < 2 * (h->prof_used + 1)) {
+    hipEvent_t a = nullptr, b = nullptr;
+    if (hipEventCreate(&a) != hipSuccess) return SLOT_KV_EDEVICE;
+    if (hipEventCreate(&b) != hipSuccess) {
+      (void)hipEventDestroy(a);
+      return SLOT_KV_EDEVICE;
+    }
+    h->prof_events.push_back(a);
+    h->prof_events.push_back(b);
+  }
+  *e0 = h->prof_events[2 * h->prof_used];
+  *e1 = h->prof_events[2 * h->prof_used + 1];
+  ++h->prof_used;
+  return SLOT_KV_OK;
+}
+
 // The work-queue counters start at zero; the kernel returns them to zero, so
 // they are cleared only when (re)allocated.
 int ensure_counters(slot_kv* h, size_t entries) {
@@ -339,27 +360,63 @@ int slot_decode_attn(slot_kv* h, uint32_t layer, const float* q, const float* k_
     p.part_acc = h->part;
     p.part_ml = h->part + static_cast<size_t>(n) * work.max_chunks * L.n_heads * D;
 
-    hipEvent_t ev_end = nullptr;
-    if (h->profiling) {
-      if (h->prof_events.size() < 2 * (h->prof_used + 1)) {
-        hipEvent_t e0 = nullptr, e1 = nullptr;
-        if (hipEventCreate(&e0) != hipSuccess) return SLOT_KV_EDEVICE;
-        if (hipEventCreate(&e1) != hipSuccess) {
-          (void)hipEventDestroy(e0);
-          return SLOT_KV_EDEVICE;
-        }
-        h->prof_events.push_back(e0);
-        h->prof_events.push_back(e1);
-      }
-      if (hipEventRecord(h->prof_events[2 * h->prof_used], s) != hipSuccess)
-        return SLOT_KV_EDEVICE;
-      ev_end = h->prof_events[2 * h->prof_used + 1];
-      ++h->prof_used;
-    }
+    hipEvent_t ev_start = nullptr, ev_end = nullptr;
+    rc = prof_pair(h, &ev_start, &ev_end);
+    if (rc) return rc;
+    if (ev_start && hipEventRecord(ev_start, s) != hipSuccess) return SLOT_KV_EDEVICE;
     const uint32_t blocks = std::min(p.n_units, resident);
     if (slotkv::launch_decode(a, L.head_dim, G, blocks, stream, ev_end) != hipSuccess)
       return SLOT_KV_EDEVICE;
   }
+  return SLOT_KV_OK;
+}
+
+int slot_prefill_attn(slot_kv* h, uint32_t layer, const float* q, const float* k_new,
+                      const float* v_new, uint32_t slot, uint32_t pos0, uint32_t T,
+                      float* out, void* stream) {
+  int rc = check_layer(h, layer);
+  if (rc) return rc;
+  LayerState& L = h->layers[layer];
+  if (!L.configured) return SLOT_KV_EINVAL;
+  if (T == 0) return SLOT_KV_OK;
+  if (!q || !k_new || !v_new || !out) return SLOT_KV_EINVAL;
+  if (slot >= h->n_slots || static_cast<uint64_t>(pos0) + T > h->slot_ctx) return SLOT_KV_ERANGE;
+  const uint32_t G = L.n_heads / L.n_kv_heads;
+  if (!slotkv::decode_shape_supported(L.head_dim, G)) return SLOT_KV_EINVAL;
+  if (static_cast<uint64_t>(T) * (L.n_heads + L.n_kv_heads) >= (uint64_t(1) << 31))
+    return SLOT_KV_EINVAL;  // keeps the kernels' 32-bit vector and tile counts exact
+  const size_t D = L.head_dim;
+  // rotated queries: the split-row scratch serves (calls on one handle are
+  // ordered on one stream)
+  rc = ensure_partials(h, static_cast<size_t>(T) * L.n_heads * D);
+  if (rc) return rc;
+
+  slotkv::PrefillParams p{};
+  p.k_cache = L.k;
+  p.v_cache = L.v;
+  p.q = q;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.qs = h->part;
+  p.out = out;
+  p.q_norm_w = L.params;
+  p.k_norm_w = L.params + D;
+  p.inv_freq = L.params + 2 * D;
+  p.sinks = L.has_sinks ? L.params + 2 * D + D / 2 : nullptr;
+  p.slot_base = static_cast<uint64_t>(slot) * h->slot_ctx * L.kv_dim;
+  p.kv_dim = L.kv_dim;
+  p.n_heads = L.n_heads;
+  p.n_kv_heads = L.n_kv_heads;
+  p.T = T;
+  p.pos0 = pos0;
+  p.n_tiles = static_cast<uint32_t>((static_cast<uint64_t>(T) * G + 15) / 16);
+  p.eps = L.eps;
+  p.qk_scale_log2 = L.scale * 1.4426950408889634f;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  rc = prof_pair(h, &e0, &e1);
+  if (rc) return rc;
+  if (slotkv::launch_prefill(p, L.head_dim, G, stream, e0, e1) != hipSuccess)
+    return SLOT_KV_EDEVICE;
   return SLOT_KV_OK;
 }
 

@@ -65,6 +65,36 @@ struct AttnArgs {
 };
 static_assert(sizeof(AttnArgs) < 4000, "kernel arguments must stay below 4 KiB");
 
+// Parameters of a slot prefill (T tokens of one slot at pos0 .. pos0+T-1).
+struct PrefillParams {
+  float* k_cache;          // layer K buffer
+  float* v_cache;          // layer V buffer
+  const float* q;          // [T][n_heads*D]
+  const float* k_new;      // [T][kv_dim]
+  const float* v_new;      // [T][kv_dim]
+  float* qs;               // [T][n_heads][D] rotated queries times scale*log2(e) (scratch)
+  float* out;              // [T][n_heads*D]
+  const float* q_norm_w;   // [D]
+  const float* k_norm_w;   // [D]
+  const float* inv_freq;   // [D/2]
+  const float* sinks;      // [n_heads] or nullptr
+  uint64_t slot_base;      // slot * slot_ctx * kv_dim (floats): the slot's row 0
+  uint32_t kv_dim;
+  uint32_t n_heads;
+  uint32_t n_kv_heads;
+  uint32_t T;
+  uint32_t pos0;
+  uint32_t n_tiles;        // 16-row query tiles per kv head: ceil(T * G / 16)
+  float eps;
+  float qk_scale_log2;     // scale * log2(e)
+};
+
+// Launches of a prefill: norm + RoPE + KV write, then the attention.
+// `before_attn` / `after_attn` (hipEvent_t or null) are recorded around the
+// attention kernel.  Returns a hipError_t value.
+int launch_prefill(const PrefillParams& p, uint32_t head_dim, uint32_t group, void* stream,
+                   void* before_attn, void* after_attn);
+
 // Validation of one batch (no device access).  Returns a SLOT_KV_* status.
 int check_batch(uint32_t n_slots, uint32_t slot_ctx, const uint32_t* positions,
                 const uint32_t* slots, uint32_t B);

@@ -270,6 +270,7 @@ template <int D, int G>
 struct alignas(16) PrepLds {
   float q[2][G][D];  // normalised, rotated, times scale*log2(e)
   float kn[2][D];    // normalised, rotated new key
+  float vn[2][D];    // its value row (v_new)
 };
 template <int D, int G>
 struct PrepRaw {
@@ -372,6 +373,7 @@ __device__ __forceinline__ void prep_finish(const AttnArgs& a, const UnitId& id,
 #pragma unroll
       for (int e = 0; e < R::EPL; ++e) {
         prep.kn[par][lane * R::EPL + e] = y[e];
+        prep.vn[par][lane * R::EPL + e] = raw.vn[e];
         p.k_cache[at + e] = y[e];
         p.v_cache[at + e] = raw.vn[e];
       }
@@ -461,17 +463,12 @@ __global__ void __launch_bounds__(kThreads)
       for (int i = 0; i < NV4; ++i) q[g][i] = ld4(&prep.q[par][g][i * SL + lo]);
     float mx[G];  // running max of this lane's key group, per head
     float s_new[G];
-    f4 vn[NV4];
 #pragma unroll
     for (int g = 0; g < G; ++g) mx[g] = -INFINITY;
     if (u.new_key) {  // wave 0 of the row's last chunk scores the new key
       f4 kn[NV4];
-      const size_t nb = static_cast<size_t>(u.b) * p.kv_dim + u.j * D + lo;
 #pragma unroll
-      for (int i = 0; i < NV4; ++i) {
-        kn[i] = ld4(&prep.kn[par][i * SL + lo]);
-        vn[i] = ld4(p.v_new + nb + i * SL);
-      }
+      for (int i = 0; i < NV4; ++i) kn[i] = ld4(&prep.kn[par][i * SL + lo]);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         float sdot = dot4(q[g][0], kn[0]);
@@ -519,6 +516,8 @@ __global__ void __launch_bounds__(kThreads)
       }
     };
     float m[G];  // wave max per head: all key groups (and the new key) share it
+    float l[G];
+    f4 acc[G][NV4];
     auto finish_max = [&]() {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -526,16 +525,11 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
         for (int off = LPK; off < kWave; off <<= 1) v = max_nc(v, __shfl_xor(v, off));
         m[g] = v;
+        l[g] = 0.f;  // pass 2's state starts here, so it holds no registers in pass 1
+#pragma unroll
+        for (int i = 0; i < NV4; ++i) acc[g][i] = f4{0.f, 0.f, 0.f, 0.f};
       }
     };
-    float l[G];
-    f4 acc[G][NV4];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      l[g] = 0.f;
-#pragma unroll
-      for (int i = 0; i < NV4; ++i) acc[g][i] = f4{0.f, 0.f, 0.f, 0.f};
-    }
     auto accumulate = [&](const Stage<D, G>& sg, uint32_t st) {
       const float* src = sc_w + (st * NG + gi) * (G * U);
       float sc[G * U];
@@ -604,6 +598,9 @@ __global__ void __launch_bounds__(kThreads)
       if (has_next) prep_finish<D, G>(a, un, w, lane, praw, pconst, prep, par ^ 1u);
     }
     if (u.new_key && gi == 0) {
+      f4 vn[NV4];
+#pragma unroll
+      for (int i = 0; i < NV4; ++i) vn[i] = ld4(&prep.vn[par][i * SL + lo]);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const float pn = fast_exp2(s_new[g] - m[g]);

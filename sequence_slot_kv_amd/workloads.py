@@ -202,3 +202,62 @@ def poison_outside(cache: np.ndarray, positions, slots, value) -> None:
         cache[s, int(p) + 1:, :] = value
         used[s] = True
     cache[~used] = value
+
+
+# ---------------------------------------------------------------- slot prefill
+@dataclasses.dataclass
+class PrefillWorkload:
+    """T tokens of one sequence written into slot ``slot`` at positions
+    pos0 .. pos0+T-1 (the history 0..pos0-1 is already in the slot)."""
+    name: str
+    seed: int
+    n_slots: int
+    slot_ctx: int
+    slot: int
+    pos0: int
+    layer: LayerParams
+    inputs: LayerInputs  # q [T, n_heads*D], k_new / v_new [T, kv_dim]
+    theta: float
+
+    @property
+    def T(self) -> int:
+        return int(self.inputs.q.shape[0])
+
+    def attn_flops(self) -> int:
+        """Multiply-adds of the attention counted as 2 flops each: token t
+        scores pos0+t+1 keys and sums as many value rows, per query head."""
+        L = self.layer
+        keys = self.T * self.pos0 + self.T * (self.T + 1) // 2
+        return 2 * 2 * keys * L.n_heads * L.head_dim
+
+
+def _build_prefill(name, seed, n_slots, slot_ctx, pos0, T, shape, theta, sinks):
+    """Recipe: slot = a uniform draw from range(n_slots); then q [T, H*D],
+    k_new / v_new [T, kv_dim] ~ N(0, 1); then the layer's tables as above."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    slot = int(rng.integers(0, n_slots))
+    H, Hkv, D = shape
+    li = _layer_inputs(rng, T, H, Hkv, D)
+    L = make_layer(rng, H, Hkv, D, theta, sinks)
+    return PrefillWorkload(name=name, seed=seed, n_slots=n_slots, slot_ctx=slot_ctx, slot=slot,
+                           pos0=pos0, layer=L, inputs=li, theta=theta)
+
+
+def prefill_tiny() -> PrefillWorkload:
+    """4 heads / 2 kv heads / D=64, 4 slots x 128; 37 tokens after 21 of history."""
+    return _build_prefill("prefill_tiny", 11, 4, 128, 21, 37, (4, 2, 64), 1e4, False)
+
+
+def prefill_prompt() -> PrefillWorkload:
+    """A 2048-token prompt from position 0 into one slot of a 64-slot x 4096
+    cache; 32 heads / 8 kv heads / D=128 (the decode workload's layer shape)."""
+    return _build_prefill("prefill_prompt", 12, 64, 4096, 0, 2048, (32, 8, 128), 1e6, False)
+
+
+def prefill_chunk() -> PrefillWorkload:
+    """A 512-token chunk appended after 3072 positions of history, same shapes."""
+    return _build_prefill("prefill_chunk", 13, 64, 4096, 3072, 512, (32, 8, 128), 1e6, False)
+
+
+PREFILL_WORKLOADS = {"prefill_tiny": prefill_tiny, "prefill_prompt": prefill_prompt,
+                     "prefill_chunk": prefill_chunk}
