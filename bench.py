@@ -20,6 +20,15 @@ Prints ONE JSON line on stdout:
   cpu_baseline the CPU oracle on the host cores over the same rows
 
     python bench.py [--steps K] [--warmup W] [--workload mid]
+
+With --workload prefill_prompt or prefill_chunk it measures the slot prefill
+instead (one slot_prefill_attn call per step: the norm / RoPE / KV-write
+kernel and the causal attention kernel on the matrix cores):
+  value        prompt tokens/s
+  roofline     the attention kernel's f32 matrix-core rate (attention flops /
+               mean kernel time from the library's HIP events) vs the
+               157.3 TFLOP/s dense f32 MFMA peak
+  cpu_baseline the CPU oracle's prefill over the first tokens of the prompt
 """
 from __future__ import annotations
 
@@ -36,6 +45,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-attn rows/sec and achieved KV HBM GB/s (% of peak) at B=64, ctx 4096"
 HBM_PEAK_GBPS = 8000.0
+MFMA_F32_PEAK_TFLOPS = 157.3
+PREFILL_METRIC = "slot prefill tokens/s and attention TFLOP/s (f32 matrix cores)"
 KERNEL_SRC = os.path.join(ROOT, "sequence_slot_kv_amd", "csrc", "slot_kv_kernels.hip")
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
@@ -94,7 +105,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mid",
-                    choices=["tiny", "mid", "long", "many", "layer_stack"])
+                    choices=["tiny", "mid", "long", "many", "layer_stack", "prefill_prompt",
+                             "prefill_chunk"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the reference "
@@ -121,6 +133,8 @@ def main():
         torch.cuda.synchronize()
         log("[bench] copied 1 GiB x 5")
         return
+    if args.workload.startswith("prefill"):
+        return prefill_bench(args, wl.PREFILL_WORKLOADS[args.workload](), b)
     w = wl.WORKLOADS[args.workload]()
     n_layers = len(w.layers)
     log(f"[bench] workload {w.name}: B={w.B} n_slots={w.n_slots} slot_ctx={w.slot_ctx} "
@@ -217,6 +231,90 @@ def main():
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "kernel": "decode_attn_kernel", "kernel_us": mean_launch_ms * 1e3,
                      "algorithmic_bytes_per_launch": bytes_per_launch},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    kv.close()
+
+
+def prefill_bench(args, w, b):
+    import numpy as np
+    import torch
+    L, li = w.layer, w.inputs
+    log(f"[bench] prefill {w.name}: T={w.T} pos0={w.pos0} slot={w.slot} heads {L.n_heads}/"
+        f"{L.n_kv_heads}/{L.head_dim}, attention {w.attn_flops() / 1e9:.1f} GFLOP per step")
+    kv = b.SlotKV()
+    kv.alloc(w.n_slots, w.slot_ctx, [L.kv_dim])
+    kv.set_layer(0, L)
+    hist_k = hist_v = np.zeros((0, L.kv_dim), np.float32)
+    if w.pos0:
+        g = torch.Generator(device="cuda")
+        g.manual_seed(77 + w.seed)
+        hk = torch.randn((w.pos0, L.kv_dim), generator=g, device="cuda")
+        hv = torch.randn((w.pos0, L.kv_dim), generator=g, device="cuda")
+        kv.write_rows(0, w.slot, 0, hk, hv)
+        if not args.no_cpu_baseline:
+            hist_k, hist_v = hk.cpu().numpy(), hv.cpu().numpy()
+    q, kn, vn = (torch.from_numpy(x).cuda() for x in (li.q, li.k_new, li.v_new))
+    out = torch.empty_like(q)
+
+    def step():
+        kv.prefill_attn(0, q, kn, vn, w.slot, w.pos0, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    rc = b.slot_kv_profile_begin(kv.h)
+    assert rc == 0
+    for _ in range(args.steps):
+        step()
+    rc, attn_ms, launches = b.slot_kv_profile_end(kv.h)
+    torch.cuda.synchronize()
+    assert rc == 0 and launches == args.steps
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    attn_us = attn_ms / launches * 1e3
+    tflops = w.attn_flops() / (attn_us * 1e-6) / 1e12
+    log(f"[bench] {ms_per_step * 1e3:.1f} us/step, attention kernel {attn_us:.1f} us, "
+        f"{tflops:.1f} TFLOP/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        # the first n tokens of the prompt, run by the oracle in order (the
+        # rest of the prompt does not change them)
+        n = 1
+        while True:
+            ck = np.zeros((1, w.pos0 + n, L.kv_dim), np.float32)
+            cv = np.zeros_like(ck)
+            ck[0, :w.pos0], cv[0, :w.pos0] = hist_k, hist_v
+            c0 = time.perf_counter()
+            rc, _ = oracle.prefill(L, ck, cv, li.q[:n], li.k_new[:n], li.v_new[:n], 0, w.pos0)
+            dt = time.perf_counter() - c0
+            assert rc == 0
+            if dt >= 2.0 or n >= w.T:
+                break
+            n = min(w.T, n * 4)
+        cpu = {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"the first {n} tokens of the prompt in order, {dt:.1f} s on one thread "
+                         f"(later tokens attend over more keys, so this overstates the "
+                         f"whole prompt's rate)"}
+    res = {
+        "metric": PREFILL_METRIC, "value": w.T / (ms_per_step / 1e3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "pos0": w.pos0, "slot_ctx": w.slot_ctx,
+                   "n_heads": L.n_heads, "n_kv_heads": L.n_kv_heads, "head_dim": L.head_dim,
+                   "seed": w.seed},
+        "attn_flops_per_step": w.attn_flops(),
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_F32_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / MFMA_F32_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "prefill_attn_kernel", "kernel_us": attn_us},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
