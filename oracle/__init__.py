@@ -72,6 +72,10 @@ def _load():
             u32, u32, u32, f32p, f32p, f32p, f32p, ctypes.c_float, ctypes.c_float,
             f32p, f32p, u32, u32, f32p, f32p, f32p, u32, u32, u32, f32p]
         lib.oracle_prefill.restype = ctypes.c_int
+        lib.oracle_verify.argtypes = [
+            u32, u32, u32, f32p, f32p, f32p, f32p, ctypes.c_float, ctypes.c_float,
+            f32p, f32p, u32, u32, f32p, f32p, f32p, u32p, u32p, u32p, u32, f32p]
+        lib.oracle_verify.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -199,3 +203,30 @@ def prefill(layer, cache_k, cache_v, q, k_new, v_new, slot, pos0):
         _f32(q, "q"), _f32(np.ascontiguousarray(k_new, np.float32), "k_new"),
         _f32(np.ascontiguousarray(v_new, np.float32), "v_new"), slot, pos0, T, _f32(out, "out"))
     return rc, out
+
+
+def verify(layer, cache_k, cache_v, q, k_new, v_new, slots, pos0, ks):
+    """ks[i] rows for each sequence i (rows sequence-major in q / k_new /
+    v_new) at positions pos0[i] .. of slot slots[i], over host mirrors
+    [n_slots, slot_ctx, kv_dim] (updated in place).  Returns (status,
+    out[sum ks, n_heads*head_dim])."""
+    L = layer
+    n_slots, slot_ctx, kv_dim = cache_k.shape
+    if kv_dim != L.n_kv_heads * L.head_dim or cache_v.shape != cache_k.shape:
+        raise ValueError("cache shape does not match the layer")
+    slots = np.ascontiguousarray(slots, np.uint32)
+    pos0 = np.ascontiguousarray(pos0, np.uint32)
+    ks = np.ascontiguousarray(ks, np.uint32)
+    rows = int(ks.astype(np.int64).sum())
+    q = np.ascontiguousarray(q, np.float32).reshape(rows, -1) if rows else np.zeros((1, L.n_heads * L.head_dim), np.float32)
+    k_new = np.ascontiguousarray(k_new, np.float32) if rows else np.zeros((1, kv_dim), np.float32)
+    v_new = np.ascontiguousarray(v_new, np.float32) if rows else np.zeros((1, kv_dim), np.float32)
+    out = np.zeros((max(rows, 1), L.n_heads * L.head_dim), np.float32)
+    rc = _load().oracle_verify(
+        L.n_heads, L.n_kv_heads, L.head_dim, _f32(L.q_norm_w, "q_norm_w"),
+        _f32(L.k_norm_w, "k_norm_w"), _f32(L.inv_freq, "inv_freq"),
+        _opt_f32(L.sinks, "sinks"), float(L.eps), float(L.scale),
+        _f32(cache_k, "cache_k"), _f32(cache_v, "cache_v"), n_slots, slot_ctx,
+        _f32(q, "q"), _f32(k_new, "k_new"), _f32(v_new, "v_new"),
+        _u32(slots, "slots"), _u32(pos0, "pos0"), _u32(ks, "ks"), slots.shape[0], _f32(out, "out"))
+    return rc, out[:rows]

@@ -240,3 +240,42 @@ int oracle_prefill(uint32_t n_heads, uint32_t n_kv_heads, uint32_t head_dim,
     }
     return ORACLE_OK;
 }
+
+/* Several rows for each of n_seq sequences (the other system's batched
+ * verify, decode_verify_multi: ks[i] consecutive rows per sequence, rows
+ * sequence-major): sequence i's rows are a slot prefill of slot slots[i] at
+ * positions pos0[i] .. pos0[i]+ks[i]-1, and sequences do not interact (each
+ * owns its slot, so a slot named twice is rejected).  Every check runs before
+ * anything is written. */
+int oracle_verify(uint32_t n_heads, uint32_t n_kv_heads, uint32_t head_dim,
+                  const float *q_norm_w, const float *k_norm_w,
+                  const float *inv_freq, const float *sinks,
+                  float eps, float scale,
+                  float *cache_k, float *cache_v,
+                  uint32_t n_slots, uint32_t slot_ctx,
+                  const float *q, const float *k_new, const float *v_new,
+                  const uint32_t *slots, const uint32_t *pos0, const uint32_t *ks,
+                  uint32_t n_seq, float *out) {
+    if (n_kv_heads == 0 || head_dim == 0) return ORACLE_EINVAL;
+    for (uint32_t i = 0; i < n_seq; ++i) {
+        if (slots[i] >= n_slots || pos0[i] >= slot_ctx || ks[i] > slot_ctx - pos0[i])
+            return ORACLE_ERANGE;
+        for (uint32_t c = 0; c < i; ++c)
+            if (slots[c] == slots[i]) return ORACLE_EDUP;
+    }
+    const uint32_t kv_dim = n_kv_heads * head_dim;
+    const size_t qd = (size_t)n_heads * head_dim;
+    size_t row = 0;
+    for (uint32_t i = 0; i < n_seq; ++i) {
+        if (ks[i] > 0) {
+            int rc = oracle_prefill(n_heads, n_kv_heads, head_dim, q_norm_w, k_norm_w,
+                                    inv_freq, sinks, eps, scale, cache_k, cache_v,
+                                    n_slots, slot_ctx, q + row * qd, k_new + row * kv_dim,
+                                    v_new + row * kv_dim, slots[i], pos0[i], ks[i],
+                                    out + row * qd);
+            if (rc != ORACLE_OK) return rc;
+        }
+        row += ks[i];
+    }
+    return ORACLE_OK;
+}

@@ -40,6 +40,10 @@ MUTANTS = {
     "prefill_ignores_pos0": ("const uint32_t p = pos0 + t;", "const uint32_t p = t;"),
     "prefill_reverse_order": ("const uint32_t p = pos0 + t;", "const uint32_t p = pos0 + (T - 1 - t);"),
     "prefill_range_off_by_one": ("T > slot_ctx - pos0", "T > slot_ctx - pos0 + 1"),
+    # multi-row verify
+    "verify_dup_allowed": ("if (slots[c] == slots[i]) return ORACLE_EDUP;", "continue;"),
+    "verify_rows_not_advanced": ("        row += ks[i];\n", "        row += (ks[i] > 0);\n"),
+    "verify_range_off_by_one": ("ks[i] > slot_ctx - pos0[i]", "ks[i] > slot_ctx - pos0[i] + 1"),
 }
 PIN_FILES = ["test_oracle_pins.py", "test_oracle_prefill_pins.py"]
 

@@ -130,3 +130,63 @@ def test_prefill_range_checks_write_nothing_on_error():
     assert oracle.prefill(L, ck, cv, q, kn, vn, 0, 8)[0] == -2      # first position past the end
     assert np.array_equal(ck, ck0) and np.array_equal(cv, cv0)      # a rejected call writes nothing
     assert oracle.prefill(L, ck, cv, q, kn, vn, 0, 5)[0] == 0       # 5 + 3 == 8 fits
+
+
+# ---------------------------------------------------------------- multi-row verify
+def _verify_setup(rng, H, Hkv, D, n_slots, slot_ctx, slots, pos0, ks):
+    L = make_layer(rng, H, Hkv, D, sinks=True)
+    kv_dim = Hkv * D
+    rows = int(sum(ks))
+    ck = rng.standard_normal((n_slots, slot_ctx, kv_dim)).astype(np.float32)
+    cv = rng.standard_normal((n_slots, slot_ctx, kv_dim)).astype(np.float32)
+    q = rng.standard_normal((rows, H * D)).astype(np.float32)
+    kn = rng.standard_normal((rows, kv_dim)).astype(np.float32)
+    vn = rng.standard_normal((rows, kv_dim)).astype(np.float32)
+    return L, ck, cv, q, kn, vn
+
+
+def test_verify_matches_per_sequence_brute_force():
+    rng = np.random.default_rng(31)
+    slots, pos0, ks = [3, 0, 2, 1], [5, 0, 11, 7], [4, 3, 0, 6]
+    L, ck, cv, q, kn, vn = _verify_setup(rng, 8, 2, 8, 4, 20, slots, pos0, ks)
+    ck0, cv0 = ck.copy(), cv.copy()
+    rc, out = oracle.verify(L, ck, cv, q, kn, vn, slots, pos0, ks)
+    assert rc == 0
+    row = 0
+    for s, p0, k in zip(slots, pos0, ks):
+        if k:
+            ref_out, ref_k = brute_force(L, ck0[s, :p0], cv0[s, :p0], q[row:row + k],
+                                         kn[row:row + k], vn[row:row + k], p0)
+            np.testing.assert_allclose(out[row:row + k], ref_out, rtol=1e-6, atol=1e-7)
+            np.testing.assert_allclose(ck[s, p0:p0 + k], ref_k, rtol=1e-6, atol=1e-7)
+        row += k
+    # rows of a sequence with no rows, and every position outside the calls, untouched
+    touched = np.zeros(ck.shape[:2], bool)
+    for s, p0, k in zip(slots, pos0, ks):
+        touched[s, p0:p0 + k] = True
+    assert np.array_equal(ck[~touched], ck0[~touched]) and np.array_equal(cv[~touched], cv0[~touched])
+
+
+def test_verify_sequences_do_not_interact():
+    rng = np.random.default_rng(32)
+    slots, pos0, ks = [1, 0], [4, 2], [3, 5]
+    L, ck, cv, q, kn, vn = _verify_setup(rng, 4, 2, 8, 2, 12, slots, pos0, ks)
+    ck2, cv2 = ck.copy(), cv.copy()
+    _, out = oracle.verify(L, ck, cv, q, kn, vn, slots, pos0, ks)
+    q2, kn2 = q.copy(), kn.copy()
+    q2[3:] += 1.0      # rows of the second sequence only
+    kn2[3:] -= 1.0
+    _, out2 = oracle.verify(L, ck2, cv2, q2, kn2, vn, slots, pos0, ks)
+    assert np.array_equal(out[:3], out2[:3])
+    assert not np.array_equal(out[3:], out2[3:])
+
+
+def test_verify_rejections_write_nothing():
+    rng = np.random.default_rng(33)
+    L, ck, cv, q, kn, vn = _verify_setup(rng, 2, 1, 4, 3, 8, [0, 1], [0, 0], [2, 2])
+    ck0, cv0 = ck.copy(), cv.copy()
+    assert oracle.verify(L, ck, cv, q, kn, vn, [1, 1], [0, 3], [2, 2])[0] == -5   # slot twice
+    assert oracle.verify(L, ck, cv, q, kn, vn, [0, 3], [0, 0], [2, 2])[0] == -2   # slot range
+    assert oracle.verify(L, ck, cv, q, kn, vn, [0, 1], [0, 7], [2, 2])[0] == -2   # 7 + 2 > 8
+    assert np.array_equal(ck, ck0) and np.array_equal(cv, cv0)
+    assert oracle.verify(L, ck, cv, q, kn, vn, [0, 1], [0, 6], [2, 2])[0] == 0    # 6 + 2 fits
