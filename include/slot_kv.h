@@ -143,6 +143,25 @@ int slot_prefill_attn(slot_kv *h, uint32_t layer, const float *q,
                       const float *k_new, const float *v_new, uint32_t slot,
                       uint32_t pos0, uint32_t T, float *out, void *stream);
 
+/* Several rows per sequence for a batch of sequences (the other system's
+ * batched verify, decode_verify_multi: ks[i] consecutive rows for each of
+ * n_seq sequences, sequence-major).  Sequence i has ks[i] rows at positions
+ * pos0[i] .. pos0[i]+ks[i]-1 of slot slots[i]; its rows follow those of
+ * sequences 0..i-1 in q / k_new / v_new / out.  Every row is processed as
+ * slot_prefill_attn processes the tokens of one sequence: row r of sequence i
+ * attends over positions 0 .. pos0[i]+r of its slot.
+ *   slots, pos0, ks  host [n_seq]; copied before the call returns
+ *   q, out  device [sum ks][n_heads*head_dim]   k_new, v_new  device [sum ks][kv_dim]
+ * Sequences with ks[i] == 0 contribute no rows (their slot and position are
+ * still checked).  n_seq == 0 is a no-op.  Errors: ENOTALLOC, EINVAL (layer
+ * unconfigured or head shape unsupported, NULL pointer), ERANGE (a slot >=
+ * n_slots or pos0[i] + ks[i] > slot_ctx), EDUP (a slot repeated), ENOMEM,
+ * EDEVICE.  Nothing is written when an error is returned. */
+int slot_verify_attn(slot_kv *h, uint32_t layer, const float *q,
+                     const float *k_new, const float *v_new, const uint32_t *slots,
+                     const uint32_t *pos0, const uint32_t *ks, uint32_t n_seq,
+                     float *out, void *stream);
+
 /* Device pointers of layer `layer`'s K and V buffers ([n_slots][slot_ctx]
  * [kv_dim] floats each; owned by the handle, valid until the next
  * slot_kv_alloc or slot_kv_destroy).  Errors: ENOTALLOC, EINVAL. */
@@ -182,7 +201,8 @@ uint32_t slot_kv_chunk_keys(void);
  * slot_kv_profile_end the handle records a HIP event pair on the call's
  * stream immediately around each launch of the fused decode kernel (one
  * launch per 256 rows of a slot_decode_attn call; it does the whole step) and
- * of the prefill attention kernel (one per slot_prefill_attn call).
+ * of the prefill attention kernel (one per slot_prefill_attn call, one per
+ * 128 sequences of a slot_verify_attn call).
  * slot_kv_profile_end waits for the recorded launches and returns their
  * summed duration in milliseconds and their count (either pointer may be
  * NULL), then stops recording.  Errors: EINVAL, EDEVICE. */

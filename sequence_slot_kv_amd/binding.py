@@ -28,6 +28,7 @@ SLOT_KV_EDEVICE = -6
 # Every symbol include/slot_kv.h declares.
 EXPORTS = ("slot_kv_create", "slot_kv_destroy", "slot_kv_alloc", "slot_kv_set_layer",
            "slot_kv_offset_bytes", "slot_reset", "slot_decode_attn", "slot_prefill_attn",
+           "slot_verify_attn",
            "slot_kv_layer_ptrs",
            "slot_kv_write_rows", "slot_kv_read_rows", "slot_kv_check_batch",
            "slot_kv_chunk_keys", "slot_kv_profile_begin", "slot_kv_profile_end",
@@ -59,6 +60,7 @@ _lib.slot_kv_offset_bytes.argtypes = [_vp, _u32, _u32, _u32, ctypes.POINTER(ctyp
 _lib.slot_reset.argtypes = [_vp, _u32]
 _lib.slot_decode_attn.argtypes = [_vp, _u32, _vp, _vp, _vp, _u32p, _u32p, _u32, _vp, _vp]
 _lib.slot_prefill_attn.argtypes = [_vp, _u32, _vp, _vp, _vp, _u32, _u32, _u32, _vp, _vp]
+_lib.slot_verify_attn.argtypes = [_vp, _u32, _vp, _vp, _vp, _u32p, _u32p, _u32p, _u32, _vp, _vp]
 _lib.slot_kv_layer_ptrs.argtypes = [_vp, _u32, ctypes.POINTER(_vp), ctypes.POINTER(_vp)]
 _lib.slot_kv_write_rows.argtypes = [_vp, _u32, _u32, _u32, _u32, _vp, _vp, _vp]
 _lib.slot_kv_read_rows.argtypes = [_vp, _u32, _u32, _u32, _u32, _vp, _vp, _vp]
@@ -193,6 +195,17 @@ def slot_prefill_attn(h, layer, q, k_new, v_new, slot, pos0, out, stream=None) -
                                   _stream_handle(stream))
 
 
+def slot_verify_attn(h, layer, q, k_new, v_new, slots, pos0, ks, out, stream=None) -> int:
+    """Raw call: q/k_new/v_new/out are GPU float32 tensors of sum(ks) rows,
+    slots/pos0/ks host integer sequences of one entry per sequence."""
+    sl, p0, k = _host_u32(slots), _host_u32(pos0), _host_u32(ks)
+    if not (sl.shape == p0.shape == k.shape) or sl.ndim != 1:
+        return SLOT_KV_EINVAL
+    ptrs = [_dev_ptr(t, n) for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (out, "out"))]
+    return _lib.slot_verify_attn(h, layer, ptrs[0], ptrs[1], ptrs[2], _ptr_u32(sl), _ptr_u32(p0),
+                                 _ptr_u32(k), int(sl.shape[0]), ptrs[3], _stream_handle(stream))
+
+
 def slot_kv_layer_ptrs(h, layer):
     """Returns (status, k_ptr, v_ptr)."""
     k, v = _vp(), _vp()
@@ -320,6 +333,23 @@ class SlotKV:
                     raise ValueError(f"{n}: expected {T}x{w} elements, got {tuple(t.shape)}")
         _check(slot_prefill_attn(self.h, layer, q, k_new, v_new, slot, pos0, out, stream),
                "slot_prefill_attn")
+        return out
+
+    def verify_attn(self, layer, q, k_new, v_new, slots, pos0, ks, out=None, stream=None):
+        """ks[i] rows for each sequence i at positions pos0[i].. of slots[i]
+        (rows sequence-major); returns out [sum ks, n_heads*head_dim]."""
+        import torch
+        if out is None:
+            out = torch.empty_like(q)
+        P = self.layers.get(layer)
+        if P is not None:
+            rows = int(np.asarray(ks, np.int64).sum())
+            for t, n, w in ((q, "q", P.n_heads * P.head_dim), (k_new, "k_new", P.kv_dim),
+                            (v_new, "v_new", P.kv_dim), (out, "out", P.n_heads * P.head_dim)):
+                if t.numel() != rows * w:
+                    raise ValueError(f"{n}: expected {rows}x{w} elements, got {tuple(t.shape)}")
+        _check(slot_verify_attn(self.h, layer, q, k_new, v_new, slots, pos0, ks, out, stream),
+               "slot_verify_attn")
         return out
 
     def layer_view(self, layer):

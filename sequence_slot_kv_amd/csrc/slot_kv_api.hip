@@ -46,7 +46,8 @@ struct slot_kv {
   uint32_t* counters = nullptr;  // work queue [2], then per (row, kv head) chunk counters;
                                  // all zero between launches
   size_t counters_cap = 0;       // entries
-  AttnArgs args;                 // kernel arguments of the launch being built
+  AttnArgs args;                 // kernel arguments of the decode launch being built
+  slotkv::PrefillArgs pargs;     // kernel arguments of the prefill launch being built
   bool profiling = false;
   std::vector<hipEvent_t> prof_events;  // start/end pairs
   size_t prof_used = 0;                 // pairs recorded since profile_begin
@@ -371,6 +372,93 @@ int slot_decode_attn(slot_kv* h, uint32_t layer, const float* q, const float* k_
   return SLOT_KV_OK;
 }
 
+namespace {
+
+// One sequence of a prefill / verify call: `len` rows starting at row `row`
+// of the call's q / k_new / v_new / out, at positions pos0 .. pos0+len-1.
+struct SeqRows {
+  uint32_t slot, pos0, len, row;
+};
+
+// Validated sequences of a call (no zero-length ones) -> launches of at most
+// kMaxSeqPerLaunch sequences, each sequence-major in the caller's buffers.
+int run_prefill(slot_kv* h, uint32_t layer, const float* q, const float* k_new,
+                const float* v_new, float* out, const std::vector<SeqRows>& seqs, void* stream) {
+  LayerState& L = h->layers[layer];
+  const uint32_t G = L.n_heads / L.n_kv_heads;
+  if (!slotkv::decode_shape_supported(L.head_dim, G)) return SLOT_KV_EINVAL;
+  const size_t D = L.head_dim;
+  const uint32_t M = slotkv::kMaxSeqPerLaunch;
+  // scratch for the rotated queries of the largest launch, before any enqueue
+  size_t max_rows = 0;
+  for (size_t s0 = 0; s0 < seqs.size(); s0 += M) {
+    size_t rows = 0;
+    for (size_t i = s0; i < std::min(seqs.size(), s0 + M); ++i) rows += seqs[i].len;
+    max_rows = std::max(max_rows, rows);
+  }
+  int rc = ensure_partials(h, max_rows * L.n_heads * D);
+  if (rc) return rc;
+
+  slotkv::PrefillArgs& a = h->pargs;
+  a.magic = slotkv::kArgsMagic;
+  slotkv::PrefillParams& p = a.p;
+  p.k_cache = L.k;
+  p.v_cache = L.v;
+  p.qs = h->part;
+  p.q_norm_w = L.params;
+  p.k_norm_w = L.params + D;
+  p.inv_freq = L.params + 2 * D;
+  p.sinks = L.has_sinks ? L.params + 2 * D + D / 2 : nullptr;
+  p.slot_stride = static_cast<uint64_t>(h->slot_ctx) * L.kv_dim;
+  p.kv_dim = L.kv_dim;
+  p.n_heads = L.n_heads;
+  p.n_kv_heads = L.n_kv_heads;
+  p.eps = L.eps;
+  p.qk_scale_log2 = L.scale * 1.4426950408889634f;
+  const size_t qd = static_cast<size_t>(L.n_heads) * D;
+  for (size_t s0 = 0; s0 < seqs.size(); s0 += M) {
+    const uint32_t n = static_cast<uint32_t>(std::min<size_t>(seqs.size() - s0, M));
+    const uint32_t first_row = seqs[s0].row;
+    uint32_t rows = 0;
+    std::vector<uint64_t> work(n);
+    for (uint32_t i = 0; i < n; ++i) {
+      const SeqRows& r = seqs[s0 + i];
+      a.s.slot[i] = r.slot;
+      a.s.pos0[i] = r.pos0;
+      a.s.len[i] = r.len;
+      a.s.row_off[i] = rows;
+      rows += r.len;
+      a.s.by_work[i] = i;
+      work[i] = static_cast<uint64_t>(r.len) * (2ull * r.pos0 + r.len);  // ~ keys scored
+    }
+    a.s.row_off[n] = rows;
+    std::stable_sort(a.s.by_work, a.s.by_work + n,
+                     [&](uint32_t x, uint32_t y) { return work[x] > work[y]; });
+    uint32_t groups = 0;
+    for (uint32_t k = 0; k < n; ++k) {
+      a.s.grp_off[k] = groups;
+      const uint32_t tiles = (a.s.len[a.s.by_work[k]] * G + 15) / 16;
+      groups += (tiles * 16 + slotkv::kPrefillRowsPerGroup - 1) / slotkv::kPrefillRowsPerGroup;
+    }
+    a.s.grp_off[n] = groups;
+    p.n_seq = n;
+    p.n_rows = rows;
+    p.n_groups = groups;
+    p.q = q + first_row * qd;
+    p.k_new = k_new + static_cast<size_t>(first_row) * L.kv_dim;
+    p.v_new = v_new + static_cast<size_t>(first_row) * L.kv_dim;
+    p.out = out + first_row * qd;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    rc = prof_pair(h, &e0, &e1);
+    if (rc) return rc;
+    if (slotkv::launch_prefill(a, L.head_dim, G, stream, e0, e1) != hipSuccess)
+      return SLOT_KV_EDEVICE;
+  }
+  return SLOT_KV_OK;
+}
+
+}  // namespace
+
 int slot_prefill_attn(slot_kv* h, uint32_t layer, const float* q, const float* k_new,
                       const float* v_new, uint32_t slot, uint32_t pos0, uint32_t T,
                       float* out, void* stream) {
@@ -381,43 +469,39 @@ int slot_prefill_attn(slot_kv* h, uint32_t layer, const float* q, const float* k
   if (T == 0) return SLOT_KV_OK;
   if (!q || !k_new || !v_new || !out) return SLOT_KV_EINVAL;
   if (slot >= h->n_slots || static_cast<uint64_t>(pos0) + T > h->slot_ctx) return SLOT_KV_ERANGE;
-  const uint32_t G = L.n_heads / L.n_kv_heads;
-  if (!slotkv::decode_shape_supported(L.head_dim, G)) return SLOT_KV_EINVAL;
   if (static_cast<uint64_t>(T) * (L.n_heads + L.n_kv_heads) >= (uint64_t(1) << 31))
-    return SLOT_KV_EINVAL;  // keeps the kernels' 32-bit vector and tile counts exact
-  const size_t D = L.head_dim;
-  // rotated queries: the split-row scratch serves (calls on one handle are
-  // ordered on one stream)
-  rc = ensure_partials(h, static_cast<size_t>(T) * L.n_heads * D);
-  if (rc) return rc;
+    return SLOT_KV_EINVAL;  // keeps the kernels' 32-bit row and tile counts exact
+  return run_prefill(h, layer, q, k_new, v_new, out, {SeqRows{slot, pos0, T, 0}}, stream);
+}
 
-  slotkv::PrefillParams p{};
-  p.k_cache = L.k;
-  p.v_cache = L.v;
-  p.q = q;
-  p.k_new = k_new;
-  p.v_new = v_new;
-  p.qs = h->part;
-  p.out = out;
-  p.q_norm_w = L.params;
-  p.k_norm_w = L.params + D;
-  p.inv_freq = L.params + 2 * D;
-  p.sinks = L.has_sinks ? L.params + 2 * D + D / 2 : nullptr;
-  p.slot_base = static_cast<uint64_t>(slot) * h->slot_ctx * L.kv_dim;
-  p.kv_dim = L.kv_dim;
-  p.n_heads = L.n_heads;
-  p.n_kv_heads = L.n_kv_heads;
-  p.T = T;
-  p.pos0 = pos0;
-  p.n_tiles = static_cast<uint32_t>((static_cast<uint64_t>(T) * G + 15) / 16);
-  p.eps = L.eps;
-  p.qk_scale_log2 = L.scale * 1.4426950408889634f;
-  hipEvent_t e0 = nullptr, e1 = nullptr;
-  rc = prof_pair(h, &e0, &e1);
+int slot_verify_attn(slot_kv* h, uint32_t layer, const float* q, const float* k_new,
+                     const float* v_new, const uint32_t* slots, const uint32_t* pos0,
+                     const uint32_t* ks, uint32_t n_seq, float* out, void* stream) {
+  int rc = check_layer(h, layer);
   if (rc) return rc;
-  if (slotkv::launch_prefill(p, L.head_dim, G, stream, e0, e1) != hipSuccess)
-    return SLOT_KV_EDEVICE;
-  return SLOT_KV_OK;
+  LayerState& L = h->layers[layer];
+  if (!L.configured) return SLOT_KV_EINVAL;
+  if (n_seq == 0) return SLOT_KV_OK;
+  if (!slots || !pos0 || !ks) return SLOT_KV_EINVAL;
+  std::vector<SeqRows> seqs;
+  seqs.reserve(n_seq);
+  std::vector<uint64_t> seen((static_cast<size_t>(h->n_slots) + 63) / 64, 0);
+  uint64_t rows = 0;
+  for (uint32_t i = 0; i < n_seq; ++i) {
+    if (slots[i] >= h->n_slots || pos0[i] >= h->slot_ctx ||
+        static_cast<uint64_t>(pos0[i]) + ks[i] > h->slot_ctx)
+      return SLOT_KV_ERANGE;
+    uint64_t& word = seen[slots[i] >> 6];
+    const uint64_t bit = uint64_t(1) << (slots[i] & 63);
+    if (word & bit) return SLOT_KV_EDUP;
+    word |= bit;
+    if (ks[i]) seqs.push_back(SeqRows{slots[i], pos0[i], ks[i], static_cast<uint32_t>(rows)});
+    rows += ks[i];
+    if (rows * (L.n_heads + L.n_kv_heads) >= (uint64_t(1) << 31)) return SLOT_KV_EINVAL;
+  }
+  if (seqs.empty()) return SLOT_KV_OK;
+  if (!q || !k_new || !v_new || !out) return SLOT_KV_EINVAL;
+  return run_prefill(h, layer, q, k_new, v_new, out, seqs, stream);
 }
 
 int slot_kv_layer_ptrs(const slot_kv* h, uint32_t layer, float** k, float** v) {

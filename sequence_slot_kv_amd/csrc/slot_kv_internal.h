@@ -65,34 +65,57 @@ struct AttnArgs {
 };
 static_assert(sizeof(AttnArgs) < 4000, "kernel arguments must stay below 4 KiB");
 
-// Parameters of a slot prefill (T tokens of one slot at pos0 .. pos0+T-1).
+// Sequences of one prefill / verify launch: sequence i has len[i] token rows
+// (rows row_off[i] .. row_off[i+1]-1 of the launch, sequence-major) at
+// positions pos0[i] .. pos0[i]+len[i]-1 of slot slot[i].
+constexpr uint32_t kMaxSeqPerLaunch = 128;
+
 struct PrefillParams {
   float* k_cache;          // layer K buffer
   float* v_cache;          // layer V buffer
-  const float* q;          // [T][n_heads*D]
-  const float* k_new;      // [T][kv_dim]
-  const float* v_new;      // [T][kv_dim]
-  float* qs;               // [T][n_heads][D] rotated queries times scale*log2(e) (scratch)
-  float* out;              // [T][n_heads*D]
+  const float* q;          // [n_rows][n_heads*D]
+  const float* k_new;      // [n_rows][kv_dim]
+  const float* v_new;      // [n_rows][kv_dim]
+  float* qs;               // [n_rows][n_heads][D] rotated queries times scale*log2(e) (scratch)
+  float* out;              // [n_rows][n_heads*D]
   const float* q_norm_w;   // [D]
   const float* k_norm_w;   // [D]
   const float* inv_freq;   // [D/2]
   const float* sinks;      // [n_heads] or nullptr
-  uint64_t slot_base;      // slot * slot_ctx * kv_dim (floats): the slot's row 0
+  uint64_t slot_stride;    // slot_ctx * kv_dim (floats)
   uint32_t kv_dim;
   uint32_t n_heads;
   uint32_t n_kv_heads;
-  uint32_t T;
-  uint32_t pos0;
-  uint32_t n_tiles;        // 16-row query tiles per kv head: ceil(T * G / 16)
+  uint32_t n_seq;          // sequences of this launch
+  uint32_t n_rows;         // token rows of this launch
+  uint32_t n_groups;       // attention workgroups per kv head (all sequences)
   float eps;
   float qk_scale_log2;     // scale * log2(e)
 };
 
-// Launches of a prefill: norm + RoPE + KV write, then the attention.
-// `before_attn` / `after_attn` (hipEvent_t or null) are recorded around the
-// attention kernel.  Returns a hipError_t value.
-int launch_prefill(const PrefillParams& p, uint32_t head_dim, uint32_t group, void* stream,
+struct PrefillSeqs {
+  uint32_t slot[kMaxSeqPerLaunch];
+  uint32_t pos0[kMaxSeqPerLaunch];
+  uint32_t len[kMaxSeqPerLaunch];
+  uint32_t row_off[kMaxSeqPerLaunch + 1];  // first row of each sequence (and the total)
+  uint32_t by_work[kMaxSeqPerLaunch];      // the sequences, most attention work first
+  uint32_t grp_off[kMaxSeqPerLaunch + 1];  // first workgroup of by_work[k] (per kv head)
+};
+
+struct PrefillArgs {
+  PrefillParams p;
+  PrefillSeqs s;
+  uint32_t magic;  // kArgsMagic; the kernels do nothing if they read another value
+};
+static_assert(sizeof(PrefillArgs) < 4000, "kernel arguments must stay below 4 KiB");
+
+// Query rows per attention workgroup of a prefill (4 waves x 16 rows).
+constexpr uint32_t kPrefillRowsPerGroup = 64;
+
+// Launches of a prefill / verify: norm + RoPE + KV write, then the
+// attention.  `before_attn` / `after_attn` (hipEvent_t or null) are recorded
+// around the attention kernel.  Returns a hipError_t value.
+int launch_prefill(const PrefillArgs& a, uint32_t head_dim, uint32_t group, void* stream,
                    void* before_attn, void* after_attn);
 
 // Validation of one batch (no device access).  Returns a SLOT_KV_* status.

@@ -1,16 +1,19 @@
-// slot_kv_prefill.hip -- gfx950 kernels of a slot prefill: T tokens of one
-// sequence into its slot ("Forward Cuda": batched prefill that writes the KV
-// cache into the slot's per-sequence region; "Forward Cuda Gemma",
-// prefillBatched, equal to the one-token step run over the tokens in order).
+// slot_kv_prefill.hip -- gfx950 kernels of a slot prefill / multi-row verify:
+// several token rows per sequence, each sequence in its own slot ("Forward
+// Cuda": batched prefill that writes the KV cache into the slot's
+// per-sequence region; "Forward Cuda Gemma", prefillBatched, equal to the
+// one-token step run over the tokens in order; the other system's batched
+// verify of ks[i] consecutive rows for each of n_seqs sequences).
 //
 // Two launches on the caller's stream:
-//   prep  one wave per head vector of a token: RMSNorm, then RoPE at the
-//         token's position; a query head goes to a scratch buffer (times
-//         scale*log2(e)), a key head and its value row go into the slot.
-//   attn  causal attention of every token over positions 0 .. pos0+t, now
-//         all in the cache.  Unlike decode this is a dense contraction
-//         (T*G query rows against each key block), so it runs on the matrix
-//         cores: v_mfma_f32_16x16x4f32 in its transposed form
+//   prep  one workgroup per token row: cos / sin of the row's angles once in
+//         LDS, then one wave per head vector: RMSNorm and RoPE; a query head
+//         goes to a scratch buffer (times scale*log2(e)), a key head and its
+//         value row go into the slot.
+//   attn  causal attention of every row over its slot's positions
+//         0 .. pos0+t, now all in the cache.  Many query rows meet each key
+//         block, so this is a dense contraction and runs on the matrix cores:
+//         v_mfma_f32_16x16x4f32 in its transposed form
 //             S^T = K * Q^T   (16 keys x 16 query rows, summed over head_dim)
 //             O^T += V^T * P^T (16 head_dim values x 16 rows, summed over keys)
 //         With the key order chosen below, the score registers of S^T are
@@ -28,6 +31,7 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 constexpr int kPrepWaves = 4;
 constexpr int kAttnWaves = 4;
+static_assert(kAttnWaves * 16 == kPrefillRowsPerGroup, "rows per attention workgroup");
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -38,91 +42,142 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// One wave per head vector: vector v of token t is query head v (v < H) or
-// kv head v - H.  Lane l holds elements l*EPL .. l*EPL+EPL-1, so the RoPE
-// partner d +- D/2 of an element sits in lane l ^ 32.
+// The sequence holding launch row `row`: the last i with row_off[i] <= row.
+__device__ __forceinline__ uint32_t seq_of_row(const PrefillArgs& a, uint32_t row) {
+  uint32_t lo = 0, hi = a.p.n_seq;
+  while (hi - lo > 1) {
+    const uint32_t mid = (lo + hi) / 2;
+    if (a.s.row_off[mid] <= row) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// One workgroup per token row.  Lane l of a wave holds elements
+// l*EPL .. l*EPL+EPL-1 of a head vector, so the RoPE partner d +- D/2 of an
+// element sits in lane l ^ 32 and both use angle (l & 31)*EPL + e.
 template <int D>
-__global__ void __launch_bounds__(kWave * kPrepWaves) prefill_prep_kernel(const PrefillParams p) {
+__global__ void __launch_bounds__(kWave * kPrepWaves) prefill_prep_kernel(const PrefillArgs a) {
   constexpr int EPL = D / kWave;
-  const uint32_t lane = threadIdx.x % kWave;
-  const uint32_t vec = blockIdx.x * kPrepWaves + threadIdx.x / kWave;
-  const uint32_t per_tok = p.n_heads + p.n_kv_heads;
-  if (vec >= p.T * per_tok) return;  // wave-uniform
-  const uint32_t t = vec / per_tok, v = vec % per_tok;
-  const uint32_t pos = p.pos0 + t;
-  const bool is_q = v < p.n_heads;
-  const uint32_t kvh = v - p.n_heads;
-  const float* src = is_q ? p.q + (static_cast<size_t>(t) * p.n_heads + v) * D
-                          : p.k_new + static_cast<size_t>(t) * p.kv_dim + kvh * D;
-  const float* w = is_q ? p.q_norm_w : p.k_norm_w;
-  float x[EPL];
-  float ss = 0.f;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    x[e] = src[lane * EPL + e];
-    ss += x[e] * x[e];
-  }
-  ss = wave_sum(ss);
-  const float rn = 1.0f / sqrtf(ss * (1.0f / D) + p.eps);
+  __shared__ float cs[D / 2], sn[D / 2];
+  if (a.magic != kArgsMagic) return;  // argument block not delivered whole
+  const PrefillParams& p = a.p;
+  const uint32_t row = blockIdx.x;  // < n_rows
+  const uint32_t i = seq_of_row(a, row);
+  const uint32_t t = row - a.s.row_off[i];
+  const uint32_t pos = a.s.pos0[i] + t;
   const float fpos = static_cast<float>(pos);
-  float y[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    const float xn = x[e] * rn * w[lane * EPL + e];
-    const float partner = __shfl_xor(xn, 32);
-    const float ang = fpos * p.inv_freq[(lane & 31) * EPL + e];  // one f32 multiply
-    float sn, cs;
-    sincosf(ang, &sn, &cs);
-    y[e] = lane < 32 ? xn * cs - partner * sn : xn * cs + partner * sn;
+  for (uint32_t e = threadIdx.x; e < D / 2; e += kWave * kPrepWaves) {
+    const float ang = fpos * p.inv_freq[e];  // one f32 multiply
+    float s_, c_;
+    sincosf(ang, &s_, &c_);
+    sn[e] = s_;
+    cs[e] = c_;
   }
-  if (is_q) {
-    float* dst = p.qs + (static_cast<size_t>(t) * p.n_heads + v) * D + lane * EPL;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) dst[e] = y[e] * p.qk_scale_log2;
-  } else {
-    const size_t at = p.slot_base + static_cast<size_t>(pos) * p.kv_dim + kvh * D + lane * EPL;
-    const float* vsrc = p.v_new + static_cast<size_t>(t) * p.kv_dim + kvh * D + lane * EPL;
+  __syncthreads();
+  const uint32_t lane = threadIdx.x % kWave;
+  const uint64_t at_row = a.s.slot[i] * p.slot_stride + static_cast<uint64_t>(pos) * p.kv_dim;
+  for (uint32_t v = threadIdx.x / kWave; v < p.n_heads + p.n_kv_heads; v += kPrepWaves) {
+    const bool is_q = v < p.n_heads;  // wave-uniform
+    const uint32_t kvh = v - p.n_heads;
+    const float* src = is_q ? p.q + (static_cast<size_t>(row) * p.n_heads + v) * D
+                            : p.k_new + static_cast<size_t>(row) * p.kv_dim + kvh * D;
+    const float* w = is_q ? p.q_norm_w : p.k_norm_w;
+    float x[EPL];
+    float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-      p.k_cache[at + e] = y[e];
-      p.v_cache[at + e] = vsrc[e];
+      x[e] = src[lane * EPL + e];
+      ss += x[e] * x[e];
+    }
+    ss = wave_sum(ss);
+    const float rn = 1.0f / sqrtf(ss * (1.0f / D) + p.eps);
+    float y[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const float xn = x[e] * rn * w[lane * EPL + e];
+      const float partner = __shfl_xor(xn, 32);
+      const uint32_t k = (lane & 31) * EPL + e;
+      y[e] = lane < 32 ? xn * cs[k] - partner * sn[k] : xn * cs[k] + partner * sn[k];
+    }
+    if (is_q) {
+      float* dst = p.qs + (static_cast<size_t>(row) * p.n_heads + v) * D + lane * EPL;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) dst[e] = y[e] * p.qk_scale_log2;
+    } else {
+      const uint64_t at = at_row + kvh * D + lane * EPL;
+      const float* vsrc = p.v_new + static_cast<size_t>(row) * p.kv_dim + kvh * D + lane * EPL;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        p.k_cache[at + e] = y[e];
+        p.v_cache[at + e] = vsrc[e];
+      }
     }
   }
 }
 
-// One wave per tile of 16 query rows of one kv head j.  Row r of tile k is
-// row R = 16k + r of the head group: token R / G, query head j*G + R % G.
-// Lane l works on row c = l % 16 and lane group g = l / 16:
+// A workgroup of four waves takes four consecutive tiles of 16 query rows of
+// one sequence and one kv head j; row r of tile k is row R = 16k + r of the
+// head group: token R / G of the sequence, query head j*G + R % G.  The
+// workgroup walks the key blocks of its last (longest) tile, 16 keys at a
+// time: all 256 threads stage a block's K and V rows in LDS
+// (double-buffered), then each wave takes its MFMA operands from there.  Lane
+// l works on row c = l % 16 and lane group g = l / 16:
 //   S^T block:  A = K[key c][d], B = Q[row c][d] with d = (D/4)*g + i for
 //               MFMA i < D/4; result lane l, register r: key 4g + r, row c;
 //   O^T tile u: MFMA m < 4 sums key 4g + m (A = V[key][d], d = (D/16)*c + u;
 //               B = the score register m); result lane l, register r:
 //               d = (D/16)*(4g + r) + u, row c.
 // So a lane's whole accumulator belongs to its own row, and its output
-// values are d = (D/4)*g .. (D/4)*g + D/4 - 1.  Tiles are launched heaviest
-// first (last tokens first) so that the short ones fill in at the end.
+// values are d = (D/4)*g .. (D/4)*g + D/4 - 1.  Workgroups are launched
+// heaviest first: sequences by decreasing work, and inside a sequence its
+// last tokens first, so that the short ones fill in at the end.
+constexpr int kLdsPad = 4;  // floats of padding per staged row: rows start 4 banks apart
+
+template <int D>
+struct PrefillLds {
+  float k[2][16][D + kLdsPad];
+  float v[2][16][D + kLdsPad];
+};
+
 template <int D, int G>
-__global__ void __launch_bounds__(kWave * kAttnWaves) prefill_attn_kernel(const PrefillParams p) {
+__global__ void __launch_bounds__(kWave * kAttnWaves) prefill_attn_kernel(const PrefillArgs a) {
   constexpr int DQ = D / 4;   // head_dim values per lane group
   constexpr int TD = D / 16;  // output tiles of 16 head_dim values
-  static_assert(DQ % 4 == 0 && TD % 4 == 0, "float4 loads");
-  const uint32_t lane = threadIdx.x % kWave;
+  constexpr int NF4 = 16 * D / 4 / (kWave * kAttnWaves);  // staged float4 per thread per block
+  static_assert(DQ % 4 == 0 && TD % 4 == 0 && NF4 >= 1, "float4 staging");
+  __shared__ __attribute__((aligned(16))) PrefillLds<D> sh;
+  if (a.magic != kArgsMagic) return;  // argument block not delivered whole
+  const PrefillParams& p = a.p;
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid % kWave;
+  const uint32_t w = tid / kWave;
   const uint32_t g = lane / 16, c = lane % 16;
-  const uint32_t wave = blockIdx.x * kAttnWaves + threadIdx.x / kWave;
-  if (wave >= p.n_tiles * p.n_kv_heads) return;  // wave-uniform
-  const uint32_t j = wave % p.n_kv_heads;
-  const uint32_t tile = p.n_tiles - 1 - wave / p.n_kv_heads;
+  // workgroup -> (kv head, sequence, tile group), heaviest first
+  const uint32_t j = blockIdx.x % p.n_kv_heads;
+  const uint32_t flat = blockIdx.x / p.n_kv_heads;  // < n_groups
+  uint32_t lo = 0, hi = p.n_seq;
+  while (hi - lo > 1) {
+    const uint32_t mid = (lo + hi) / 2;
+    if (a.s.grp_off[mid] <= flat) lo = mid; else hi = mid;
+  }
+  const uint32_t sq = a.s.by_work[lo];
+  const uint32_t grp = a.s.grp_off[lo + 1] - 1 - flat;  // the sequence's last group first
+  const uint32_t T = a.s.len[sq], pos0 = a.s.pos0[sq], row0 = a.s.row_off[sq];
+  const uint32_t n_tiles = (T * G + 15) / 16;
+  const uint32_t tile = grp * kAttnWaves + w;  // may be past the last tile: then it only stages
   const uint32_t R = tile * 16 + c;
   const uint32_t t = R / G, h = j * G + R % G;
-  const bool row_ok = t < p.T;
-  const uint32_t tq = row_ok ? t : p.T - 1;  // rows past the last token compute on it, unused
-  const uint32_t row_pos = p.pos0 + tq;
-  const uint32_t t_last = min((tile * 16 + 15) / G, p.T - 1);
-  const uint32_t n_keys = p.pos0 + t_last + 1;  // keys 0 .. position of the tile's last token
+  const bool row_ok = t < T;
+  const uint32_t tq = row_ok ? t : T - 1;  // rows past the last token compute on it, unused
+  const uint32_t row_pos = pos0 + tq;
+  // keys of this wave's tile, and of the workgroup (its last existing tile)
+  const uint32_t wave_keys = pos0 + min((tile * 16 + 15) / G, T - 1) + 1;
+  const uint32_t last_tile = min(grp * kAttnWaves + kAttnWaves - 1, n_tiles - 1);
+  const uint32_t n_keys = pos0 + min((last_tile * 16 + 15) / G, T - 1) + 1;
 
   float qv[DQ];
   {
-    const float* qsrc = p.qs + (static_cast<size_t>(tq) * p.n_heads + h) * D + DQ * g;
+    const float* qsrc = p.qs + (static_cast<size_t>(row0 + tq) * p.n_heads + h) * D + DQ * g;
 #pragma unroll
     for (int i = 0; i < DQ; i += 4) {
       const f4 v = *reinterpret_cast<const f4*>(qsrc + i);
@@ -132,8 +187,31 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) prefill_attn_kernel(const 
       qv[i + 3] = v[3];
     }
   }
-  const float* kbase = p.k_cache + p.slot_base + j * D;
-  const float* vbase = p.v_cache + p.slot_base + j * D;
+  const uint64_t slot_base = a.s.slot[sq] * p.slot_stride;
+  const float* kbase = p.k_cache + slot_base + j * D;
+  const float* vbase = p.v_cache + slot_base + j * D;
+  // Staging: float4 f = tid + 256*s of a block is row f / (D/4), column
+  // 4 * (f % (D/4)).  Keys past the workgroup's range re-read its last key.
+  f4 stk[NF4], stv[NF4];
+  auto fetch = [&](uint32_t kb) {
+#pragma unroll
+    for (int s = 0; s < NF4; ++s) {
+      const uint32_t f = tid + kWave * kAttnWaves * s;
+      const uint32_t row = f / (D / 4), col = 4 * (f % (D / 4));
+      const size_t at = static_cast<size_t>(min(kb + row, n_keys - 1)) * p.kv_dim + col;
+      stk[s] = *reinterpret_cast<const f4*>(kbase + at);
+      stv[s] = *reinterpret_cast<const f4*>(vbase + at);
+    }
+  };
+  auto stage = [&](uint32_t buf) {
+#pragma unroll
+    for (int s = 0; s < NF4; ++s) {
+      const uint32_t f = tid + kWave * kAttnWaves * s;
+      const uint32_t row = f / (D / 4), col = 4 * (f % (D / 4));
+      *reinterpret_cast<f4*>(&sh.k[buf][row][col]) = stk[s];
+      *reinterpret_cast<f4*>(&sh.v[buf][row][col]) = stv[s];
+    }
+  };
 
   float m_run = -INFINITY, l_run = 0.f;
   f4 o[TD];
@@ -141,61 +219,55 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) prefill_attn_kernel(const 
   for (int u = 0; u < TD; ++u) o[u] = f4{0.f, 0.f, 0.f, 0.f};
 
   const uint32_t n_blk = (n_keys + 15) / 16;
-  for (uint32_t blk = 0; blk < n_blk; ++blk) {
+  fetch(0);
+  stage(0);
+  __syncthreads();
+  for (uint32_t blk = 0; blk < n_blk; ++blk) {  // workgroup-uniform
+    const uint32_t buf = blk & 1;
     const uint32_t kb = blk * 16;
-    // keys past the tile's range re-read its last key (their scores are masked)
-    float ka[DQ];
-    {
-      const float* kr = kbase + static_cast<size_t>(min(kb + c, n_keys - 1)) * p.kv_dim + DQ * g;
+    if (blk + 1 < n_blk) fetch(kb + 16);
+    if (kb < wave_keys) {  // wave-uniform: blocks past the tile are all masked
+      f4 s = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < DQ; i += 4) {
-        const f4 v = *reinterpret_cast<const f4*>(kr + i);
-        ka[i] = v[0];
-        ka[i + 1] = v[1];
-        ka[i + 2] = v[2];
-        ka[i + 3] = v[3];
+        const f4 ka = *reinterpret_cast<const f4*>(&sh.k[buf][c][DQ * g + i]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          s = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[e], qv[i + e], s, 0, 0, 0);
       }
-    }
-    float va[4][TD];
+      // causal mask: key kb + 4g + r is visible to the row iff it is <= the
+      // row's position (every key >= n_keys is also past every row)
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const float* vr =
-          vbase + static_cast<size_t>(min(kb + 4 * g + m, n_keys - 1)) * p.kv_dim + TD * c;
+      for (int r = 0; r < 4; ++r)
+        if (kb + 4 * g + r > row_pos) s[r] = -INFINITY;
+      float mb = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+      mb = fmaxf(mb, __shfl_xor(mb, 16));
+      mb = fmaxf(mb, __shfl_xor(mb, 32));
+      const float m_new = fmaxf(m_run, mb);  // finite: key 0 is visible to every row
+      const float corr = fast_exp2(m_run - m_new);
+      f4 pr;
 #pragma unroll
-      for (int u = 0; u < TD; u += 4) {
-        const f4 v = *reinterpret_cast<const f4*>(vr + u);
-        va[m][u] = v[0];
-        va[m][u + 1] = v[1];
-        va[m][u + 2] = v[2];
-        va[m][u + 3] = v[3];
+      for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(s[r] - m_new);
+      l_run = l_run * corr + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+#pragma unroll
+      for (int u = 0; u < TD; ++u) o[u] *= corr;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+#pragma unroll
+        for (int u = 0; u < TD; u += 4) {
+          const f4 va = *reinterpret_cast<const f4*>(&sh.v[buf][4 * g + m][TD * c + u]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            o[u + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(va[e], pr[m], o[u + e], 0, 0, 0);
+        }
       }
+      m_run = m_new;
     }
-    f4 s = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < DQ; ++i) s = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[i], qv[i], s, 0, 0, 0);
-    // causal mask: key kb + 4g + r is visible to the row iff it is <= the
-    // row's position (every key >= n_keys is also past the row)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (kb + 4 * g + r > row_pos) s[r] = -INFINITY;
-    float mb = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    mb = fmaxf(mb, __shfl_xor(mb, 16));
-    mb = fmaxf(mb, __shfl_xor(mb, 32));
-    const float m_new = fmaxf(m_run, mb);  // finite: key 0 is visible to every row
-    const float corr = fast_exp2(m_run - m_new);
-    f4 pr;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(s[r] - m_new);
-    l_run = l_run * corr + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-#pragma unroll
-    for (int u = 0; u < TD; ++u) o[u] *= corr;
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int u = 0; u < TD; ++u) o[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(va[m][u], pr[m], o[u], 0, 0, 0);
-    m_run = m_new;
+    if (blk + 1 < n_blk) stage(buf ^ 1u);
+    __syncthreads();
   }
 
+  if (tile >= n_tiles) return;
   // the row's sum over its four lane groups, the sink, and the output
   float L = l_run + __shfl_xor(l_run, 16);
   L += __shfl_xor(L, 32);
@@ -210,7 +282,7 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) prefill_attn_kernel(const 
   }
   if (!row_ok) return;
   const float rs = sa / L;
-  float* dst = p.out + (static_cast<size_t>(t) * p.n_heads + h) * D + DQ * g;
+  float* dst = p.out + (static_cast<size_t>(row0 + t) * p.n_heads + h) * D + DQ * g;
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -220,27 +292,24 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) prefill_attn_kernel(const 
 }
 
 template <int D, int G>
-hipError_t launch_attn(const PrefillParams& p, hipStream_t s) {
-  const uint32_t waves = p.n_tiles * p.n_kv_heads;
-  const uint32_t blocks = (waves + kAttnWaves - 1) / kAttnWaves;
-  hipLaunchKernelGGL((prefill_attn_kernel<D, G>), dim3(blocks), dim3(kWave * kAttnWaves), 0, s, p);
+hipError_t launch_attn(const PrefillArgs& a, hipStream_t s) {
+  const uint32_t blocks = a.p.n_groups * a.p.n_kv_heads;
+  hipLaunchKernelGGL((prefill_attn_kernel<D, G>), dim3(blocks), dim3(kWave * kAttnWaves), 0, s, a);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(const PrefillParams& p, uint32_t G, hipStream_t s, hipEvent_t before,
+hipError_t launch_d(const PrefillArgs& a, uint32_t G, hipStream_t s, hipEvent_t before,
                     hipEvent_t after) {
-  const uint32_t vecs = p.T * (p.n_heads + p.n_kv_heads);
-  hipLaunchKernelGGL((prefill_prep_kernel<D>), dim3((vecs + kPrepWaves - 1) / kPrepWaves),
-                     dim3(kWave * kPrepWaves), 0, s, p);
+  hipLaunchKernelGGL((prefill_prep_kernel<D>), dim3(a.p.n_rows), dim3(kWave * kPrepWaves), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && before) e = hipEventRecord(before, s);
   if (e != hipSuccess) return e;
   switch (G) {
-    case 1: e = launch_attn<D, 1>(p, s); break;
-    case 2: e = launch_attn<D, 2>(p, s); break;
-    case 4: e = launch_attn<D, 4>(p, s); break;
-    case 8: e = launch_attn<D, 8>(p, s); break;
+    case 1: e = launch_attn<D, 1>(a, s); break;
+    case 2: e = launch_attn<D, 2>(a, s); break;
+    case 4: e = launch_attn<D, 4>(a, s); break;
+    case 8: e = launch_attn<D, 8>(a, s); break;
     default: return hipErrorInvalidValue;
   }
   if (e == hipSuccess && after) e = hipEventRecord(after, s);
@@ -249,15 +318,15 @@ hipError_t launch_d(const PrefillParams& p, uint32_t G, hipStream_t s, hipEvent_
 
 }  // namespace
 
-int launch_prefill(const PrefillParams& p, uint32_t head_dim, uint32_t group, void* stream,
+int launch_prefill(const PrefillArgs& a, uint32_t head_dim, uint32_t group, void* stream,
                    void* before_attn, void* after_attn) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t b = static_cast<hipEvent_t>(before_attn);
-  hipEvent_t a = static_cast<hipEvent_t>(after_attn);
+  hipEvent_t e = static_cast<hipEvent_t>(after_attn);
   switch (head_dim) {
-    case 64: return launch_d<64>(p, group, s, b, a);
-    case 128: return launch_d<128>(p, group, s, b, a);
-    case 256: return launch_d<256>(p, group, s, b, a);
+    case 64: return launch_d<64>(a, group, s, b, e);
+    case 128: return launch_d<128>(a, group, s, b, e);
+    case 256: return launch_d<256>(a, group, s, b, e);
     default: return hipErrorInvalidValue;
   }
 }

@@ -261,3 +261,55 @@ def prefill_chunk() -> PrefillWorkload:
 
 PREFILL_WORKLOADS = {"prefill_tiny": prefill_tiny, "prefill_prompt": prefill_prompt,
                      "prefill_chunk": prefill_chunk}
+
+
+# ---------------------------------------------------------------- multi-row verify
+@dataclasses.dataclass
+class VerifyWorkload:
+    """ks[i] consecutive rows for each sequence i, at positions pos0[i] ..
+    of slot slots[i] (rows sequence-major in ``inputs``)."""
+    name: str
+    seed: int
+    n_slots: int
+    slot_ctx: int
+    slots: np.ndarray  # [n_seq] u32
+    pos0: np.ndarray   # [n_seq] u32
+    ks: np.ndarray     # [n_seq] u32
+    layer: LayerParams
+    inputs: LayerInputs  # [sum ks] rows
+    theta: float
+
+    @property
+    def rows(self) -> int:
+        return int(self.ks.astype(np.int64).sum())
+
+    def kv_bytes(self) -> int:
+        """K and V bytes of the keys the rows attend over, each key once per
+        sequence: sum_i (pos0_i + ks_i) * kv_dim * 4 * 2."""
+        keys = int((self.pos0.astype(np.int64) + self.ks).sum())
+        return keys * self.layer.kv_dim * 4 * 2
+
+
+def _build_verify(name, seed, n_slots, slot_ctx, n_seq, k, shape, theta, sinks):
+    """Recipe: slots = a permutation of range(n_slots) cut to n_seq; pos0 ~
+    U{1 .. slot_ctx - k}; every sequence has k rows; then q / k_new / v_new
+    [n_seq*k, ...] ~ N(0, 1) and the layer's tables as above."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    slots = rng.permutation(n_slots)[:n_seq].astype(np.uint32)
+    pos0 = rng.integers(1, slot_ctx - k + 1, size=n_seq).astype(np.uint32)
+    ks = np.full(n_seq, k, np.uint32)
+    H, Hkv, D = shape
+    li = _layer_inputs(rng, n_seq * k, H, Hkv, D)
+    L = make_layer(rng, H, Hkv, D, theta, sinks)
+    return VerifyWorkload(name=name, seed=seed, n_slots=n_slots, slot_ctx=slot_ctx, slots=slots,
+                          pos0=pos0, ks=ks, layer=L, inputs=li, theta=theta)
+
+
+def verify_mid() -> VerifyWorkload:
+    """4 rows (a draft to verify) for each of 64 sequences, one per slot of a
+    64-slot x 4096 cache, at pos0 U{1..4092}; the decode workload's layer
+    shape (32 heads / 8 kv heads / D=128)."""
+    return _build_verify("verify_mid", 14, 64, 4096, 64, 4, (32, 8, 128), 1e6, False)
+
+
+VERIFY_WORKLOADS = {"verify_mid": verify_mid}
