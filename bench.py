@@ -29,6 +29,12 @@ kernel and the causal attention kernel on the matrix cores):
                mean kernel time from the library's HIP events) vs the
                157.3 TFLOP/s dense f32 MFMA peak
   cpu_baseline the CPU oracle's prefill over the first tokens of the prompt
+
+With --workload verify_mid it measures the multi-row verify (one
+slot_verify_attn call per step: 4 rows for each of 64 sequences):
+  value        rows/s
+  roofline     KV bytes (each sequence's keys 0..pos0+k-1, K and V, once) /
+               mean attention-kernel time vs 8 TB/s
 """
 from __future__ import annotations
 
@@ -47,6 +53,7 @@ METRIC = "decode-attn rows/sec and achieved KV HBM GB/s (% of peak) at B=64, ctx
 HBM_PEAK_GBPS = 8000.0
 MFMA_F32_PEAK_TFLOPS = 157.3
 PREFILL_METRIC = "slot prefill tokens/s and attention TFLOP/s (f32 matrix cores)"
+VERIFY_METRIC = "multi-row verify rows/s and achieved KV HBM GB/s (% of peak)"
 KERNEL_SRC = os.path.join(ROOT, "sequence_slot_kv_amd", "csrc", "slot_kv_kernels.hip")
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
@@ -106,7 +113,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mid",
                     choices=["tiny", "mid", "long", "many", "layer_stack", "prefill_prompt",
-                             "prefill_chunk"])
+                             "prefill_chunk", "verify_mid"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the reference "
@@ -135,6 +142,8 @@ def main():
         return
     if args.workload.startswith("prefill"):
         return prefill_bench(args, wl.PREFILL_WORKLOADS[args.workload](), b)
+    if args.workload.startswith("verify"):
+        return verify_bench(args, wl.VERIFY_WORKLOADS[args.workload](), b)
     w = wl.WORKLOADS[args.workload]()
     n_layers = len(w.layers)
     log(f"[bench] workload {w.name}: B={w.B} n_slots={w.n_slots} slot_ctx={w.slot_ctx} "
@@ -314,6 +323,91 @@ def prefill_bench(args, w, b):
         "attn_flops_per_step": w.attn_flops(),
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_F32_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": tflops / MFMA_F32_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "prefill_attn_kernel", "kernel_us": attn_us},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    kv.close()
+
+
+def verify_bench(args, w, b):
+    import numpy as np
+    import torch
+    L, li = w.layer, w.inputs
+    log(f"[bench] verify {w.name}: {len(w.ks)} sequences x {int(w.ks[0])} rows, heads "
+        f"{L.n_heads}/{L.n_kv_heads}/{L.head_dim}, KV bytes per step {w.kv_bytes()}")
+    kv = b.SlotKV()
+    kv.alloc(w.n_slots, w.slot_ctx, [L.kv_dim])
+    kv.set_layer(0, L)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(99)
+    hist = {}
+    for s, p0 in zip(w.slots.tolist(), w.pos0.tolist()):
+        hk = torch.randn((p0, L.kv_dim), generator=g, device="cuda")
+        hv = torch.randn((p0, L.kv_dim), generator=g, device="cuda")
+        kv.write_rows(0, s, 0, hk, hv)
+        if not args.no_cpu_baseline:
+            hist[s] = (hk.cpu().numpy(), hv.cpu().numpy())
+    q, kn, vn = (torch.from_numpy(x).cuda() for x in (li.q, li.k_new, li.v_new))
+    out = torch.empty_like(q)
+
+    def step():
+        kv.verify_attn(0, q, kn, vn, w.slots, w.pos0, w.ks, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    rc = b.slot_kv_profile_begin(kv.h)
+    assert rc == 0
+    for _ in range(args.steps):
+        step()
+    rc, attn_ms, launches = b.slot_kv_profile_end(kv.h)
+    torch.cuda.synchronize()
+    assert rc == 0 and launches == args.steps
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    attn_us = attn_ms / launches * 1e3
+    achieved = w.kv_bytes() / (attn_us * 1e-6) / 1e9
+    log(f"[bench] {ms_per_step * 1e3:.1f} us/step, attention kernel {attn_us:.1f} us, "
+        f"{achieved:.0f} GB/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        # whole sequences, in order, until ~10 s of one thread
+        c0, done, n_seq = time.perf_counter(), 0, 0
+        row_off = [0] + np.cumsum(w.ks.astype(np.int64)).tolist()
+        for i in range(len(w.ks)):
+            s, p0, k = int(w.slots[i]), int(w.pos0[i]), int(w.ks[i])
+            ck = np.zeros((1, p0 + k, L.kv_dim), np.float32)
+            cv = np.zeros_like(ck)
+            ck[0, :p0], cv[0, :p0] = hist[s]
+            r0 = row_off[i]
+            rc, _ = oracle.prefill(L, ck, cv, li.q[r0:r0 + k], li.k_new[r0:r0 + k],
+                                   li.v_new[r0:r0 + k], 0, p0)
+            assert rc == 0
+            done += k
+            n_seq += 1
+            if time.perf_counter() - c0 >= 10.0:
+                break
+        dt = time.perf_counter() - c0
+        cpu = {"value": done / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+               "sample": f"the first {n_seq} sequences ({done} rows) in order, {dt:.1f} s on "
+                         f"one thread"}
+    res = {
+        "metric": VERIFY_METRIC, "value": w.rows / (ms_per_step / 1e3), "unit": "rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "n_seq": len(w.ks), "rows_per_seq": int(w.ks[0]),
+                   "n_slots": w.n_slots, "slot_ctx": w.slot_ctx, "n_heads": L.n_heads,
+                   "n_kv_heads": L.n_kv_heads, "head_dim": L.head_dim, "seed": w.seed},
+        "kv_bytes_per_step": w.kv_bytes(),
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
                      "kernel": "prefill_attn_kernel", "kernel_us": attn_us},
         "cpu_baseline": cpu,
     }
