@@ -60,22 +60,28 @@ def _load():
         lib.oracle_rope.restype = None
         lib.oracle_decode_row.argtypes = [
             u32, u32, u32, f32p, f32p, f32p, f32p, ctypes.c_float, ctypes.c_float,
-            u32, f32p, f32p, f32p, f32p, f32p, u64, f32p, f32p, f32p]
+            u32, f32p, f32p, f32p, f32p, f32p, u64, f32p, f32p, f32p, u32]
         lib.oracle_decode_row.restype = ctypes.c_int
         lib.oracle_check_batch.argtypes = [u32, u32, u32p, u32p, u32]
         lib.oracle_check_batch.restype = ctypes.c_int
         lib.oracle_decode_batch.argtypes = [
             u32, u32, u32, f32p, f32p, f32p, f32p, ctypes.c_float, ctypes.c_float,
-            f32p, f32p, u32, u32, f32p, f32p, f32p, u32p, u32p, u32, f32p]
+            f32p, f32p, u32, u32, f32p, f32p, f32p, u32p, u32p, u32, f32p, u32]
         lib.oracle_decode_batch.restype = ctypes.c_int
         lib.oracle_prefill.argtypes = [
             u32, u32, u32, f32p, f32p, f32p, f32p, ctypes.c_float, ctypes.c_float,
-            f32p, f32p, u32, u32, f32p, f32p, f32p, u32, u32, u32, f32p]
+            f32p, f32p, u32, u32, f32p, f32p, f32p, u32, u32, u32, f32p, u32]
         lib.oracle_prefill.restype = ctypes.c_int
         lib.oracle_verify.argtypes = [
             u32, u32, u32, f32p, f32p, f32p, f32p, ctypes.c_float, ctypes.c_float,
-            f32p, f32p, u32, u32, f32p, f32p, f32p, u32p, u32p, u32p, u32, f32p]
+            f32p, f32p, u32, u32, f32p, f32p, f32p, u32p, u32p, u32p, u32, f32p, u32]
         lib.oracle_verify.restype = ctypes.c_int
+        lib.oracle_rms_norm_1pw.argtypes = [f32p, f32p, u32, ctypes.c_double, f64p]
+        lib.oracle_rms_norm_1pw.restype = None
+        lib.oracle_rms_norm_plain.argtypes = [f32p, u32, ctypes.c_double, f64p]
+        lib.oracle_rms_norm_plain.restype = None
+        lib.oracle_rope_interleaved.argtypes = [f64p, f32p, u32, u32]
+        lib.oracle_rope_interleaved.restype = None
         _lib = lib
     return _lib
 
@@ -96,6 +102,14 @@ def _opt_f32(a, name):
     return None if a is None else _f32(a, name)
 
 
+# Convention flags of a layer (LayerParams.flags): see slot_kv_oracle.c.
+V_NORM, ROPE_INTERLEAVED, NORM_ONE_PLUS_W = 1, 2, 4
+
+
+def _flags(layer) -> int:
+    return int(getattr(layer, "flags", 0))
+
+
 def slot_kv_offset_bytes(slot: int, pos: int, slot_ctx: int, kv_dim: int) -> int:
     """(slot * slot_ctx + pos) * kv_dim * 4, in 64-bit arithmetic."""
     return int(_load().oracle_slot_kv_offset_bytes(slot, pos, slot_ctx, kv_dim))
@@ -108,6 +122,34 @@ def rms_norm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
     y = np.empty(x.shape[0], np.float64)
     _load().oracle_rms_norm(_f32(x, "x"), _f32(w, "w"), x.shape[0], float(eps),
                             y.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    return y
+
+
+def rms_norm_1pw(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm with (1 + w) weights, float64."""
+    x = np.ascontiguousarray(x, np.float32)
+    w = np.ascontiguousarray(w, np.float32)
+    y = np.empty(x.shape[0], np.float64)
+    _load().oracle_rms_norm_1pw(_f32(x, "x"), _f32(w, "w"), x.shape[0], float(eps),
+                                y.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    return y
+
+
+def rms_norm_plain(x: np.ndarray, eps: float) -> np.ndarray:
+    """Weightless RMSNorm, float64."""
+    x = np.ascontiguousarray(x, np.float32)
+    y = np.empty(x.shape[0], np.float64)
+    _load().oracle_rms_norm_plain(_f32(x, "x"), x.shape[0], float(eps),
+                                  y.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    return y
+
+
+def rope_interleaved(x: np.ndarray, inv_freq: np.ndarray, pos: int) -> np.ndarray:
+    """Interleaved-pair RoPE of one float64 head vector at position ``pos``."""
+    y = np.array(x, dtype=np.float64, copy=True)
+    inv_freq = np.ascontiguousarray(inv_freq, np.float32)
+    _load().oracle_rope_interleaved(y.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                    _f32(inv_freq, "inv_freq"), pos, y.shape[0])
     return y
 
 
@@ -146,7 +188,7 @@ def decode_row(layer, pos, q_row, k_new_row, v_new_row, hist_k, hist_v):
         _f32(np.ascontiguousarray(q_row, np.float32), "q"),
         _f32(np.ascontiguousarray(k_new_row, np.float32), "k_new"),
         _f32(np.ascontiguousarray(v_new_row, np.float32), "v_new"),
-        hk, hv, stride, _f32(k_w, "k_w"), _f32(v_w, "v_w"), _f32(out, "out"))
+        hk, hv, stride, _f32(k_w, "k_w"), _f32(v_w, "v_w"), _f32(out, "out"), _flags(layer))
     if rc != OK:
         raise ValueError(f"oracle_decode_row failed: {rc}")
     return k_w, v_w, out
@@ -179,7 +221,7 @@ def decode_batch(layer, cache_k, cache_v, q, k_new, v_new, positions, slots):
         _f32(np.ascontiguousarray(q, np.float32), "q"),
         _f32(np.ascontiguousarray(k_new, np.float32), "k_new"),
         _f32(np.ascontiguousarray(v_new, np.float32), "v_new"),
-        _u32(positions, "positions"), _u32(slots, "slots"), B, _f32(out, "out"))
+        _u32(positions, "positions"), _u32(slots, "slots"), B, _f32(out, "out"), _flags(L))
     return rc, out
 
 
@@ -201,7 +243,8 @@ def prefill(layer, cache_k, cache_v, q, k_new, v_new, slot, pos0):
         _opt_f32(L.sinks, "sinks"), float(L.eps), float(L.scale),
         _f32(cache_k, "cache_k"), _f32(cache_v, "cache_v"), n_slots, slot_ctx,
         _f32(q, "q"), _f32(np.ascontiguousarray(k_new, np.float32), "k_new"),
-        _f32(np.ascontiguousarray(v_new, np.float32), "v_new"), slot, pos0, T, _f32(out, "out"))
+        _f32(np.ascontiguousarray(v_new, np.float32), "v_new"), slot, pos0, T, _f32(out, "out"),
+        _flags(L))
     return rc, out
 
 
@@ -228,5 +271,6 @@ def verify(layer, cache_k, cache_v, q, k_new, v_new, slots, pos0, ks):
         _opt_f32(L.sinks, "sinks"), float(L.eps), float(L.scale),
         _f32(cache_k, "cache_k"), _f32(cache_v, "cache_v"), n_slots, slot_ctx,
         _f32(q, "q"), _f32(k_new, "k_new"), _f32(v_new, "v_new"),
-        _u32(slots, "slots"), _u32(pos0, "pos0"), _u32(ks, "ks"), slots.shape[0], _f32(out, "out"))
+        _u32(slots, "slots"), _u32(pos0, "pos0"), _u32(ks, "ks"), slots.shape[0], _f32(out, "out"),
+        _flags(L))
     return rc, out[:rows]

@@ -41,6 +41,16 @@
 #define ORACLE_ERANGE (-2)
 #define ORACLE_EDUP (-5)
 
+/* Convention flags (the pages' "per-head V/Q/K norm" and the variants a model
+ * may use; default 0 = the conventions described above):
+ *   V_NORM            weightless RMSNorm of each value head before it is
+ *                     written (the "V" of "per-head V/Q/K norm");
+ *   ROPE_INTERLEAVED  RoPE pairs (x[2i], x[2i+1]) instead of (x[i], x[i+D/2]);
+ *   NORM_ONE_PLUS_W   the Q and K norms multiply by (1 + w) instead of w. */
+#define ORACLE_V_NORM 1u
+#define ORACLE_ROPE_INTERLEAVED 2u
+#define ORACLE_NORM_ONE_PLUS_W 4u
+
 /* [FG] slotKvOffsetBytes; [FC] slot K/V byte offset:
  * byte offset of (slot, pos) in one layer's slot KV buffer,
  * (slot * slot_ctx + pos) * kv_dim * sizeof(f32), computed in 64 bits. */
@@ -76,6 +86,36 @@ void oracle_rope(double *x, const float *inv_freq, uint32_t pos, uint32_t D) {
     }
 }
 
+/* NORM_ONE_PLUS_W variant of oracle_rms_norm: y[i] = x[i] / sqrt(mean(x^2) +
+ * eps) * (1 + w[i]), all in double. */
+void oracle_rms_norm_1pw(const float *x, const float *w, uint32_t n, double eps, double *y) {
+    double ss = 0.0;
+    for (uint32_t i = 0; i < n; ++i) ss += (double)x[i] * (double)x[i];
+    double r = 1.0 / sqrt(ss / (double)n + eps);
+    for (uint32_t i = 0; i < n; ++i) y[i] = (double)x[i] * r * (1.0 + (double)w[i]);
+}
+
+/* V_NORM: the weightless RMSNorm y[i] = x[i] / sqrt(mean(x^2) + eps). */
+void oracle_rms_norm_plain(const float *x, uint32_t n, double eps, double *y) {
+    double ss = 0.0;
+    for (uint32_t i = 0; i < n; ++i) ss += (double)x[i] * (double)x[i];
+    double r = 1.0 / sqrt(ss / (double)n + eps);
+    for (uint32_t i = 0; i < n; ++i) y[i] = (double)x[i] * r;
+}
+
+/* ROPE_INTERLEAVED: the pair (x[2i], x[2i+1]) is rotated by
+ * theta_i = float32(float(pos) * inv_freq[i]), for i < D/2. */
+void oracle_rope_interleaved(double *x, const float *inv_freq, uint32_t pos, uint32_t D) {
+    for (uint32_t i = 0; i < D / 2; ++i) {
+        volatile float ang_f = (float)pos * inv_freq[i]; /* one f32 multiply */
+        double th = (double)ang_f;
+        double c = cos(th), s = sin(th);
+        double a = x[2 * i], b = x[2 * i + 1];
+        x[2 * i] = a * c - b * s;
+        x[2 * i + 1] = b * c + a * s;
+    }
+}
+
 /* [FG] decodeBatch: the whole step for one row b.
  *
  *   q_row      [n_heads * head_dim]      this row's query
@@ -87,6 +127,7 @@ void oracle_rope(double *x, const float *inv_freq, uint32_t pos, uint32_t D) {
  *   v_written  [kv_dim]  the V row this step stores at (slot, pos)
  *   out_row    [n_heads * head_dim]      attention output
  *   sinks      [n_heads] or NULL
+ *   flags      ORACLE_V_NORM | ORACLE_ROPE_INTERLEAVED | ORACLE_NORM_ONE_PLUS_W
  *
  * Returns ORACLE_OK, or ORACLE_EINVAL for an inconsistent head shape. */
 int oracle_decode_row(uint32_t n_heads, uint32_t n_kv_heads, uint32_t head_dim,
@@ -97,7 +138,8 @@ int oracle_decode_row(uint32_t n_heads, uint32_t n_kv_heads, uint32_t head_dim,
                       const float *v_new_row,
                       const float *hist_k, const float *hist_v,
                       uint64_t hist_stride,
-                      float *k_written, float *v_written, float *out_row) {
+                      float *k_written, float *v_written, float *out_row,
+                      uint32_t flags) {
     if (n_heads == 0 || n_kv_heads == 0 || head_dim == 0 || head_dim % 2 != 0 ||
         n_heads % n_kv_heads != 0)
         return ORACLE_EINVAL;
@@ -115,20 +157,37 @@ int oracle_decode_row(uint32_t n_heads, uint32_t n_kv_heads, uint32_t head_dim,
         return ORACLE_EINVAL;
     }
 
-    /* New K row: norm, then RoPE at pos, rounded once to f32.  V verbatim. */
+    /* New K row: norm, then RoPE at pos, rounded once to f32.  V verbatim
+     * (or, with V_NORM, its weightless RMSNorm rounded once to f32). */
     for (uint32_t j = 0; j < n_kv_heads; ++j) {
-        oracle_rms_norm(k_new_row + (size_t)j * D, k_norm_w, D, (double)eps, tmp);
-        oracle_rope(tmp, inv_freq, pos, D);
+        if (flags & ORACLE_NORM_ONE_PLUS_W)
+            oracle_rms_norm_1pw(k_new_row + (size_t)j * D, k_norm_w, D, (double)eps, tmp);
+        else
+            oracle_rms_norm(k_new_row + (size_t)j * D, k_norm_w, D, (double)eps, tmp);
+        if (flags & ORACLE_ROPE_INTERLEAVED)
+            oracle_rope_interleaved(tmp, inv_freq, pos, D);
+        else
+            oracle_rope(tmp, inv_freq, pos, D);
         for (uint32_t d = 0; d < D; ++d) {
             k_written[(size_t)j * D + d] = (float)tmp[d];
             v_written[(size_t)j * D + d] = v_new_row[(size_t)j * D + d];
+        }
+        if (flags & ORACLE_V_NORM) {
+            oracle_rms_norm_plain(v_new_row + (size_t)j * D, D, (double)eps, tmp);
+            for (uint32_t d = 0; d < D; ++d) v_written[(size_t)j * D + d] = (float)tmp[d];
         }
     }
 
     for (uint32_t h = 0; h < n_heads; ++h) {
         const uint32_t j = h / G;
-        oracle_rms_norm(q_row + (size_t)h * D, q_norm_w, D, (double)eps, qh);
-        oracle_rope(qh, inv_freq, pos, D);
+        if (flags & ORACLE_NORM_ONE_PLUS_W)
+            oracle_rms_norm_1pw(q_row + (size_t)h * D, q_norm_w, D, (double)eps, qh);
+        else
+            oracle_rms_norm(q_row + (size_t)h * D, q_norm_w, D, (double)eps, qh);
+        if (flags & ORACLE_ROPE_INTERLEAVED)
+            oracle_rope_interleaved(qh, inv_freq, pos, D);
+        else
+            oracle_rope(qh, inv_freq, pos, D);
 
         /* scores over keys 0..pos; key pos is the row written above */
         double m = -INFINITY;
@@ -188,7 +247,7 @@ int oracle_decode_batch(uint32_t n_heads, uint32_t n_kv_heads, uint32_t head_dim
                         uint32_t n_slots, uint32_t slot_ctx,
                         const float *q, const float *k_new, const float *v_new,
                         const uint32_t *positions, const uint32_t *slots,
-                        uint32_t B, float *out) {
+                        uint32_t B, float *out, uint32_t flags) {
     if (n_kv_heads == 0 || head_dim == 0) return ORACLE_EINVAL;
     const uint32_t kv_dim = n_kv_heads * head_dim;
     const size_t qd = (size_t)n_heads * head_dim;
@@ -203,7 +262,7 @@ int oracle_decode_batch(uint32_t n_heads, uint32_t n_kv_heads, uint32_t head_dim
                                q + (size_t)b * qd, k_new + (size_t)b * kv_dim,
                                v_new + (size_t)b * kv_dim,
                                cache_k + base, cache_v + base, kv_dim,
-                               cache_k + at, cache_v + at, out + (size_t)b * qd);
+                               cache_k + at, cache_v + at, out + (size_t)b * qd, flags);
         if (rc != ORACLE_OK) return rc;
     }
     return ORACLE_OK;
@@ -224,7 +283,7 @@ int oracle_prefill(uint32_t n_heads, uint32_t n_kv_heads, uint32_t head_dim,
                    float *cache_k, float *cache_v,
                    uint32_t n_slots, uint32_t slot_ctx,
                    const float *q, const float *k_new, const float *v_new,
-                   uint32_t slot, uint32_t pos0, uint32_t T, float *out) {
+                   uint32_t slot, uint32_t pos0, uint32_t T, float *out, uint32_t flags) {
     if (n_kv_heads == 0 || head_dim == 0) return ORACLE_EINVAL;
     if (slot >= n_slots || pos0 >= slot_ctx || T > slot_ctx - pos0) return ORACLE_ERANGE;
     const uint32_t kv_dim = n_kv_heads * head_dim;
@@ -235,7 +294,7 @@ int oracle_prefill(uint32_t n_heads, uint32_t n_kv_heads, uint32_t head_dim,
                                      inv_freq, sinks, eps, scale, cache_k, cache_v,
                                      n_slots, slot_ctx, q + (size_t)t * qd,
                                      k_new + (size_t)t * kv_dim, v_new + (size_t)t * kv_dim,
-                                     &p, &slot, 1, out + (size_t)t * qd);
+                                     &p, &slot, 1, out + (size_t)t * qd, flags);
         if (rc != ORACLE_OK) return rc;
     }
     return ORACLE_OK;
@@ -255,7 +314,7 @@ int oracle_verify(uint32_t n_heads, uint32_t n_kv_heads, uint32_t head_dim,
                   uint32_t n_slots, uint32_t slot_ctx,
                   const float *q, const float *k_new, const float *v_new,
                   const uint32_t *slots, const uint32_t *pos0, const uint32_t *ks,
-                  uint32_t n_seq, float *out) {
+                  uint32_t n_seq, float *out, uint32_t flags) {
     if (n_kv_heads == 0 || head_dim == 0) return ORACLE_EINVAL;
     for (uint32_t i = 0; i < n_seq; ++i) {
         if (slots[i] >= n_slots || pos0[i] >= slot_ctx || ks[i] > slot_ctx - pos0[i])
@@ -272,7 +331,7 @@ int oracle_verify(uint32_t n_heads, uint32_t n_kv_heads, uint32_t head_dim,
                                     inv_freq, sinks, eps, scale, cache_k, cache_v,
                                     n_slots, slot_ctx, q + row * qd, k_new + row * kv_dim,
                                     v_new + row * kv_dim, slots[i], pos0[i], ks[i],
-                                    out + row * qd);
+                                    out + row * qd, flags);
             if (rc != ORACLE_OK) return rc;
         }
         row += ks[i];

@@ -42,6 +42,7 @@ class LayerParams:
     sinks: Optional[np.ndarray]  # [n_heads] f32 or None
     eps: float
     scale: float
+    flags: int = 0  # convention flags: 1 V-norm, 2 interleaved RoPE, 4 (1 + w) norm weights
 
     @property
     def kv_dim(self) -> int:

@@ -44,8 +44,17 @@ MUTANTS = {
     "verify_dup_allowed": ("if (slots[c] == slots[i]) return ORACLE_EDUP;", "continue;"),
     "verify_rows_not_advanced": ("        row += ks[i];\n", "        row += (ks[i] > 0);\n"),
     "verify_range_off_by_one": ("ks[i] > slot_ctx - pos0[i]", "ks[i] > slot_ctx - pos0[i] + 1"),
+    # convention flags
+    "interleaved_minus_theta": ("x[2 * i] = a * c - b * s;", "x[2 * i] = a * c + b * s;"),
+    "interleaved_angle_index": ("double a = x[2 * i], b = x[2 * i + 1];",
+                                "double a = x[2 * i], b = x[2 * i + 1]; th = th * 2.0; c = cos(th); s = sin(th);"),
+    "one_plus_w_dropped": ("y[i] = (double)x[i] * r * (1.0 + (double)w[i]);",
+                           "y[i] = (double)x[i] * r * (double)w[i];"),
+    "vnorm_skipped": ("if (flags & ORACLE_V_NORM) {", "if (0) {"),
+    "interleaved_not_on_queries": ("if (flags & ORACLE_ROPE_INTERLEAVED)\n            oracle_rope_interleaved(qh",
+                                   "if (0)\n            oracle_rope_interleaved(qh"),
 }
-PIN_FILES = ["test_oracle_pins.py", "test_oracle_prefill_pins.py"]
+PIN_FILES = ["test_oracle_pins.py", "test_oracle_prefill_pins.py", "test_oracle_conventions.py"]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
