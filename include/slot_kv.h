@@ -72,13 +72,33 @@ int slot_kv_alloc(slot_kv *h, uint32_t n_slots, uint32_t slot_ctx,
  * (RMSNorm weights shared by all query heads, resp. all key heads),
  * inv_freq[head_dim/2] (RoPE frequencies), sinks[n_heads] (one extra softmax
  * logit per query head; NULL for none).  eps is the RMSNorm epsilon and
- * scale multiplies q.k (not the sink).
+ * scale multiplies q.k (not the sink).  The layer's convention flags are
+ * reset to 0 (see slot_kv_set_layer_flags).
  * Errors: ENOTALLOC, EINVAL, EDEVICE. */
 int slot_kv_set_layer(slot_kv *h, uint32_t layer, uint32_t n_heads,
                       uint32_t n_kv_heads, uint32_t head_dim,
                       const float *q_norm_w, const float *k_norm_w,
                       const float *inv_freq, const float *sinks, float eps,
                       float scale);
+
+/* Convention flags of a layer ("Forward Cuda Gemma", decodeBatch: "per-head
+ * V/Q/K norm"; variants a model may use).  Default 0:
+ *   SLOT_KV_FLAG_V_NORM            each value head is replaced by its
+ *                                  weightless RMSNorm, v / sqrt(mean(v^2) +
+ *                                  eps), before it is written and attended;
+ *   SLOT_KV_FLAG_ROPE_INTERLEAVED  RoPE rotates the pairs (x[2i], x[2i+1]) by
+ *                                  angle float(pos)*inv_freq[i] instead of the
+ *                                  pairs (x[i], x[i + head_dim/2]);
+ *   SLOT_KV_FLAG_NORM_ONE_PLUS_W   the query and key norms multiply by
+ *                                  (1 + w) instead of w. */
+#define SLOT_KV_FLAG_V_NORM 1u
+#define SLOT_KV_FLAG_ROPE_INTERLEAVED 2u
+#define SLOT_KV_FLAG_NORM_ONE_PLUS_W 4u
+
+/* Sets the convention flags of configured layer `layer` for every later call
+ * (slot_kv_set_layer resets them to 0).  Errors: ENOTALLOC, EINVAL (layer
+ * unconfigured, unknown flag bits). */
+int slot_kv_set_layer_flags(slot_kv *h, uint32_t layer, uint32_t flags);
 
 /* "Forward Cuda Gemma", slotKvOffsetBytes; "Forward Cuda", slot K/V offset.
  * *out_bytes = (slot * slot_ctx + pos) * kv_dims[layer] * 4, in 64 bits: the

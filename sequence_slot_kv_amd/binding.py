@@ -18,6 +18,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libslot_kv.so")
 
 SLOT_KV_OK = 0
+SLOT_KV_FLAG_V_NORM, SLOT_KV_FLAG_ROPE_INTERLEAVED, SLOT_KV_FLAG_NORM_ONE_PLUS_W = 1, 2, 4
 SLOT_KV_EINVAL = -1
 SLOT_KV_ERANGE = -2
 SLOT_KV_ENOTALLOC = -3
@@ -27,7 +28,8 @@ SLOT_KV_EDEVICE = -6
 
 # Every symbol include/slot_kv.h declares.
 EXPORTS = ("slot_kv_create", "slot_kv_destroy", "slot_kv_alloc", "slot_kv_set_layer",
-           "slot_kv_offset_bytes", "slot_reset", "slot_decode_attn", "slot_prefill_attn",
+           "slot_kv_set_layer_flags", "slot_kv_offset_bytes", "slot_reset", "slot_decode_attn",
+           "slot_prefill_attn",
            "slot_verify_attn",
            "slot_kv_layer_ptrs",
            "slot_kv_write_rows", "slot_kv_read_rows", "slot_kv_check_batch",
@@ -58,6 +60,7 @@ _lib.slot_kv_set_layer.argtypes = [_vp, _u32, _u32, _u32, _u32, _f32p, _f32p, _f
                                    ctypes.c_float, ctypes.c_float]
 _lib.slot_kv_offset_bytes.argtypes = [_vp, _u32, _u32, _u32, ctypes.POINTER(ctypes.c_uint64)]
 _lib.slot_reset.argtypes = [_vp, _u32]
+_lib.slot_kv_set_layer_flags.argtypes = [_vp, _u32, _u32]
 _lib.slot_decode_attn.argtypes = [_vp, _u32, _vp, _vp, _vp, _u32p, _u32p, _u32, _vp, _vp]
 _lib.slot_prefill_attn.argtypes = [_vp, _u32, _vp, _vp, _vp, _u32, _u32, _u32, _vp, _vp]
 _lib.slot_verify_attn.argtypes = [_vp, _u32, _vp, _vp, _vp, _u32p, _u32p, _u32p, _u32, _vp, _vp]
@@ -206,6 +209,10 @@ def slot_verify_attn(h, layer, q, k_new, v_new, slots, pos0, ks, out, stream=Non
                                  _ptr_u32(k), int(sl.shape[0]), ptrs[3], _stream_handle(stream))
 
 
+def slot_kv_set_layer_flags(h, layer, flags) -> int:
+    return _lib.slot_kv_set_layer_flags(h, layer, flags)
+
+
 def slot_kv_layer_ptrs(h, layer):
     """Returns (status, k_ptr, v_ptr)."""
     k, v = _vp(), _vp()
@@ -293,6 +300,9 @@ class SlotKV:
         _check(slot_kv_set_layer(self.h, layer, P.n_heads, P.n_kv_heads, P.head_dim, P.q_norm_w,
                                  P.k_norm_w, P.inv_freq, P.sinks, P.eps, P.scale),
                "slot_kv_set_layer")
+        flags = int(getattr(P, "flags", 0))
+        if flags:
+            _check(slot_kv_set_layer_flags(self.h, layer, flags), "slot_kv_set_layer_flags")
         self.layers[layer] = P
 
     def offset_bytes(self, layer, slot, pos) -> int:

@@ -33,6 +33,7 @@ struct LayerState {
   float* params = nullptr;  // q_norm_w[D] | k_norm_w[D] | inv_freq[D/2] | sinks[n_heads]
   bool has_sinks = false;
   float eps = 0.f, scale = 0.f;
+  uint32_t flags = 0;  // SLOT_KV_FLAG_*
 };
 
 }  // namespace
@@ -251,7 +252,19 @@ int slot_kv_set_layer(slot_kv* h, uint32_t layer, uint32_t n_heads, uint32_t n_k
   L.has_sinks = sinks != nullptr;
   L.eps = eps;
   L.scale = scale;
+  L.flags = 0;
   L.configured = true;
+  return SLOT_KV_OK;
+}
+
+int slot_kv_set_layer_flags(slot_kv* h, uint32_t layer, uint32_t flags) {
+  int rc = check_layer(h, layer);
+  if (rc) return rc;
+  LayerState& L = h->layers[layer];
+  const uint32_t known =
+      SLOT_KV_FLAG_V_NORM | SLOT_KV_FLAG_ROPE_INTERLEAVED | SLOT_KV_FLAG_NORM_ONE_PLUS_W;
+  if (!L.configured || (flags & ~known)) return SLOT_KV_EINVAL;
+  L.flags = flags;
   return SLOT_KV_OK;
 }
 
@@ -346,6 +359,7 @@ int slot_decode_attn(slot_kv* h, uint32_t layer, const float* q, const float* k_
   p.chunk = C;
   p.eps = L.eps;
   p.qk_scale_log2 = L.scale * 1.4426950408889634f;
+  p.flags = L.flags;
   const size_t qd = static_cast<size_t>(L.n_heads) * D;
   for (uint32_t r0 = 0; r0 < B; r0 += R) {  // rows are independent: launch in slices
     const uint32_t n = std::min(B - r0, R);
@@ -415,6 +429,7 @@ int run_prefill(slot_kv* h, uint32_t layer, const float* q, const float* k_new,
   p.n_kv_heads = L.n_kv_heads;
   p.eps = L.eps;
   p.qk_scale_log2 = L.scale * 1.4426950408889634f;
+  p.flags = L.flags;
   const size_t qd = static_cast<size_t>(L.n_heads) * D;
   for (size_t s0 = 0; s0 < seqs.size(); s0 += M) {
     const uint32_t n = static_cast<uint32_t>(std::min<size_t>(seqs.size() - s0, M));

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "slot_kv.h"
+
 #ifndef SLOT_KV_CHUNK
 #define SLOT_KV_CHUNK 512  // keys per split-K chunk (a multiple of 64)
 #endif
@@ -54,6 +56,7 @@ struct AttnParams {
   uint32_t chunk;
   float eps;
   float qk_scale_log2;     // scale * log2(e)
+  uint32_t flags;          // SLOT_KV_FLAG_*
 };
 
 constexpr uint32_t kArgsMagic = 0x534c4b56u;  // last word of the kernel arguments
@@ -91,6 +94,7 @@ struct PrefillParams {
   uint32_t n_groups;       // attention workgroups per kv head (all sequences)
   float eps;
   float qk_scale_log2;     // scale * log2(e)
+  uint32_t flags;          // SLOT_KV_FLAG_*
 };
 
 struct PrefillSeqs {

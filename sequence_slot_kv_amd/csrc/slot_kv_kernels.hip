@@ -279,7 +279,10 @@ struct PrepRaw {
   float x[SLOTS][EPL];
   float vn[EPL];  // v_new of the row, for the wave that holds the new key
 };
-// The lane's norm weights and RoPE frequencies, the same for every unit.
+// The lane's norm weights (1 + w under SLOT_KV_FLAG_NORM_ONE_PLUS_W) and the
+// RoPE frequencies of its elements, the same for every unit.  Element d of a
+// head vector uses frequency d mod D/2 for rotate-half pairs and d / 2 for
+// interleaved pairs.
 template <int D>
 struct PrepConst {
   static constexpr int EPL = D / kWave;
@@ -287,12 +290,15 @@ struct PrepConst {
 };
 template <int D>
 __device__ __forceinline__ PrepConst<D> prep_const(const AttnParams& p, uint32_t lane) {
+  constexpr int EPL = PrepConst<D>::EPL;
+  const float one = (p.flags & SLOT_KV_FLAG_NORM_ONE_PLUS_W) ? 1.f : 0.f;
+  const bool inter = p.flags & SLOT_KV_FLAG_ROPE_INTERLEAVED;
   PrepConst<D> c;
 #pragma unroll
-  for (int e = 0; e < PrepConst<D>::EPL; ++e) {
-    c.wq[e] = p.q_norm_w[lane * PrepConst<D>::EPL + e];
-    c.wk[e] = p.k_norm_w[lane * PrepConst<D>::EPL + e];
-    c.freq[e] = p.inv_freq[(lane & 31) * PrepConst<D>::EPL + e];
+  for (int e = 0; e < EPL; ++e) {
+    c.wq[e] = one + p.q_norm_w[lane * EPL + e];
+    c.wk[e] = one + p.k_norm_w[lane * EPL + e];
+    c.freq[e] = p.inv_freq[inter ? (lane * EPL + e) / 2 : (lane & 31) * EPL + e];
   }
   return c;
 }
@@ -345,20 +351,35 @@ __device__ __forceinline__ void prep_finish(const AttnArgs& a, const UnitId& id,
     if (!prep_has<D, G>(a, id, v)) continue;  // wave-uniform
     // norm with weights wts, then RoPE at pos (two inlined copies, so that
     // each reads its weights straight from registers)
+    // RoPE partners: element d pairs with d +- D/2 (lane ^ 32, same slot) or,
+    // interleaved, with d ^ 1 (the neighbouring slot of the lane, or lane ^ 1
+    // when a lane holds one element).
+    const bool inter = p.flags & SLOT_KV_FLAG_ROPE_INTERLEAVED;  // uniform
     auto norm_rope = [&](const float (&wts)[R::EPL], float (&y)[R::EPL]) {
       float ss = 0.f;
 #pragma unroll
       for (int e = 0; e < R::EPL; ++e) ss += raw.x[s][e] * raw.x[s][e];
       ss = wave_sum(ss);
       const float rn = 1.0f / sqrtf(ss * (1.0f / D) + p.eps);
+      float xs[R::EPL];
+#pragma unroll
+      for (int e = 0; e < R::EPL; ++e) xs[e] = raw.x[s][e] * rn * wts[e];
 #pragma unroll
       for (int e = 0; e < R::EPL; ++e) {
-        const float x = raw.x[s][e] * rn * wts[e];
-        const float partner = __shfl_xor(x, 32);
+        float partner;
+        bool first;
+        if (inter) {
+          if constexpr (R::EPL >= 2) partner = xs[e ^ 1];
+          else partner = __shfl_xor(xs[e], 1);
+          first = ((lane * R::EPL + e) & 1u) == 0;
+        } else {
+          partner = __shfl_xor(xs[e], 32);
+          first = lane < 32;
+        }
         const float ang = fpos * pc.freq[e];  // one f32 multiply
         float sn, cs;
         sincosf(ang, &sn, &cs);
-        y[e] = lane < 32 ? x * cs - partner * sn : x * cs + partner * sn;
+        y[e] = first ? xs[e] * cs - partner * sn : xs[e] * cs + partner * sn;
       }
     };
     float y[R::EPL];
@@ -367,15 +388,27 @@ __device__ __forceinline__ void prep_finish(const AttnArgs& a, const UnitId& id,
 #pragma unroll
       for (int e = 0; e < R::EPL; ++e) prep.q[par][v][lane * R::EPL + e] = y[e] * p.qk_scale_log2;
     } else {
-      // the step's KV write: rotated key and v_new at (slot*slot_ctx + pos)*kv_dim
+      // the step's KV write: rotated key and v_new (or its weightless RMSNorm
+      // under SLOT_KV_FLAG_V_NORM) at (slot*slot_ctx + pos)*kv_dim
       const uint64_t at = static_cast<uint64_t>(a.rows.slot[id.b]) * p.slot_stride +
                           static_cast<uint64_t>(pos) * p.kv_dim + id.j * D + lane * R::EPL;
+      float vw[R::EPL];
+#pragma unroll
+      for (int e = 0; e < R::EPL; ++e) vw[e] = raw.vn[e];
+      if (p.flags & SLOT_KV_FLAG_V_NORM) {  // uniform
+        float sv = 0.f;
+#pragma unroll
+        for (int e = 0; e < R::EPL; ++e) sv += vw[e] * vw[e];
+        const float rv = 1.0f / sqrtf(wave_sum(sv) * (1.0f / D) + p.eps);
+#pragma unroll
+        for (int e = 0; e < R::EPL; ++e) vw[e] *= rv;
+      }
 #pragma unroll
       for (int e = 0; e < R::EPL; ++e) {
         prep.kn[par][lane * R::EPL + e] = y[e];
-        prep.vn[par][lane * R::EPL + e] = raw.vn[e];
+        prep.vn[par][lane * R::EPL + e] = vw[e];
         p.k_cache[at + e] = y[e];
-        p.v_cache[at + e] = raw.vn[e];
+        p.v_cache[at + e] = vw[e];
       }
     }
   }

@@ -54,7 +54,9 @@ __device__ __forceinline__ uint32_t seq_of_row(const PrefillArgs& a, uint32_t ro
 
 // One workgroup per token row.  Lane l of a wave holds elements
 // l*EPL .. l*EPL+EPL-1 of a head vector, so the RoPE partner d +- D/2 of an
-// element sits in lane l ^ 32 and both use angle (l & 31)*EPL + e.
+// element sits in lane l ^ 32 and both use angle (l & 31)*EPL + e; with
+// interleaved pairs the partner d ^ 1 is the neighbouring element of the lane
+// (lane l ^ 1 when a lane holds one) and the angle is d / 2.
 template <int D>
 __global__ void __launch_bounds__(kWave * kPrepWaves) prefill_prep_kernel(const PrefillArgs a) {
   constexpr int EPL = D / kWave;
@@ -82,6 +84,8 @@ __global__ void __launch_bounds__(kWave * kPrepWaves) prefill_prep_kernel(const 
     const float* src = is_q ? p.q + (static_cast<size_t>(row) * p.n_heads + v) * D
                             : p.k_new + static_cast<size_t>(row) * p.kv_dim + kvh * D;
     const float* w = is_q ? p.q_norm_w : p.k_norm_w;
+    const float one = (p.flags & SLOT_KV_FLAG_NORM_ONE_PLUS_W) ? 1.f : 0.f;
+    const bool inter = p.flags & SLOT_KV_FLAG_ROPE_INTERLEAVED;  // uniform
     float x[EPL];
     float ss = 0.f;
 #pragma unroll
@@ -91,13 +95,26 @@ __global__ void __launch_bounds__(kWave * kPrepWaves) prefill_prep_kernel(const 
     }
     ss = wave_sum(ss);
     const float rn = 1.0f / sqrtf(ss * (1.0f / D) + p.eps);
+    float xn[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) xn[e] = x[e] * rn * (one + w[lane * EPL + e]);
     float y[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-      const float xn = x[e] * rn * w[lane * EPL + e];
-      const float partner = __shfl_xor(xn, 32);
-      const uint32_t k = (lane & 31) * EPL + e;
-      y[e] = lane < 32 ? xn * cs[k] - partner * sn[k] : xn * cs[k] + partner * sn[k];
+      float partner;
+      bool first;
+      uint32_t k;
+      if (inter) {
+        if constexpr (EPL >= 2) partner = xn[e ^ 1];
+        else partner = __shfl_xor(xn[e], 1);
+        first = ((lane * EPL + e) & 1u) == 0;
+        k = (lane * EPL + e) / 2;
+      } else {
+        partner = __shfl_xor(xn[e], 32);
+        first = lane < 32;
+        k = (lane & 31) * EPL + e;
+      }
+      y[e] = first ? xn[e] * cs[k] - partner * sn[k] : xn[e] * cs[k] + partner * sn[k];
     }
     if (is_q) {
       float* dst = p.qs + (static_cast<size_t>(row) * p.n_heads + v) * D + lane * EPL;
@@ -106,10 +123,21 @@ __global__ void __launch_bounds__(kWave * kPrepWaves) prefill_prep_kernel(const 
     } else {
       const uint64_t at = at_row + kvh * D + lane * EPL;
       const float* vsrc = p.v_new + static_cast<size_t>(row) * p.kv_dim + kvh * D + lane * EPL;
+      float vw[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) vw[e] = vsrc[e];
+      if (p.flags & SLOT_KV_FLAG_V_NORM) {  // uniform: weightless RMSNorm of the value
+        float sv = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) sv += vw[e] * vw[e];
+        const float rv = 1.0f / sqrtf(wave_sum(sv) * (1.0f / D) + p.eps);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) vw[e] *= rv;
+      }
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         p.k_cache[at + e] = y[e];
-        p.v_cache[at + e] = vsrc[e];
+        p.v_cache[at + e] = vw[e];
       }
     }
   }

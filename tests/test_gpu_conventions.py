@@ -1,0 +1,92 @@
+"""GPU parity of the convention flags (SLOT_KV_FLAG_*: V-norm, interleaved
+RoPE, (1 + w) norm weights) on every entry point, against the oracle run with
+the same flags."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sequence_slot_kv_amd import binding as b
+from sequence_slot_kv_amd import workloads as wl
+
+from _gpu_util import assert_close
+
+pytestmark = pytest.mark.gpu
+
+FLAG_SETS = [oracle.V_NORM, oracle.ROPE_INTERLEAVED, oracle.NORM_ONE_PLUS_W,
+             oracle.V_NORM | oracle.ROPE_INTERLEAVED | oracle.NORM_ONE_PLUS_W]
+
+
+def _layer(rng, H, Hkv, D, flags, sinks):
+    L = wl.make_layer(rng, H, Hkv, D, 1e4, sinks)
+    return dataclasses.replace(L, flags=flags)
+
+
+def _cache(rng, n_slots, slot_ctx, kv_dim):
+    return (rng.standard_normal((n_slots, slot_ctx, kv_dim), dtype=np.float32),
+            rng.standard_normal((n_slots, slot_ctx, kv_dim), dtype=np.float32))
+
+
+def _handle(n_slots, slot_ctx, L, ck, cv):
+    kv = b.SlotKV()
+    kv.alloc(n_slots, slot_ctx, [L.kv_dim])
+    kv.set_layer(0, L)
+    for s in range(n_slots):
+        kv.write_rows(0, s, 0, torch.from_numpy(ck[s]).cuda(), torch.from_numpy(cv[s]).cuda())
+    return kv
+
+
+@pytest.mark.parametrize("flags", FLAG_SETS)
+@pytest.mark.parametrize("H,Hkv,D", [(4, 2, 64), (8, 2, 128), (4, 2, 256)])
+def test_decode_with_flags(flags, H, Hkv, D):
+    rng = np.random.default_rng(50 + flags + D)
+    n_slots, slot_ctx, B = 6, 700, 5   # rows up to two 512-key chunks
+    L = _layer(rng, H, Hkv, D, flags, sinks=True)
+    ck, cv = _cache(rng, n_slots, slot_ctx, L.kv_dim)
+    slots = rng.permutation(n_slots)[:B].astype(np.uint32)
+    positions = np.array([0, 1, 37, 511, 699], np.uint32)
+    q = rng.standard_normal((B, H * D), dtype=np.float32)
+    kn = rng.standard_normal((B, L.kv_dim), dtype=np.float32)
+    vn = rng.standard_normal((B, L.kv_dim), dtype=np.float32)
+    kv = _handle(n_slots, slot_ctx, L, ck, cv)
+    out = kv.decode_attn(0, *(torch.from_numpy(x).cuda() for x in (q, kn, vn)), positions, slots)
+    gk, gv = (x.cpu().numpy() for x in kv.layer_view(0))
+    out = out.cpu().numpy()
+    kv.close()
+    rc, ref = oracle.decode_batch(L, ck, cv, q, kn, vn, positions, slots)
+    assert rc == 0
+    assert_close(out, ref, f"decode out flags={flags}")
+    for p_, s_ in zip(positions, slots):
+        assert_close(gk[s_, p_], ck[s_, p_], "written K")
+        assert_close(gv[s_, p_], cv[s_, p_], "written V")
+
+
+@pytest.mark.parametrize("flags", FLAG_SETS)
+@pytest.mark.parametrize("H,Hkv,D", [(4, 2, 64), (8, 2, 128), (4, 2, 256)])
+def test_prefill_and_verify_with_flags(flags, H, Hkv, D):
+    rng = np.random.default_rng(60 + flags + D)
+    n_slots, slot_ctx = 4, 96
+    L = _layer(rng, H, Hkv, D, flags, sinks=True)
+    ck, cv = _cache(rng, n_slots, slot_ctx, L.kv_dim)
+    slots, pos0, ks = [2, 0, 3], [10, 0, 50], [21, 5, 9]
+    rows = sum(ks)
+    q = rng.standard_normal((rows, H * D), dtype=np.float32)
+    kn = rng.standard_normal((rows, L.kv_dim), dtype=np.float32)
+    vn = rng.standard_normal((rows, L.kv_dim), dtype=np.float32)
+    kv = _handle(n_slots, slot_ctx, L, ck, cv)
+    q_d, k_d, v_d = (torch.from_numpy(x).cuda() for x in (q, kn, vn))
+    # the first sequence by prefill, the others by one verify call
+    out_p = kv.prefill_attn(0, q_d[:ks[0]], k_d[:ks[0]], v_d[:ks[0]], slots[0], pos0[0]).cpu().numpy()
+    out_v = kv.verify_attn(0, q_d[ks[0]:], k_d[ks[0]:], v_d[ks[0]:], slots[1:], pos0[1:],
+                           ks[1:]).cpu().numpy()
+    gk, gv = (x.cpu().numpy() for x in kv.layer_view(0))
+    kv.close()
+    rc, ref = oracle.verify(L, ck, cv, q, kn, vn, slots, pos0, ks)
+    assert rc == 0
+    assert_close(out_p, ref[:ks[0]], f"prefill out flags={flags}")
+    assert_close(out_v, ref[ks[0]:], f"verify out flags={flags}")
+    for s_, p0, k in zip(slots, pos0, ks):
+        assert_close(gk[s_, p0:p0 + k], ck[s_, p0:p0 + k], "written K")
+        assert_close(gv[s_, p0:p0 + k], cv[s_, p0:p0 + k], "written V")
