@@ -82,6 +82,11 @@ def _load():
         lib.oracle_rms_norm_plain.restype = None
         lib.oracle_rope_interleaved.argtypes = [f64p, f32p, u32, u32]
         lib.oracle_rope_interleaved.restype = None
+        lib.oracle_slot_state_offset_bytes.argtypes = [u32, u32]
+        lib.oracle_slot_state_offset_bytes.restype = u64
+        lib.oracle_slot_reset.argtypes = [ctypes.POINTER(f32p), ctypes.POINTER(f32p), u32p, u32p,
+                                          u32, u32, u32p, u32]
+        lib.oracle_slot_reset.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -274,3 +279,34 @@ def verify(layer, cache_k, cache_v, q, k_new, v_new, slots, pos0, ks):
         _u32(slots, "slots"), _u32(pos0, "pos0"), _u32(ks, "ks"), slots.shape[0], _f32(out, "out"),
         _flags(L))
     return rc, out[:rows]
+
+
+# ---------------------------------------------------------------- per-slot SSM state
+def slot_state_offset_bytes(slot: int, state_len: int) -> int:
+    """Byte offset of slot ``slot`` in a [slot][state_len] f32 buffer: the conv
+    ring (state_len = conv_state_len) or the recurrent state (ssm_state_len)."""
+    return int(_load().oracle_slot_state_offset_bytes(slot, state_len))
+
+
+def slot_reset(conv, ssm, slots, n_slots=None) -> int:
+    """Reset of reused slots on admit: zeroes, in place, each listed slot's conv
+    ring and recurrent state in every ssm layer.  ``conv`` / ``ssm`` are lists
+    (one entry per ssm layer) of C-contiguous float32 arrays of shape
+    [n_slots, state_len].  Returns the status (ERANGE writes nothing)."""
+    lib = _load()
+    n_layers = len(conv)
+    if len(ssm) != n_layers:
+        raise ValueError("conv and ssm need one buffer per ssm layer each")
+    if n_slots is None:
+        n_slots = conv[0].shape[0] if n_layers else 0
+    for a in list(conv) + list(ssm):
+        if a.ndim != 2 or a.shape[0] != n_slots:
+            raise ValueError("state buffers must be [n_slots, state_len]")
+    f32p = ctypes.POINTER(ctypes.c_float)
+    cp = (f32p * max(n_layers, 1))(*[_f32(a, "conv") for a in conv])
+    sp = (f32p * max(n_layers, 1))(*[_f32(a, "ssm") for a in ssm])
+    cl = np.array([a.shape[1] for a in conv] or [0], np.uint32)
+    sl = np.array([a.shape[1] for a in ssm] or [0], np.uint32)
+    sv = np.ascontiguousarray(np.asarray(slots, np.uint32).reshape(-1))
+    return int(lib.oracle_slot_reset(cp, sp, _u32(cl, "conv_len"), _u32(sl, "ssm_len"), n_layers,
+                                     n_slots, _u32(sv, "slots"), sv.size))

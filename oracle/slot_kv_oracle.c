@@ -338,3 +338,45 @@ int oracle_verify(uint32_t n_heads, uint32_t n_kv_heads, uint32_t head_dim,
     }
     return ORACLE_OK;
 }
+
+/* ---------------------------------------------------------------- per-slot SSM state
+ * [FC] allocation of the per-sequence slot state: every ssm layer gets, per
+ * slot, a conv ring of conv_state_len floats and a recurrent state of
+ * ssm_state_len floats, each layer's buffers laid out [slot][state_len] and
+ * zero-initialised.  ssm layers are numbered on their own (0 .. n_layers-1).
+ *
+ * [FC] per-slot offsets: slot `slot`'s conv ring starts slot*conv_state_len*4
+ * bytes into its layer's conv buffer, and its recurrent state
+ * slot*ssm_state_len*4 bytes into its layer's state buffer.  One function
+ * serves both: the byte offset of slot `slot` in a [slot][state_len] f32
+ * buffer, in 64 bits. */
+uint64_t oracle_slot_state_offset_bytes(uint32_t slot, uint32_t state_len) {
+    return (uint64_t)slot * (uint64_t)state_len * (uint64_t)sizeof(float);
+}
+
+/* [FC] reset of a reused slot on admit: the SSM state accumulates over a
+ * sequence rather than being indexed by position, so a slot handed to a new
+ * request has its conv ring and its recurrent state zeroed in every ssm
+ * layer; the attention KV of the slot is left alone (nothing reads it past
+ * the new sequence's own positions).  A call names n slots (a slot may
+ * appear more than once: zeroing twice is zeroing once).  Every slot is
+ * checked before anything is written; with no state allocated (n_slots == 0)
+ * the call does nothing and succeeds.
+ * conv[l] / ssm[l] are layer l's buffers of n_slots*conv_len[l] and
+ * n_slots*ssm_len[l] floats. */
+int oracle_slot_reset(float **conv, float **ssm, const uint32_t *conv_len,
+                      const uint32_t *ssm_len, uint32_t n_layers, uint32_t n_slots,
+                      const uint32_t *slots, uint32_t n) {
+    if (n_slots == 0) return ORACLE_OK;
+    for (uint32_t i = 0; i < n; ++i)
+        if (slots[i] >= n_slots) return ORACLE_ERANGE;
+    for (uint32_t i = 0; i < n; ++i) {
+        for (uint32_t l = 0; l < n_layers; ++l) {
+            float *c = conv[l] + oracle_slot_state_offset_bytes(slots[i], conv_len[l]) / sizeof(float);
+            for (uint32_t e = 0; e < conv_len[l]; ++e) c[e] = 0.0f;
+            float *s = ssm[l] + oracle_slot_state_offset_bytes(slots[i], ssm_len[l]) / sizeof(float);
+            for (uint32_t e = 0; e < ssm_len[l]; ++e) s[e] = 0.0f;
+        }
+    }
+    return ORACLE_OK;
+}

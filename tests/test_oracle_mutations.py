@@ -53,8 +53,30 @@ MUTANTS = {
     "vnorm_skipped": ("if (flags & ORACLE_V_NORM) {", "if (0) {"),
     "interleaved_not_on_queries": ("if (flags & ORACLE_ROPE_INTERLEAVED)\n            oracle_rope_interleaved(qh",
                                    "if (0)\n            oracle_rope_interleaved(qh"),
+    # per-slot SSM state
+    "state_offset_32bit": (
+        "return (uint64_t)slot * (uint64_t)state_len * (uint64_t)sizeof(float);",
+        "return (uint64_t)(uint32_t)(slot * state_len * 4u);"),
+    "reset_conv_only": (
+        "for (uint32_t e = 0; e < ssm_len[l]; ++e) s[e] = 0.0f;", "(void)s;"),
+    "reset_first_layer_only": (
+        "for (uint32_t l = 0; l < n_layers; ++l) {\n            float *c",
+        "for (uint32_t l = 0; l < n_layers && l < 1; ++l) {\n            float *c"),
+    "reset_short_by_one": (
+        "e < conv_len[l]; ++e) c[e]", "e + 1 < conv_len[l]; ++e) c[e]"),
+    "reset_ssm_stride_from_conv": (
+        "oracle_slot_state_offset_bytes(slots[i], ssm_len[l])",
+        "oracle_slot_state_offset_bytes(slots[i], conv_len[l])"),
+    "reset_partial_write_on_error": (
+        "for (uint32_t i = 0; i < n; ++i)\n        if (slots[i] >= n_slots) return ORACLE_ERANGE;\n"
+        "    for (uint32_t i = 0; i < n; ++i) {\n",
+        "for (uint32_t i = 0; i < n; ++i) {\n        if (slots[i] >= n_slots) return ORACLE_ERANGE;\n"),
+    "reset_unallocated_not_noop": (
+        "if (n_slots == 0) return ORACLE_OK;\n    for (uint32_t i = 0; i < n; ++i)\n        if (slots",
+        "for (uint32_t i = 0; i < n; ++i)\n        if (slots"),
 }
-PIN_FILES = ["test_oracle_pins.py", "test_oracle_prefill_pins.py", "test_oracle_conventions.py"]
+PIN_FILES = ["test_oracle_pins.py", "test_oracle_prefill_pins.py", "test_oracle_conventions.py",
+             "test_oracle_state_pins.py"]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
