@@ -35,6 +35,13 @@ slot_verify_attn call per step: 4 rows for each of 64 sequences):
   value        rows/s
   roofline     KV bytes (each sequence's keys 0..pos0+k-1, K and V, once) /
                mean attention-kernel time vs 8 TB/s
+
+With --workload state_admit it measures the reset of reused slots on admit
+(one slot_reset_batch call per step: 8 slots of a 36-ssm-layer state):
+  value        slot resets/s
+  roofline     bytes zeroed (every listed slot's conv ring and recurrent state)
+               / mean reset-kernel time vs 8 TB/s
+  cpu_baseline the CPU oracle's reset of the same slots' state in host memory
 """
 from __future__ import annotations
 
@@ -54,6 +61,7 @@ HBM_PEAK_GBPS = 8000.0
 MFMA_F32_PEAK_TFLOPS = 157.3
 PREFILL_METRIC = "slot prefill tokens/s and attention TFLOP/s (f32 matrix cores)"
 VERIFY_METRIC = "multi-row verify rows/s and achieved KV HBM GB/s (% of peak)"
+STATE_METRIC = "slot resets/s on admit and achieved HBM write GB/s (% of peak)"
 KERNEL_SRC = os.path.join(ROOT, "sequence_slot_kv_amd", "csrc", "slot_kv_kernels.hip")
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
@@ -113,7 +121,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mid",
                     choices=["tiny", "mid", "long", "many", "layer_stack", "prefill_prompt",
-                             "prefill_chunk", "verify_mid"])
+                             "prefill_chunk", "verify_mid", "state_admit"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the reference "
@@ -144,6 +152,8 @@ def main():
         return prefill_bench(args, wl.PREFILL_WORKLOADS[args.workload](), b)
     if args.workload.startswith("verify"):
         return verify_bench(args, wl.VERIFY_WORKLOADS[args.workload](), b)
+    if args.workload.startswith("state"):
+        return state_bench(args, wl.STATE_WORKLOADS[args.workload](), b)
     w = wl.WORKLOADS[args.workload]()
     n_layers = len(w.layers)
     log(f"[bench] workload {w.name}: B={w.B} n_slots={w.n_slots} slot_ctx={w.slot_ctx} "
@@ -413,6 +423,81 @@ def verify_bench(args, w, b):
     }
     print(json.dumps(res), flush=True)
     kv.close()
+
+
+def state_bench(args, w, b):
+    import numpy as np
+    import torch
+    n_layers = len(w.conv_state_len)
+    log(f"[bench] state reset {w.name}: {len(w.slots)} of {w.n_slots} slots, {n_layers} ssm "
+        f"layers, {w.bytes_per_slot()} bytes per slot, {w.write_bytes()} bytes per step")
+    kv = b.SlotKV()
+    kv.alloc_state(w.n_slots, 1, [], w.conv_state_len, w.ssm_state_len)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w.state_seed)
+    for l in range(n_layers):
+        for view in kv.state_view(l):
+            view.normal_(generator=g)
+    torch.cuda.synchronize()
+
+    def step():
+        kv.reset_batch(w.slots)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    rc = b.slot_kv_profile_begin(kv.h)
+    assert rc == 0
+    for _ in range(args.steps):
+        step()
+    rc, k_ms, launches = b.slot_kv_profile_end(kv.h)
+    torch.cuda.synchronize()
+    assert rc == 0 and launches == args.steps
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    k_us = k_ms / launches * 1e3
+    achieved = w.write_bytes() / (k_us * 1e-6) / 1e9
+    log(f"[bench] {ms_per_step * 1e3:.1f} us/step, reset kernel {k_us:.1f} us, "
+        f"{achieved:.0f} GB/s")
+    kv.close()
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        # the oracle's reset of the same slots, each held in its own host
+        # state (one slot per entry, so only the listed slots are allocated)
+        n = len(w.slots)
+        conv = [np.ones((n, c), np.float32) for c in w.conv_state_len]
+        ssm = [np.ones((n, s_), np.float32) for s_ in w.ssm_state_len]
+        idx = np.arange(n, dtype=np.uint32)
+        c0, reps = time.perf_counter(), 0
+        while True:
+            assert oracle.slot_reset(conv, ssm, idx) == 0
+            reps += 1
+            if time.perf_counter() - c0 >= 10.0:
+                break
+        dt = time.perf_counter() - c0
+        cpu = {"value": reps * n / dt, "unit": "slot resets/s", "cores": 1, "kind": "oracle",
+               "sample": f"{reps} resets of {n} slots ({w.write_bytes()} bytes each) in host "
+                         f"memory, {dt:.1f} s on one thread"}
+    res = {
+        "metric": STATE_METRIC, "value": len(w.slots) / (ms_per_step / 1e3),
+        "unit": "slot resets/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "n_reset": len(w.slots), "n_slots": w.n_slots,
+                   "n_ssm_layers": n_layers, "conv_state_len": w.conv_state_len[0],
+                   "ssm_state_len": w.ssm_state_len[0], "seed": w.seed},
+        "write_bytes_per_step": w.write_bytes(),
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "state_reset_kernel", "kernel_us": k_us},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
 
 
 if __name__ == "__main__":

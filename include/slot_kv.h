@@ -6,8 +6,9 @@
  *   "Forward Cuda Gemma" (Zig API of ForwardGemma): sections decodeBatch,
  *       allocSlotKv, slotKvOffsetBytes, slotKvSmoke;
  *   "Forward Cuda" (Zig API of ForwardCuda): sections on init (upload of the
- *       inv_freq table and the sinks, zeroed KV cache), the slot K/V byte
- *       offset, and the reset of a reused slot on admit.
+ *       inv_freq table and the sinks, zeroed KV cache and SSM state), the
+ *       allocation of per-sequence slot state, the slot K/V, conv-ring and
+ *       recurrent-state byte offsets, and the reset of a reused slot on admit.
  *
  * Conventions shared by every entry point
  *   - Status codes: 0 on success, a negative SLOT_KV_E* value on failure;
@@ -59,9 +60,30 @@ void slot_kv_destroy(slot_kv *h);
  * and fills them with zeros.  kv_dims is a host array of n_layers counts of
  * floats per KV row.  Idempotent: any previous allocation of this handle is
  * freed first (layer configurations are dropped with it).
- * Errors: EINVAL (zero sizes, NULL kv_dims, size overflow), ENOMEM, EDEVICE. */
+ * Errors: EINVAL (zero sizes, NULL kv_dims, size overflow), ENOMEM, EDEVICE.
+ * The same as slot_state_alloc with no ssm layers. */
 int slot_kv_alloc(slot_kv *h, uint32_t n_slots, uint32_t slot_ctx,
                   const uint32_t *kv_dims, uint32_t n_layers);
+
+/* "Forward Cuda", allocation of the per-sequence slot state for a hybrid
+ * attention + SSM model: attention layers get slot KV (as slot_kv_alloc),
+ * ssm layers get per slot a conv ring and a recurrent state, all zeroed.
+ * Attention layers are numbered 0 .. n_attn_layers-1 and ssm layers,
+ * separately, 0 .. n_ssm_layers-1.  Ssm layer l owns two device buffers:
+ *   conv  [n_slots][conv_state_len[l]] floats,
+ *   state [n_slots][ssm_state_len[l]]  floats.
+ * kv_dims (host, n_attn_layers entries) may be NULL when n_attn_layers is 0;
+ * conv_state_len and ssm_state_len (host, n_ssm_layers entries, each > 0)
+ * may be NULL when n_ssm_layers is 0.  At least one layer is required.
+ * What the SSM kernels keep in the buffers is theirs to define; this library
+ * lays them out, addresses them and zeroes them.  Idempotent: any previous
+ * allocation of the handle (KV and state, and the layer configurations) is
+ * freed first.  Errors: EINVAL (zero sizes, NULL arrays, one slot's state
+ * above 2^31 tiles of 16 KiB), ENOMEM, EDEVICE. */
+int slot_state_alloc(slot_kv *h, uint32_t n_slots, uint32_t slot_ctx,
+                     const uint32_t *kv_dims, uint32_t n_attn_layers,
+                     const uint32_t *conv_state_len, const uint32_t *ssm_state_len,
+                     uint32_t n_ssm_layers);
 
 /* "Forward Cuda", init: upload of inv_freq and sinks.
  * Configures attention layer `layer`: n_heads query heads and n_kv_heads KV
@@ -108,12 +130,35 @@ int slot_kv_set_layer_flags(slot_kv *h, uint32_t layer, uint32_t flags);
 int slot_kv_offset_bytes(const slot_kv *h, uint32_t layer, uint32_t slot,
                          uint32_t pos, uint64_t *out_bytes);
 
-/* "Forward Cuda", reset of a reused slot on admit.
- * The attention slot KV needs no clearing: it is indexed by position, each
- * sequence overwrites from position 0 and reads only what it wrote.  So this
- * validates `slot` and does nothing else.  Returns OK when nothing is
- * allocated (no-op), ERANGE when slot >= n_slots. */
-int slot_reset(slot_kv *h, uint32_t slot);
+/* "Forward Cuda", byte offsets of slot `slot`'s conv ring and recurrent state
+ * in ssm layer `ssm_layer`'s buffers: slot * conv_state_len * 4 and
+ * slot * ssm_state_len * 4, in 64 bits.  Errors: ENOTALLOC, EINVAL (ssm_layer
+ * or out_bytes), ERANGE (slot >= n_slots). */
+int slot_conv_offset_bytes(const slot_kv *h, uint32_t ssm_layer, uint32_t slot,
+                           uint64_t *out_bytes);
+int slot_ssm_offset_bytes(const slot_kv *h, uint32_t ssm_layer, uint32_t slot,
+                          uint64_t *out_bytes);
+
+/* Device pointers of ssm layer `ssm_layer`'s conv and recurrent-state buffers
+ * (owned by the handle, valid until the next allocation or slot_kv_destroy;
+ * either output may be NULL).  Errors: ENOTALLOC, EINVAL. */
+int slot_state_ptrs(const slot_kv *h, uint32_t ssm_layer, float **conv, float **ssm);
+
+/* "Forward Cuda", reset of a reused slot on admit, before the new request's
+ * prefill.  The SSM state accumulates over a sequence, so the slot's conv
+ * ring and recurrent state are zeroed in every ssm layer (one kernel launch
+ * on `stream`, hipStream_t, NULL = the null stream).  The attention slot KV
+ * needs no clearing: it is indexed by position, each sequence overwrites from
+ * position 0 and reads only what it wrote, so it is left as it is; with no
+ * ssm layers the call only validates.  Returns OK without doing anything when
+ * nothing is allocated, ERANGE when slot >= n_slots. */
+int slot_reset(slot_kv *h, uint32_t slot, void *stream);
+
+/* slot_reset for n slots at once (host array, copied before the call
+ * returns; a slot may appear twice).  Every slot is checked before anything
+ * is enqueued; one launch per 256 slots.  n == 0 is a no-op.  Errors: EINVAL
+ * (NULL slots with n > 0), ERANGE, EDEVICE. */
+int slot_reset_batch(slot_kv *h, const uint32_t *slots, uint32_t n, void *stream);
 
 /* "Forward Cuda Gemma", decodeBatch (its attention part).
  * Advances B independent sequences by one token each.  Row b uses its own
@@ -220,9 +265,10 @@ uint32_t slot_kv_chunk_keys(void);
 /* Profiling of the attention kernels.  Between slot_kv_profile_begin and
  * slot_kv_profile_end the handle records a HIP event pair on the call's
  * stream immediately around each launch of the fused decode kernel (one
- * launch per 256 rows of a slot_decode_attn call; it does the whole step) and
- * of the prefill attention kernel (one per slot_prefill_attn call, one per
- * 128 sequences of a slot_verify_attn call).
+ * launch per 256 rows of a slot_decode_attn call; it does the whole step), of
+ * the prefill attention kernel (one per slot_prefill_attn call, one per 128
+ * sequences of a slot_verify_attn call) and of the state-reset kernel (one per
+ * 256 slots of a slot_reset / slot_reset_batch call).
  * slot_kv_profile_end waits for the recorded launches and returns their
  * summed duration in milliseconds and their count (either pointer may be
  * NULL), then stops recording.  Errors: EINVAL, EDEVICE. */

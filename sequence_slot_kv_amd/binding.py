@@ -30,7 +30,8 @@ SLOT_KV_EDEVICE = -6
 EXPORTS = ("slot_kv_create", "slot_kv_destroy", "slot_kv_alloc", "slot_kv_set_layer",
            "slot_kv_set_layer_flags", "slot_kv_offset_bytes", "slot_reset", "slot_decode_attn",
            "slot_prefill_attn",
-           "slot_verify_attn",
+           "slot_verify_attn", "slot_state_alloc", "slot_conv_offset_bytes",
+           "slot_ssm_offset_bytes", "slot_state_ptrs", "slot_reset_batch",
            "slot_kv_layer_ptrs",
            "slot_kv_write_rows", "slot_kv_read_rows", "slot_kv_check_batch",
            "slot_kv_chunk_keys", "slot_kv_profile_begin", "slot_kv_profile_end",
@@ -59,7 +60,12 @@ _lib.slot_kv_alloc.argtypes = [_vp, _u32, _u32, _u32p, _u32]
 _lib.slot_kv_set_layer.argtypes = [_vp, _u32, _u32, _u32, _u32, _f32p, _f32p, _f32p, _f32p,
                                    ctypes.c_float, ctypes.c_float]
 _lib.slot_kv_offset_bytes.argtypes = [_vp, _u32, _u32, _u32, ctypes.POINTER(ctypes.c_uint64)]
-_lib.slot_reset.argtypes = [_vp, _u32]
+_lib.slot_reset.argtypes = [_vp, _u32, _vp]
+_lib.slot_reset_batch.argtypes = [_vp, _u32p, _u32, _vp]
+_lib.slot_state_alloc.argtypes = [_vp, _u32, _u32, _u32p, _u32, _u32p, _u32p, _u32]
+_lib.slot_conv_offset_bytes.argtypes = [_vp, _u32, _u32, ctypes.POINTER(ctypes.c_uint64)]
+_lib.slot_ssm_offset_bytes.argtypes = [_vp, _u32, _u32, ctypes.POINTER(ctypes.c_uint64)]
+_lib.slot_state_ptrs.argtypes = [_vp, _u32, ctypes.POINTER(_vp), ctypes.POINTER(_vp)]
 _lib.slot_kv_set_layer_flags.argtypes = [_vp, _u32, _u32]
 _lib.slot_decode_attn.argtypes = [_vp, _u32, _vp, _vp, _vp, _u32p, _u32p, _u32, _vp, _vp]
 _lib.slot_prefill_attn.argtypes = [_vp, _u32, _vp, _vp, _vp, _u32, _u32, _u32, _vp, _vp]
@@ -172,8 +178,43 @@ def slot_kv_offset_bytes(h, layer, slot, pos):
     return rc, int(out.value)
 
 
-def slot_reset(h, slot) -> int:
-    return _lib.slot_reset(h, slot)
+def slot_reset(h, slot, stream=None) -> int:
+    return _lib.slot_reset(h, slot, _stream_handle(stream))
+
+
+def slot_reset_batch(h, slots, stream=None) -> int:
+    sv = _host_u32(slots)
+    return _lib.slot_reset_batch(h, _ptr_u32(sv), sv.size, _stream_handle(stream))
+
+
+def slot_state_alloc(h, n_slots, slot_ctx, kv_dims, conv_state_len, ssm_state_len) -> int:
+    dims, cl, sl = (_host_u32(x) for x in (kv_dims, conv_state_len, ssm_state_len))
+    if cl.size != sl.size:
+        return SLOT_KV_EINVAL
+    return _lib.slot_state_alloc(h, n_slots, slot_ctx, _ptr_u32(dims) if dims.size else None,
+                                 dims.size, _ptr_u32(cl) if cl.size else None,
+                                 _ptr_u32(sl) if sl.size else None, cl.size)
+
+
+def slot_conv_offset_bytes(h, ssm_layer, slot):
+    """Returns (status, offset)."""
+    out = ctypes.c_uint64(0)
+    rc = _lib.slot_conv_offset_bytes(h, ssm_layer, slot, ctypes.byref(out))
+    return rc, int(out.value)
+
+
+def slot_ssm_offset_bytes(h, ssm_layer, slot):
+    """Returns (status, offset)."""
+    out = ctypes.c_uint64(0)
+    rc = _lib.slot_ssm_offset_bytes(h, ssm_layer, slot, ctypes.byref(out))
+    return rc, int(out.value)
+
+
+def slot_state_ptrs(h, ssm_layer):
+    """Returns (status, conv pointer, recurrent-state pointer)."""
+    c, s_ = _vp(), _vp()
+    rc = _lib.slot_state_ptrs(h, ssm_layer, ctypes.byref(c), ctypes.byref(s_))
+    return rc, c.value, s_.value
 
 
 def slot_decode_attn(h, layer, q, k_new, v_new, positions, slots, out, stream=None) -> int:
@@ -269,6 +310,19 @@ def slot_kv_strerror(status: int) -> str:
 
 
 # ---------------------------------------------------------------- convenience
+def _device_view(ptr, shape):
+    """A torch float32 tensor over device memory the handle owns (no copy)."""
+    import torch
+
+    class _Arr:
+        def __init__(self):
+            self.__cuda_array_interface__ = {
+                "shape": tuple(shape), "typestr": "<f4", "data": (ptr, False), "version": 2,
+                "strides": None}
+
+    return torch.as_tensor(_Arr(), device=torch.device("cuda", torch.cuda.current_device()))
+
+
 class SlotKV:
     """Owning wrapper of one handle; raises SlotKVError on any failure."""
 
@@ -276,6 +330,7 @@ class SlotKV:
         self.h = slot_kv_create()
         self.n_slots = self.slot_ctx = 0
         self.kv_dims: list = []
+        self.state_lens: list = []  # (conv_state_len, ssm_state_len) per ssm layer
         self.layers: dict = {}
 
     def close(self):
@@ -292,7 +347,37 @@ class SlotKV:
     def alloc(self, n_slots, slot_ctx, kv_dims):
         _check(slot_kv_alloc(self.h, n_slots, slot_ctx, kv_dims), "slot_kv_alloc")
         self.n_slots, self.slot_ctx, self.kv_dims = n_slots, slot_ctx, list(kv_dims)
+        self.state_lens, self.layers = [], {}
+
+    def alloc_state(self, n_slots, slot_ctx, kv_dims, conv_state_len, ssm_state_len):
+        """Slot KV for the attention layers and a conv ring and recurrent state
+        per slot for each ssm layer (slot_state_alloc)."""
+        _check(slot_state_alloc(self.h, n_slots, slot_ctx, kv_dims, conv_state_len,
+                                ssm_state_len), "slot_state_alloc")
+        self.n_slots, self.slot_ctx, self.kv_dims = n_slots, slot_ctx, list(kv_dims)
+        self.state_lens = list(zip(conv_state_len, ssm_state_len))
         self.layers = {}
+
+    def state_view(self, ssm_layer):
+        """torch views of ssm layer ``ssm_layer``'s conv ring [n_slots, conv_state_len]
+        and recurrent state [n_slots, ssm_state_len] (device memory owned by the handle)."""
+        rc, cp, sp = slot_state_ptrs(self.h, ssm_layer)
+        _check(rc, "slot_state_ptrs")
+        cl, sl = self.state_lens[ssm_layer]
+        return _device_view(cp, (self.n_slots, cl)), _device_view(sp, (self.n_slots, sl))
+
+    def conv_offset_bytes(self, ssm_layer, slot) -> int:
+        rc, off = slot_conv_offset_bytes(self.h, ssm_layer, slot)
+        _check(rc, "slot_conv_offset_bytes")
+        return off
+
+    def ssm_offset_bytes(self, ssm_layer, slot) -> int:
+        rc, off = slot_ssm_offset_bytes(self.h, ssm_layer, slot)
+        _check(rc, "slot_ssm_offset_bytes")
+        return off
+
+    def reset_batch(self, slots, stream=None):
+        _check(slot_reset_batch(self.h, slots, stream), "slot_reset_batch")
 
     def set_layer(self, layer, params):
         """``params`` has the fields of workloads.LayerParams."""
@@ -310,8 +395,8 @@ class SlotKV:
         _check(rc, "slot_kv_offset_bytes")
         return off
 
-    def reset(self, slot):
-        _check(slot_reset(self.h, slot), "slot_reset")
+    def reset(self, slot, stream=None):
+        _check(slot_reset(self.h, slot, stream), "slot_reset")
 
     def decode_attn(self, layer, q, k_new, v_new, positions, slots, out=None, stream=None):
         import torch
@@ -369,15 +454,7 @@ class SlotKV:
         rc, kp, vp = slot_kv_layer_ptrs(self.h, layer)
         _check(rc, "slot_kv_layer_ptrs")
         shape = (self.n_slots, self.slot_ctx, self.kv_dims[layer])
-
-        class _Arr:
-            def __init__(self, ptr):
-                self.__cuda_array_interface__ = {
-                    "shape": shape, "typestr": "<f4", "data": (ptr, False), "version": 2,
-                    "strides": None}
-
-        dev = torch.device("cuda", torch.cuda.current_device())
-        return (torch.as_tensor(_Arr(kp), device=dev), torch.as_tensor(_Arr(vp), device=dev))
+        return _device_view(kp, shape), _device_view(vp, shape)
 
     def write_rows(self, layer, slot, pos0, k_src=None, v_src=None, stream=None):
         _check(slot_kv_write_rows(self.h, layer, slot, pos0, k_src, v_src, stream=stream),

@@ -21,7 +21,8 @@ LIB = os.path.join(PKG, "libslot_kv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["slot_kv_api.hip", "slot_kv_kernels.hip", "slot_kv_prefill.hip", "slot_kv_plan.cpp"]
+SOURCES = ["slot_kv_api.hip", "slot_kv_kernels.hip", "slot_kv_prefill.hip", "slot_kv_state.hip",
+           "slot_kv_plan.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

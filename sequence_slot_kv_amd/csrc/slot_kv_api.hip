@@ -6,7 +6,10 @@
 // "Forward Cuda Gemma": allocSlotKv (idempotent, frees first), slotKvOffsetBytes
 // ((slot*slot_ctx + pos)*kv_dim*4), decodeBatch (preconditions, per-row
 // slot and position); "Forward Cuda": init (zeroed cache, inv_freq and sinks
-// uploaded), reset of a reused slot (nothing to clear for attention KV).
+// uploaded), allocation of the per-sequence slot state (attention KV, and a
+// conv ring and recurrent state per ssm layer), their byte offsets, and the
+// reset of a reused slot (nothing to clear for attention KV; the SSM state
+// is zeroed).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -36,12 +39,21 @@ struct LayerState {
   uint32_t flags = 0;  // SLOT_KV_FLAG_*
 };
 
+struct SsmLayer {
+  uint32_t conv_len = 0, ssm_len = 0;  // floats per slot
+  float* conv = nullptr;               // [n_slots][conv_len]
+  float* ssm = nullptr;                // [n_slots][ssm_len]
+};
+
 }  // namespace
 
 struct slot_kv {
   int device = -1;
   uint32_t n_slots = 0, slot_ctx = 0;
   std::vector<LayerState> layers;
+  std::vector<SsmLayer> ssm;                  // per-slot SSM state, one entry per ssm layer
+  slotkv::StateSeg* state_segs = nullptr;     // device table of the reset kernel
+  uint32_t state_tiles_per_slot = 0;
   float* part = nullptr;         // partial results of split rows (acc, then max/sum)
   size_t part_cap = 0;           // floats
   uint32_t* counters = nullptr;  // work queue [2], then per (row, kv head) chunk counters;
@@ -49,10 +61,11 @@ struct slot_kv {
   size_t counters_cap = 0;       // entries
   AttnArgs args;                 // kernel arguments of the decode launch being built
   slotkv::PrefillArgs pargs;     // kernel arguments of the prefill launch being built
+  slotkv::ResetArgs rargs;       // kernel arguments of the state-reset launch being built
   bool profiling = false;
   std::vector<hipEvent_t> prof_events;  // start/end pairs
   size_t prof_used = 0;                 // pairs recorded since profile_begin
-  bool allocated() const { return !layers.empty(); }
+  bool allocated() const { return n_slots != 0; }
 };
 
 namespace {
@@ -64,6 +77,14 @@ void free_layers(slot_kv* h) {
     if (L.params) (void)hipFree(L.params);
   }
   h->layers.clear();
+  for (auto& S : h->ssm) {
+    if (S.conv) (void)hipFree(S.conv);
+    if (S.ssm) (void)hipFree(S.ssm);
+  }
+  h->ssm.clear();
+  if (h->state_segs) (void)hipFree(h->state_segs);
+  h->state_segs = nullptr;
+  h->state_tiles_per_slot = 0;
 }
 
 void free_scratch(slot_kv* h) {
@@ -162,15 +183,23 @@ void slot_kv_destroy(slot_kv* h) {
   delete h;
 }
 
-int slot_kv_alloc(slot_kv* h, uint32_t n_slots, uint32_t slot_ctx, const uint32_t* kv_dims,
-                  uint32_t n_layers) {
-  if (!h || !kv_dims || n_slots == 0 || slot_ctx == 0 || n_layers == 0) return SLOT_KV_EINVAL;
-  for (uint32_t L = 0; L < n_layers; ++L) {
+int slot_state_alloc(slot_kv* h, uint32_t n_slots, uint32_t slot_ctx, const uint32_t* kv_dims,
+                     uint32_t n_attn_layers, const uint32_t* conv_state_len,
+                     const uint32_t* ssm_state_len, uint32_t n_ssm_layers) {
+  if (!h || n_slots == 0 || slot_ctx == 0 || n_attn_layers + uint64_t(n_ssm_layers) == 0)
+    return SLOT_KV_EINVAL;
+  if (n_attn_layers && !kv_dims) return SLOT_KV_EINVAL;
+  if (n_ssm_layers && (!conv_state_len || !ssm_state_len)) return SLOT_KV_EINVAL;
+  // Byte sizes are products of 32-bit factors (times 4), so they fit 64 bits.
+  for (uint32_t L = 0; L < n_attn_layers; ++L)
     if (kv_dims[L] == 0) return SLOT_KV_EINVAL;
-    // bytes = n_slots*slot_ctx*kv_dim*4 must fit 64 bits (it always does for
-    // 32-bit factors below 2^62 / 4); rows must also fit the u32 kernel math
-    // of positions, which they do by type.
+  uint64_t tiles = 0;
+  for (uint32_t L = 0; L < n_ssm_layers; ++L) {
+    if (conv_state_len[L] == 0 || ssm_state_len[L] == 0) return SLOT_KV_EINVAL;
+    tiles += slotkv::reset_tiles(conv_state_len[L]) + slotkv::reset_tiles(ssm_state_len[L]);
   }
+  // one slot's reset must fit one grid (and tile0 must fit 32 bits)
+  if (tiles > 0x7fffffffu) return SLOT_KV_EINVAL;
   // Idempotent: drop any earlier allocation (and its layer configurations).
   if (h->device >= 0) (void)hipDeviceSynchronize();
   free_layers(h);
@@ -179,39 +208,63 @@ int slot_kv_alloc(slot_kv* h, uint32_t n_slots, uint32_t slot_ctx, const uint32_
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return SLOT_KV_EDEVICE;
   h->device = dev;
-  std::vector<LayerState> layers(n_layers);
-  const uint64_t rows = static_cast<uint64_t>(n_slots) * slot_ctx;
-  for (uint32_t L = 0; L < n_layers; ++L) {
-    const uint64_t bytes = rows * kv_dims[L] * sizeof(float);
-    layers[L].kv_dim = kv_dims[L];
-    void* k = nullptr;
-    void* v = nullptr;
-    if (hipMalloc(&k, bytes) != hipSuccess) k = nullptr;
-    if (k && hipMalloc(&v, bytes) != hipSuccess) v = nullptr;
-    layers[L].k = static_cast<float*>(k);
-    layers[L].v = static_cast<float*>(v);
-    if (!k || !v) {
-      h->layers.swap(layers);
-      free_layers(h);
-      (void)hipGetLastError();
-      return SLOT_KV_ENOMEM;
-    }
-    // "Forward Cuda", init: the KV cache starts zeroed.
-    if (hipMemset(k, 0, bytes) != hipSuccess || hipMemset(v, 0, bytes) != hipSuccess) {
-      h->layers.swap(layers);
-      free_layers(h);
-      return SLOT_KV_EDEVICE;
-    }
-  }
-  if (hipDeviceSynchronize() != hipSuccess) {
-    h->layers.swap(layers);
+  // Everything is allocated into h's vectors as it goes, so a failure part
+  // way frees exactly what was made.
+  auto fail = [h](int rc) {
+    (void)hipGetLastError();
     free_layers(h);
-    return SLOT_KV_EDEVICE;
+    return rc;
+  };
+  // "Forward Cuda", init: the KV cache and the SSM state start zeroed.
+  auto zeroed = [](size_t bytes, float** out) {
+    void* p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess) return SLOT_KV_ENOMEM;
+    *out = static_cast<float*>(p);
+    return hipMemset(p, 0, bytes) == hipSuccess ? SLOT_KV_OK : SLOT_KV_EDEVICE;
+  };
+  h->layers.resize(n_attn_layers);
+  const uint64_t rows = static_cast<uint64_t>(n_slots) * slot_ctx;
+  for (uint32_t L = 0; L < n_attn_layers; ++L) {
+    const uint64_t bytes = rows * kv_dims[L] * sizeof(float);
+    h->layers[L].kv_dim = kv_dims[L];
+    int rc = zeroed(bytes, &h->layers[L].k);
+    if (!rc) rc = zeroed(bytes, &h->layers[L].v);
+    if (rc) return fail(rc);
   }
-  h->layers.swap(layers);
+  h->ssm.resize(n_ssm_layers);
+  std::vector<slotkv::StateSeg> segs;
+  uint32_t tile0 = 0;
+  for (uint32_t L = 0; L < n_ssm_layers; ++L) {
+    SsmLayer& S = h->ssm[L];
+    S.conv_len = conv_state_len[L];
+    S.ssm_len = ssm_state_len[L];
+    int rc = zeroed(uint64_t(n_slots) * S.conv_len * sizeof(float), &S.conv);
+    if (!rc) rc = zeroed(uint64_t(n_slots) * S.ssm_len * sizeof(float), &S.ssm);
+    if (rc) return fail(rc);
+    segs.push_back({S.conv, S.conv_len, tile0, 0});
+    tile0 += static_cast<uint32_t>(slotkv::reset_tiles(S.conv_len));
+    segs.push_back({S.ssm, S.ssm_len, tile0, 0});
+    tile0 += static_cast<uint32_t>(slotkv::reset_tiles(S.ssm_len));
+  }
+  if (!segs.empty()) {
+    const size_t bytes = segs.size() * sizeof(slotkv::StateSeg);
+    void* p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess) return fail(SLOT_KV_ENOMEM);
+    h->state_segs = static_cast<slotkv::StateSeg*>(p);
+    if (hipMemcpy(p, segs.data(), bytes, hipMemcpyHostToDevice) != hipSuccess)
+      return fail(SLOT_KV_EDEVICE);
+    h->state_tiles_per_slot = tile0;
+  }
+  if (hipDeviceSynchronize() != hipSuccess) return fail(SLOT_KV_EDEVICE);
   h->n_slots = n_slots;
   h->slot_ctx = slot_ctx;
   return SLOT_KV_OK;
+}
+
+int slot_kv_alloc(slot_kv* h, uint32_t n_slots, uint32_t slot_ctx, const uint32_t* kv_dims,
+                  uint32_t n_layers) {
+  if (!h || !kv_dims || n_layers == 0) return SLOT_KV_EINVAL;
+  return slot_state_alloc(h, n_slots, slot_ctx, kv_dims, n_layers, nullptr, nullptr, 0);
 }
 
 int slot_kv_set_layer(slot_kv* h, uint32_t layer, uint32_t n_heads, uint32_t n_kv_heads,
@@ -279,10 +332,66 @@ int slot_kv_offset_bytes(const slot_kv* h, uint32_t layer, uint32_t slot, uint32
   return SLOT_KV_OK;
 }
 
-int slot_reset(slot_kv* h, uint32_t slot) {
+int slot_reset_batch(slot_kv* h, const uint32_t* slots, uint32_t n, void* stream) {
   if (!h) return SLOT_KV_EINVAL;
   if (!h->allocated()) return SLOT_KV_OK;  // no-op when nothing is allocated
-  return slot < h->n_slots ? SLOT_KV_OK : SLOT_KV_ERANGE;
+  if (n && !slots) return SLOT_KV_EINVAL;
+  for (uint32_t i = 0; i < n; ++i)
+    if (slots[i] >= h->n_slots) return SLOT_KV_ERANGE;
+  // Attention KV needs no clearing; only ssm layers have state to zero.
+  if (h->ssm.empty() || n == 0) return SLOT_KV_OK;
+  slotkv::ResetArgs& a = h->rargs;
+  a.segs = h->state_segs;
+  a.n_seg = static_cast<uint32_t>(2 * h->ssm.size());
+  a.tiles_per_slot = h->state_tiles_per_slot;
+  // slots per launch: at most kMaxResetPerLaunch, and a grid below 2^31
+  const uint32_t per = static_cast<uint32_t>(std::min<uint64_t>(
+      slotkv::kMaxResetPerLaunch, std::max<uint64_t>(1, 0x7fffffffu / a.tiles_per_slot)));
+  for (uint32_t i0 = 0; i0 < n; i0 += per) {
+    a.n = std::min(per, n - i0);
+    std::memcpy(a.slots, slots + i0, a.n * sizeof(uint32_t));
+    hipEvent_t e0, e1;
+    int rc = prof_pair(h, &e0, &e1);
+    if (rc) return rc;
+    if (slotkv::launch_state_reset(a, stream, e0, e1) != hipSuccess) return SLOT_KV_EDEVICE;
+  }
+  return SLOT_KV_OK;
+}
+
+int slot_reset(slot_kv* h, uint32_t slot, void* stream) {
+  return slot_reset_batch(h, &slot, 1, stream);
+}
+
+// Offset of `slot` in ssm layer `ssm_layer`'s conv buffer (which = 0) or
+// recurrent-state buffer (which = 1).
+static int state_offset(const slot_kv* h, uint32_t ssm_layer, uint32_t slot, uint32_t which,
+                        uint64_t* out_bytes) {
+  if (!h) return SLOT_KV_EINVAL;
+  if (!h->allocated()) return SLOT_KV_ENOTALLOC;
+  if (ssm_layer >= h->ssm.size() || which > 1 || !out_bytes) return SLOT_KV_EINVAL;
+  if (slot >= h->n_slots) return SLOT_KV_ERANGE;
+  const SsmLayer& S = h->ssm[ssm_layer];
+  *out_bytes = static_cast<uint64_t>(slot) * (which ? S.ssm_len : S.conv_len) * sizeof(float);
+  return SLOT_KV_OK;
+}
+
+int slot_conv_offset_bytes(const slot_kv* h, uint32_t ssm_layer, uint32_t slot,
+                           uint64_t* out_bytes) {
+  return state_offset(h, ssm_layer, slot, 0, out_bytes);
+}
+
+int slot_ssm_offset_bytes(const slot_kv* h, uint32_t ssm_layer, uint32_t slot,
+                          uint64_t* out_bytes) {
+  return state_offset(h, ssm_layer, slot, 1, out_bytes);
+}
+
+int slot_state_ptrs(const slot_kv* h, uint32_t ssm_layer, float** conv, float** ssm) {
+  if (!h) return SLOT_KV_EINVAL;
+  if (!h->allocated()) return SLOT_KV_ENOTALLOC;
+  if (ssm_layer >= h->ssm.size()) return SLOT_KV_EINVAL;
+  if (conv) *conv = h->ssm[ssm_layer].conv;
+  if (ssm) *ssm = h->ssm[ssm_layer].ssm;
+  return SLOT_KV_OK;
 }
 
 int slot_kv_check_batch(uint32_t n_slots, uint32_t slot_ctx, const uint32_t* positions,

@@ -146,4 +146,42 @@ int launch_decode(const AttnArgs& a, uint32_t head_dim, uint32_t group, uint32_t
 uint32_t resident_blocks(uint32_t head_dim, uint32_t group);
 bool decode_shape_supported(uint32_t head_dim, uint32_t group);
 
+// ---------------------------------------------------------------- per-slot SSM state
+// One [slot][len] f32 buffer of an ssm layer (its conv ring or its recurrent
+// state).  The reset kernel cuts each slot's region of a segment into tiles
+// of kResetTileUnits 16-byte units; `tile0` is the first tile of this segment
+// within one slot's tiles (segments in table order), so a slot's tiles are
+// [0, tiles_per_slot) and segment k holds [tile0_k, tile0_{k+1}).
+constexpr uint32_t kResetThreads = 256;
+constexpr uint32_t kResetUnitsPerThread = 4;
+constexpr uint32_t kResetTileUnits = kResetThreads * kResetUnitsPerThread;  // 16 KiB
+constexpr uint32_t kMaxResetPerLaunch = 256;
+
+struct StateSeg {
+  float* base;    // device buffer [n_slots][len]
+  uint64_t len;   // floats per slot
+  uint32_t tile0; // first tile of this segment in a slot's tile range
+  uint32_t pad;
+};
+
+// Tiles covering one slot's region of `len` floats wherever it starts: the
+// region spans at most ceil((len + 3) / 4) 16-byte units.
+inline uint64_t reset_tiles(uint64_t len) {
+  const uint64_t units = (len + 3) / 4 + (len ? 1 : 0);
+  return (units + kResetTileUnits - 1) / kResetTileUnits;
+}
+
+struct ResetArgs {
+  const StateSeg* segs;     // device table, n_seg entries
+  uint32_t n_seg;
+  uint32_t tiles_per_slot;  // tile0 of a one-past-the-end segment
+  uint32_t n;               // slots in this launch
+  uint32_t slots[kMaxResetPerLaunch];
+};
+
+// Zeroes the regions of a.slots[0..n) in every segment: n * tiles_per_slot
+// workgroups.  `before` / `after` (hipEvent_t or null) are recorded around the
+// kernel.  Returns a hipError_t value.
+int launch_state_reset(const ResetArgs& a, void* stream, void* before, void* after);
+
 }  // namespace slotkv

@@ -314,3 +314,57 @@ def verify_mid() -> VerifyWorkload:
 
 
 VERIFY_WORKLOADS = {"verify_mid": verify_mid}
+
+
+# ---------------------------------------------------------------- per-slot SSM state
+@dataclasses.dataclass
+class StateWorkload:
+    """Reset on admit of ``slots`` in a slot state of ``n_slots`` slots whose
+    ssm layers each hold a conv ring of conv_state_len floats and a recurrent
+    state of ssm_state_len floats per slot (no attention layers: their KV
+    needs no reset).  The state's contents before the reset are seeded
+    N(0, 1) (``state_seed`` drives torch generators on the device)."""
+    name: str
+    seed: int
+    n_slots: int
+    conv_state_len: list
+    ssm_state_len: list
+    slots: np.ndarray  # [n_reset] u32
+
+    @property
+    def state_seed(self) -> int:
+        return 1000 + self.seed
+
+    def bytes_per_slot(self) -> int:
+        return 4 * (sum(self.conv_state_len) + sum(self.ssm_state_len))
+
+    def write_bytes(self) -> int:
+        """Bytes a reset writes: every listed slot's conv ring and recurrent
+        state in every ssm layer, once per listed slot."""
+        return len(self.slots) * self.bytes_per_slot()
+
+
+def _build_state(name, seed, n_slots, conv_lens, ssm_lens, n_reset):
+    """Recipe: slots = a permutation of range(n_slots) cut to n_reset."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    slots = rng.permutation(n_slots)[:n_reset].astype(np.uint32)
+    return StateWorkload(name=name, seed=seed, n_slots=n_slots, conv_state_len=list(conv_lens),
+                         ssm_state_len=list(ssm_lens), slots=slots)
+
+
+def state_tiny() -> StateWorkload:
+    """Ragged sizes (not multiples of 4 floats; one state spanning several
+    16 KiB tiles) over few slots."""
+    return _build_state("state_tiny", 16, 6, [27, 8, 3], [4099, 10000, 7], 3)
+
+
+def state_admit() -> StateWorkload:
+    """8 admits into 64 slots of a 36-ssm-layer hybrid whose layers keep a
+    3-step conv ring over 8192 channels (24576 floats) and a 32-head
+    128 x 128 recurrent state (524288 floats) per slot: 2.2 MB per layer and
+    slot, 633 MB written per call.  The sizes are chosen here as typical of a
+    gated linear-attention layer; the pages give none."""
+    return _build_state("state_admit", 15, 64, [3 * 8192] * 36, [32 * 128 * 128] * 36, 8)
+
+
+STATE_WORKLOADS = {"state_tiny": state_tiny, "state_admit": state_admit}

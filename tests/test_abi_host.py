@@ -47,7 +47,12 @@ def test_unallocated_handle_paths():
         assert b.slot_kv_offset_bytes(h, 0, 0, 0)[0] == b.SLOT_KV_ENOTALLOC
         assert b.slot_kv_layer_ptrs(h, 0)[0] == b.SLOT_KV_ENOTALLOC
         # "Forward Cuda", reset on admit: a no-op when slot state is unallocated
-        assert b.slot_reset(h, 12345) == b.SLOT_KV_OK
+        assert b._lib.slot_reset(h, 12345, None) == b.SLOT_KV_OK
+        many = np.array([7, 9999], np.uint32)
+        assert b._lib.slot_reset_batch(h, many.ctypes.data_as(b._u32p), 2, None) == b.SLOT_KV_OK
+        assert b.slot_conv_offset_bytes(h, 0, 0)[0] == b.SLOT_KV_ENOTALLOC
+        assert b.slot_ssm_offset_bytes(h, 0, 0)[0] == b.SLOT_KV_ENOTALLOC
+        assert b.slot_state_ptrs(h, 0)[0] == b.SLOT_KV_ENOTALLOC
         ones = np.ones(64, np.float32)
         assert b.slot_kv_set_layer(h, 0, 4, 2, 64, ones, ones, ones[:32]) == b.SLOT_KV_ENOTALLOC
         assert b._lib.slot_decode_attn(h, 0, None, None, None, None, None, 0, None,
@@ -57,6 +62,20 @@ def test_unallocated_handle_paths():
         assert b._lib.slot_kv_alloc(h, 4, 0, dims.ctypes.data_as(b._u32p), 1) == b.SLOT_KV_EINVAL
         zero = np.array([0], np.uint32)
         assert b._lib.slot_kv_alloc(h, 4, 128, zero.ctypes.data_as(b._u32p), 1) == b.SLOT_KV_EINVAL
+        # slot_state_alloc: argument checks that precede any device call
+        u = lambda a: np.asarray(a, np.uint32).ctypes.data_as(b._u32p)
+        lens = np.array([8, 16], np.uint32)
+        p8 = lens.ctypes.data_as(b._u32p)
+        assert b._lib.slot_state_alloc(h, 4, 16, None, 0, None, None, 0) == b.SLOT_KV_EINVAL
+        assert b._lib.slot_state_alloc(h, 0, 16, None, 0, p8, p8, 1) == b.SLOT_KV_EINVAL
+        assert b._lib.slot_state_alloc(h, 4, 16, None, 1, p8, p8, 1) == b.SLOT_KV_EINVAL
+        assert b._lib.slot_state_alloc(h, 4, 16, None, 0, None, p8, 1) == b.SLOT_KV_EINVAL
+        assert b._lib.slot_state_alloc(h, 4, 16, None, 0, p8, None, 1) == b.SLOT_KV_EINVAL
+        assert b._lib.slot_state_alloc(h, 4, 16, None, 0, zero.ctypes.data_as(b._u32p), p8,
+                                       1) == b.SLOT_KV_EINVAL
+        big = np.array([0xFFFFFFFF] * 1100, np.uint32)  # one slot: 2^31 tiles and more
+        assert b._lib.slot_state_alloc(h, 4, 16, None, 0, big.ctypes.data_as(b._u32p),
+                                       big.ctypes.data_as(b._u32p), 1100) == b.SLOT_KV_EINVAL
     finally:
         b.slot_kv_destroy(h)
     b.slot_kv_destroy(None)  # NULL accepted
