@@ -79,7 +79,7 @@ int slot_kv_alloc(slot_kv *h, uint32_t n_slots, uint32_t slot_ctx,
  * lays them out, addresses them and zeroes them.  Idempotent: any previous
  * allocation of the handle (KV and state, and the layer configurations) is
  * freed first.  Errors: EINVAL (zero sizes, NULL arrays, one slot's state
- * above 2^31 tiles of 16 KiB), ENOMEM, EDEVICE. */
+ * above 2^31 tiles of 8 KiB), ENOMEM, EDEVICE. */
 int slot_state_alloc(slot_kv *h, uint32_t n_slots, uint32_t slot_ctx,
                      const uint32_t *kv_dims, uint32_t n_attn_layers,
                      const uint32_t *conv_state_len, const uint32_t *ssm_state_len,

@@ -153,8 +153,8 @@ bool decode_shape_supported(uint32_t head_dim, uint32_t group);
 // within one slot's tiles (segments in table order), so a slot's tiles are
 // [0, tiles_per_slot) and segment k holds [tile0_k, tile0_{k+1}).
 constexpr uint32_t kResetThreads = 256;
-constexpr uint32_t kResetUnitsPerThread = 4;
-constexpr uint32_t kResetTileUnits = kResetThreads * kResetUnitsPerThread;  // 16 KiB
+constexpr uint32_t kResetUnitsPerThread = 2;
+constexpr uint32_t kResetTileUnits = kResetThreads * kResetUnitsPerThread;  // 8 KiB
 constexpr uint32_t kMaxResetPerLaunch = 256;
 
 struct StateSeg {
