@@ -505,6 +505,36 @@ struct SeqRows {
 
 // Validated sequences of a call (no zero-length ones) -> launches of at most
 // kMaxSeqPerLaunch sequences, each sequence-major in the caller's buffers.
+// One launch of a prefill / verify: sequences [s0, s0 + n) of the call.
+struct PrefillLaunch {
+  size_t s0 = 0;
+  uint32_t n = 0, rows = 0;
+  uint32_t split_keys = 0;  // 0: tiled attention
+  uint32_t n_items = 0;     // split-K work items
+};
+
+// Keys per chunk of a split-K launch: the smallest power-of-two multiple of
+// kSplitMinKeys that keeps its work items within kMaxSplitItems (0 if none).
+uint32_t plan_split(const std::vector<SeqRows>& seqs, size_t s0, uint32_t n, uint32_t G,
+                    uint32_t n_kv_heads, uint32_t* n_items) {
+  uint64_t max_keys = 0;
+  for (size_t i = s0; i < s0 + n; ++i)
+    max_keys = std::max<uint64_t>(max_keys, uint64_t(seqs[i].pos0) + seqs[i].len);
+  for (uint64_t ck = slotkv::kSplitMinKeys;; ck *= 2) {
+    uint64_t items = 0;
+    for (size_t i = s0; i < s0 + n; ++i) {
+      const uint64_t tiles = (uint64_t(seqs[i].len) * G + 15) / 16;
+      const uint64_t chunks = (uint64_t(seqs[i].pos0) + seqs[i].len + ck - 1) / ck;
+      items += tiles * chunks * n_kv_heads;
+    }
+    if (items <= slotkv::kMaxSplitItems) {
+      *n_items = static_cast<uint32_t>(items);
+      return static_cast<uint32_t>(ck);
+    }
+    if (ck >= max_keys) return 0;
+  }
+}
+
 int run_prefill(slot_kv* h, uint32_t layer, const float* q, const float* k_new,
                 const float* v_new, float* out, const std::vector<SeqRows>& seqs, void* stream) {
   LayerState& L = h->layers[layer];
@@ -512,14 +542,31 @@ int run_prefill(slot_kv* h, uint32_t layer, const float* q, const float* k_new,
   if (!slotkv::decode_shape_supported(L.head_dim, G)) return SLOT_KV_EINVAL;
   const size_t D = L.head_dim;
   const uint32_t M = slotkv::kMaxSeqPerLaunch;
-  // scratch for the rotated queries of the largest launch, before any enqueue
-  size_t max_rows = 0;
+  // Sequences with few query rows per kv head (a verify of k rows, a short
+  // prefill) run the split-K attention; others the tiled one, whose
+  // workgroups share each K/V block between four tiles.
+  bool split = true;
+  for (const SeqRows& r : seqs) split = split && uint64_t(r.len) * G <= slotkv::kSplitMaxRows;
+  // plan every launch, then size the scratch (rotated queries, then the
+  // split-K partials) for the largest one, before any enqueue
+  std::vector<PrefillLaunch> plan;
+  size_t scratch = 0;
   for (size_t s0 = 0; s0 < seqs.size(); s0 += M) {
-    size_t rows = 0;
-    for (size_t i = s0; i < std::min(seqs.size(), s0 + M); ++i) rows += seqs[i].len;
-    max_rows = std::max(max_rows, rows);
+    PrefillLaunch pl;
+    pl.s0 = s0;
+    pl.n = static_cast<uint32_t>(std::min<size_t>(seqs.size() - s0, M));
+    for (size_t i = s0; i < s0 + pl.n; ++i) pl.rows += seqs[i].len;
+    if (split) pl.split_keys = plan_split(seqs, s0, pl.n, G, L.n_kv_heads, &pl.n_items);
+    plan.push_back(pl);
   }
-  int rc = ensure_partials(h, max_rows * L.n_heads * D);
+  // one call takes one kernel: split-K only if every launch can
+  for (const PrefillLaunch& pl : plan) split = split && pl.split_keys != 0;
+  for (PrefillLaunch& pl : plan) {
+    if (!split) pl.split_keys = pl.n_items = 0;
+    scratch = std::max(scratch, size_t(pl.rows) * L.n_heads * D +
+                                    size_t(pl.n_items) * 16 * (D + 2));
+  }
+  int rc = ensure_partials(h, scratch);
   if (rc) return rc;
 
   slotkv::PrefillArgs& a = h->pargs;
@@ -540,34 +587,52 @@ int run_prefill(slot_kv* h, uint32_t layer, const float* q, const float* k_new,
   p.qk_scale_log2 = L.scale * 1.4426950408889634f;
   p.flags = L.flags;
   const size_t qd = static_cast<size_t>(L.n_heads) * D;
-  for (size_t s0 = 0; s0 < seqs.size(); s0 += M) {
-    const uint32_t n = static_cast<uint32_t>(std::min<size_t>(seqs.size() - s0, M));
-    const uint32_t first_row = seqs[s0].row;
+  for (const PrefillLaunch& pl : plan) {
+    const uint32_t n = pl.n;
+    const uint32_t first_row = seqs[pl.s0].row;
     uint32_t rows = 0;
-    std::vector<uint64_t> work(n);
     for (uint32_t i = 0; i < n; ++i) {
-      const SeqRows& r = seqs[s0 + i];
+      const SeqRows& r = seqs[pl.s0 + i];
       a.s.slot[i] = r.slot;
       a.s.pos0[i] = r.pos0;
       a.s.len[i] = r.len;
       a.s.row_off[i] = rows;
       rows += r.len;
-      a.s.by_work[i] = i;
-      work[i] = static_cast<uint64_t>(r.len) * (2ull * r.pos0 + r.len);  // ~ keys scored
     }
     a.s.row_off[n] = rows;
-    std::stable_sort(a.s.by_work, a.s.by_work + n,
-                     [&](uint32_t x, uint32_t y) { return work[x] > work[y]; });
-    uint32_t groups = 0;
-    for (uint32_t k = 0; k < n; ++k) {
-      a.s.grp_off[k] = groups;
-      const uint32_t tiles = (a.s.len[a.s.by_work[k]] * G + 15) / 16;
-      groups += (tiles * 16 + slotkv::kPrefillRowsPerGroup - 1) / slotkv::kPrefillRowsPerGroup;
+    if (split) {
+      uint32_t items = 0;
+      for (uint32_t i = 0; i < n; ++i) {
+        a.s.item_off[i] = items;
+        a.s.n_chunks[i] = (a.s.pos0[i] + a.s.len[i] + pl.split_keys - 1) / pl.split_keys;
+        items += (a.s.len[i] * G + 15) / 16 * a.s.n_chunks[i] * L.n_kv_heads;
+      }
+      a.s.item_off[n] = items;
+      p.part = h->part + size_t(pl.rows) * qd;
+      p.n_items = items;
+      p.split_keys = pl.split_keys;
+      p.n_groups = 0;
+    } else {
+      std::vector<uint64_t> work(n);
+      for (uint32_t i = 0; i < n; ++i) {
+        a.s.by_work[i] = i;
+        work[i] = static_cast<uint64_t>(a.s.len[i]) * (2ull * a.s.pos0[i] + a.s.len[i]);
+      }
+      std::stable_sort(a.s.by_work, a.s.by_work + n,
+                       [&](uint32_t x, uint32_t y) { return work[x] > work[y]; });
+      uint32_t groups = 0;
+      for (uint32_t k = 0; k < n; ++k) {
+        a.s.grp_off[k] = groups;
+        const uint32_t tiles = (a.s.len[a.s.by_work[k]] * G + 15) / 16;
+        groups += (tiles * 16 + slotkv::kPrefillRowsPerGroup - 1) / slotkv::kPrefillRowsPerGroup;
+      }
+      a.s.grp_off[n] = groups;
+      p.part = nullptr;
+      p.n_items = p.split_keys = 0;
+      p.n_groups = groups;
     }
-    a.s.grp_off[n] = groups;
     p.n_seq = n;
     p.n_rows = rows;
-    p.n_groups = groups;
     p.q = q + first_row * qd;
     p.k_new = k_new + static_cast<size_t>(first_row) * L.kv_dim;
     p.v_new = v_new + static_cast<size_t>(first_row) * L.kv_dim;
@@ -575,7 +640,7 @@ int run_prefill(slot_kv* h, uint32_t layer, const float* q, const float* k_new,
     hipEvent_t e0 = nullptr, e1 = nullptr;
     rc = prof_pair(h, &e0, &e1);
     if (rc) return rc;
-    if (slotkv::launch_prefill(a, L.head_dim, G, stream, e0, e1) != hipSuccess)
+    if (slotkv::launch_prefill(a, L.head_dim, G, split, stream, e0, e1) != hipSuccess)
       return SLOT_KV_EDEVICE;
   }
   return SLOT_KV_OK;

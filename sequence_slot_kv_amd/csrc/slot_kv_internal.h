@@ -80,6 +80,8 @@ struct PrefillParams {
   const float* k_new;      // [n_rows][kv_dim]
   const float* v_new;      // [n_rows][kv_dim]
   float* qs;               // [n_rows][n_heads][D] rotated queries times scale*log2(e) (scratch)
+  float* part;             // split-K partials (scratch): acc [n_items][16][D], then
+                           // (max, sum) [n_items][16][2]
   float* out;              // [n_rows][n_heads*D]
   const float* q_norm_w;   // [D]
   const float* k_norm_w;   // [D]
@@ -92,6 +94,8 @@ struct PrefillParams {
   uint32_t n_seq;          // sequences of this launch
   uint32_t n_rows;         // token rows of this launch
   uint32_t n_groups;       // attention workgroups per kv head (all sequences)
+  uint32_t n_items;        // split-K: work items (one wave each) of this launch
+  uint32_t split_keys;     // split-K: keys per chunk (a multiple of 16)
   float eps;
   float qk_scale_log2;     // scale * log2(e)
   uint32_t flags;          // SLOT_KV_FLAG_*
@@ -102,8 +106,16 @@ struct PrefillSeqs {
   uint32_t pos0[kMaxSeqPerLaunch];
   uint32_t len[kMaxSeqPerLaunch];
   uint32_t row_off[kMaxSeqPerLaunch + 1];  // first row of each sequence (and the total)
-  uint32_t by_work[kMaxSeqPerLaunch];      // the sequences, most attention work first
-  uint32_t grp_off[kMaxSeqPerLaunch + 1];  // first workgroup of by_work[k] (per kv head)
+  // The attention of a launch runs one of two kernels, and each reads its
+  // own view of the last two tables.
+  union {
+    uint32_t by_work[kMaxSeqPerLaunch];    // tiled: the sequences, most attention work first
+    uint32_t n_chunks[kMaxSeqPerLaunch];   // split-K: key chunks of each sequence
+  };
+  union {
+    uint32_t grp_off[kMaxSeqPerLaunch + 1];   // tiled: first workgroup of by_work[k] (per kv head)
+    uint32_t item_off[kMaxSeqPerLaunch + 1];  // split-K: first work item of each sequence
+  };
 };
 
 struct PrefillArgs {
@@ -116,11 +128,21 @@ static_assert(sizeof(PrefillArgs) < 4000, "kernel arguments must stay below 4 Ki
 // Query rows per attention workgroup of a prefill (4 waves x 16 rows).
 constexpr uint32_t kPrefillRowsPerGroup = 64;
 
+// Split-K attention (sequences with at most kSplitMaxRows query rows per kv
+// head, as in a multi-row verify): one wave per work item (sequence, kv
+// head, key chunk, 16-row tile), items of one sequence ordered
+//   item_off[i] + (j * n_chunks[i] + chunk) * n_tiles + tile,
+// n_tiles = ceil(len * G / 16); a merge kernel then combines the chunks.
+constexpr uint32_t kSplitMaxRows = 64;
+constexpr uint32_t kSplitMinKeys = 256;       // smallest chunk
+constexpr uint32_t kMaxSplitItems = 1u << 14; // per launch (bounds the partials)
+
 // Launches of a prefill / verify: norm + RoPE + KV write, then the
-// attention.  `before_attn` / `after_attn` (hipEvent_t or null) are recorded
-// around the attention kernel.  Returns a hipError_t value.
-int launch_prefill(const PrefillArgs& a, uint32_t head_dim, uint32_t group, void* stream,
-                   void* before_attn, void* after_attn);
+// attention (tiled, or split-K and merge when `split`).  `before_attn` /
+// `after_attn` (hipEvent_t or null) are recorded around the attention
+// kernels.  Returns a hipError_t value.
+int launch_prefill(const PrefillArgs& a, uint32_t head_dim, uint32_t group, bool split,
+                   void* stream, void* before_attn, void* after_attn);
 
 // Validation of one batch (no device access).  Returns a SLOT_KV_* status.
 int check_batch(uint32_t n_slots, uint32_t slot_ctx, const uint32_t* positions,

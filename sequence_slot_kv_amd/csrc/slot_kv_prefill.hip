@@ -319,6 +319,199 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) prefill_attn_kernel(const 
           f4{o[u][r], o[u + 1][r], o[u + 2][r], o[u + 3][r]} * rs;
 }
 
+// Split-K attention for sequences with few query rows per kv head (a verify
+// of k rows, a short prefill).  Every wave is one work item: a 16-row tile of
+// one sequence and kv head j against one chunk of split_keys keys, loaded
+// straight from the cache into registers (no other wave needs them), with the
+// next 16-key block in flight while the current one is multiplied.  The
+// MFMA forms are those of prefill_attn_kernel, except that the head_dim
+// order of the score product is permuted so that each K load instruction
+// reads 64 contiguous bytes per row: lane (c, g) multiplies
+// d = 16v + 4g + e at MFMA (v, e), for K row c and for its query row c.
+// A wave writes its unnormalised partial (per row: running max m in log2
+// units, sum l, and acc[D]); split_merge_kernel combines them.
+template <int D, int G>
+__global__ void __launch_bounds__(kWave * kAttnWaves) split_attn_kernel(const PrefillArgs a) {
+  constexpr int NK = D / 16;   // K float4 per lane per block
+  constexpr int TD = D / 16;   // output tiles of 16 head_dim values
+  constexpr int DQ = D / 4;
+  constexpr int NV = TD / 4;   // V float4 per lane per key of a lane group
+  if (a.magic != kArgsMagic) return;  // argument block not delivered whole
+  const PrefillParams& p = a.p;
+  const uint32_t lane = threadIdx.x % kWave;
+  const uint32_t g = lane / 16, c = lane % 16;
+  const uint32_t item = blockIdx.x * kAttnWaves + threadIdx.x / kWave;
+  if (item >= p.n_items) return;  // wave-uniform
+  uint32_t lo = 0, hi = p.n_seq;  // the sequence: last i with item_off[i] <= item
+  while (hi - lo > 1) {
+    const uint32_t mid = (lo + hi) / 2;
+    if (a.s.item_off[mid] <= item) lo = mid; else hi = mid;
+  }
+  const uint32_t sq = lo;
+  const uint32_t T = a.s.len[sq], pos0 = a.s.pos0[sq], row0 = a.s.row_off[sq];
+  const uint32_t n_tiles = (T * G + 15) / 16;
+  const uint32_t idx = item - a.s.item_off[sq];
+  const uint32_t tile = idx % n_tiles;
+  const uint32_t jc = idx / n_tiles;
+  const uint32_t chunk = jc % a.s.n_chunks[sq];
+  const uint32_t j = jc / a.s.n_chunks[sq];
+  const uint32_t R = tile * 16 + c;
+  const uint32_t t = R / G, h = j * G + R % G;
+  const uint32_t tq = t < T ? t : T - 1;  // rows past the last token compute on it, unused
+  const uint32_t row_pos = pos0 + tq;
+  const uint32_t tile_keys = pos0 + min((tile * 16 + 15) / G, T - 1) + 1;
+  const uint32_t k0 = chunk * p.split_keys;
+  if (k0 >= tile_keys) return;  // past this tile's keys: the merge does not read it
+  const uint32_t k1 = min(k0 + p.split_keys, tile_keys);
+
+  float qv[DQ];
+  {
+    const float* qsrc = p.qs + (static_cast<size_t>(row0 + tq) * p.n_heads + h) * D + 4 * g;
+#pragma unroll
+    for (int v = 0; v < NK; ++v) {
+      const f4 x = *reinterpret_cast<const f4*>(qsrc + 16 * v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qv[4 * v + e] = x[e];
+    }
+  }
+  const uint64_t slot_base = a.s.slot[sq] * p.slot_stride;
+  const float* kbase = p.k_cache + slot_base + j * D;
+  const float* vbase = p.v_cache + slot_base + j * D;
+  // block kb: K row kb + c, V rows kb + 4g + m; keys past the chunk re-read
+  // its last key and are masked
+  f4 nk[NK], nv[4][NV];
+  auto load = [&](uint32_t kb) {
+    const float* kr = kbase + static_cast<size_t>(min(kb + c, k1 - 1)) * p.kv_dim + 4 * g;
+#pragma unroll
+    for (int v = 0; v < NK; ++v) nk[v] = *reinterpret_cast<const f4*>(kr + 16 * v);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const float* vr = vbase + static_cast<size_t>(min(kb + 4 * g + m, k1 - 1)) * p.kv_dim + TD * c;
+#pragma unroll
+      for (int x = 0; x < NV; ++x) nv[m][x] = *reinterpret_cast<const f4*>(vr + 4 * x);
+    }
+  };
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f4 o[TD];
+#pragma unroll
+  for (int u = 0; u < TD; ++u) o[u] = f4{0.f, 0.f, 0.f, 0.f};
+  load(k0);
+  for (uint32_t kb = k0; kb < k1; kb += 16) {  // wave-uniform
+    f4 ck[NK], cv[4][NV];
+#pragma unroll
+    for (int v = 0; v < NK; ++v) ck[v] = nk[v];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int x = 0; x < NV; ++x) cv[m][x] = nv[m][x];
+    if (kb + 16 < k1) load(kb + 16);
+    f4 s = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int v = 0; v < NK; ++v)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        s = __builtin_amdgcn_mfma_f32_16x16x4f32(ck[v][e], qv[4 * v + e], s, 0, 0, 0);
+    // key kb + 4g + r counts iff it is in the chunk and not after the row
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t key = kb + 4 * g + r;
+      if (key >= k1 || key > row_pos) s[r] = -INFINITY;
+    }
+    float mb = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mb = fmaxf(mb, __shfl_xor(mb, 16));
+    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    const float m_new = fmaxf(m_run, mb);
+    // a row may have no key yet in this chunk: keep everything at zero
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float corr = fast_exp2(m_run - m_use);
+    f4 pr;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(s[r] - m_use);
+    l_run = l_run * corr + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+#pragma unroll
+    for (int u = 0; u < TD; ++u) o[u] *= corr;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int x = 0; x < NV; ++x)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[4 * x + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(cv[m][x][e], pr[m], o[4 * x + e], 0, 0, 0);
+    m_run = m_new;
+  }
+  float L = l_run + __shfl_xor(l_run, 16);
+  L += __shfl_xor(L, 32);
+  float* acc = p.part + (static_cast<size_t>(item) * 16 + c) * D + DQ * g;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int u = 0; u < TD; u += 4)
+      *reinterpret_cast<f4*>(acc + TD * r + u) = f4{o[u][r], o[u + 1][r], o[u + 2][r], o[u + 3][r]};
+  if (g == 0) {
+    float* ml = p.part + static_cast<size_t>(p.n_items) * 16 * D + (static_cast<size_t>(item) * 16 + c) * 2;
+    ml[0] = m_run;
+    ml[1] = L;
+  }
+}
+
+// One wave per (row, query head) of the launch: combines the row's chunk
+// partials (max over chunks, each rescaled by 2^(m_c - max)), adds the sink
+// and writes the normalised output row.
+template <int D, int G>
+__global__ void __launch_bounds__(kWave * kAttnWaves) split_merge_kernel(const PrefillArgs a) {
+  constexpr int EPL = D / kWave;
+  if (a.magic != kArgsMagic) return;
+  const PrefillParams& p = a.p;
+  const uint32_t lane = threadIdx.x % kWave;
+  const uint32_t wid = blockIdx.x * kAttnWaves + threadIdx.x / kWave;
+  if (wid >= p.n_rows * p.n_heads) return;  // wave-uniform
+  const uint32_t row = wid / p.n_heads, h = wid - row * p.n_heads;
+  const uint32_t sq = seq_of_row(a, row);
+  const uint32_t T = a.s.len[sq], pos0 = a.s.pos0[sq];
+  const uint32_t t = row - a.s.row_off[sq];
+  const uint32_t j = h / G, R = t * G + h % G, tile = R / 16, c = R % 16;
+  const uint32_t n_tiles = (T * G + 15) / 16;
+  const uint32_t tile_keys = pos0 + min((tile * 16 + 15) / G, T - 1) + 1;
+  const uint32_t nck = (tile_keys + p.split_keys - 1) / p.split_keys;
+  const uint32_t first = a.s.item_off[sq] + j * a.s.n_chunks[sq] * n_tiles + tile;
+  const float* ml = p.part + static_cast<size_t>(p.n_items) * 16 * D;
+  float mx = -INFINITY;  // finite after chunk 0, which holds key 0
+  for (uint32_t k = 0; k < nck; ++k) mx = fmaxf(mx, ml[(static_cast<size_t>(first + k * n_tiles) * 16 + c) * 2]);
+  float sk = -INFINITY;
+  if (p.sinks) sk = p.sinks[h] * kLog2e;
+  mx = fmaxf(mx, sk);
+  float L = sk == -INFINITY ? 0.f : fast_exp2(sk - mx);
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (uint32_t k = 0; k < nck; ++k) {
+    const size_t it = static_cast<size_t>(first + k * n_tiles) * 16 + c;
+    const float m = ml[it * 2];
+    const float wgt = m == -INFINITY ? 0.f : fast_exp2(m - mx);
+    L += ml[it * 2 + 1] * wgt;
+    const float* src = p.part + it * D + lane * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] += src[e] * wgt;
+  }
+  const float rl = 1.f / L;
+  float* dst = p.out + (static_cast<size_t>(row) * p.n_heads + h) * D + lane * EPL;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) dst[e] = acc[e] * rl;
+}
+
+template <int D, int G>
+hipError_t launch_split(const PrefillArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((split_attn_kernel<D, G>), dim3((a.p.n_items + kAttnWaves - 1) / kAttnWaves),
+                     dim3(kWave * kAttnWaves), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const uint32_t waves = a.p.n_rows * a.p.n_heads;
+  hipLaunchKernelGGL((split_merge_kernel<D, G>), dim3((waves + kAttnWaves - 1) / kAttnWaves),
+                     dim3(kWave * kAttnWaves), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int D, int G>
 hipError_t launch_attn(const PrefillArgs& a, hipStream_t s) {
   const uint32_t blocks = a.p.n_groups * a.p.n_kv_heads;
@@ -327,17 +520,17 @@ hipError_t launch_attn(const PrefillArgs& a, hipStream_t s) {
 }
 
 template <int D>
-hipError_t launch_d(const PrefillArgs& a, uint32_t G, hipStream_t s, hipEvent_t before,
-                    hipEvent_t after) {
+hipError_t launch_d(const PrefillArgs& a, uint32_t G, bool split, hipStream_t s,
+                    hipEvent_t before, hipEvent_t after) {
   hipLaunchKernelGGL((prefill_prep_kernel<D>), dim3(a.p.n_rows), dim3(kWave * kPrepWaves), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && before) e = hipEventRecord(before, s);
   if (e != hipSuccess) return e;
   switch (G) {
-    case 1: e = launch_attn<D, 1>(a, s); break;
-    case 2: e = launch_attn<D, 2>(a, s); break;
-    case 4: e = launch_attn<D, 4>(a, s); break;
-    case 8: e = launch_attn<D, 8>(a, s); break;
+    case 1: e = split ? launch_split<D, 1>(a, s) : launch_attn<D, 1>(a, s); break;
+    case 2: e = split ? launch_split<D, 2>(a, s) : launch_attn<D, 2>(a, s); break;
+    case 4: e = split ? launch_split<D, 4>(a, s) : launch_attn<D, 4>(a, s); break;
+    case 8: e = split ? launch_split<D, 8>(a, s) : launch_attn<D, 8>(a, s); break;
     default: return hipErrorInvalidValue;
   }
   if (e == hipSuccess && after) e = hipEventRecord(after, s);
@@ -346,15 +539,15 @@ hipError_t launch_d(const PrefillArgs& a, uint32_t G, hipStream_t s, hipEvent_t 
 
 }  // namespace
 
-int launch_prefill(const PrefillArgs& a, uint32_t head_dim, uint32_t group, void* stream,
-                   void* before_attn, void* after_attn) {
+int launch_prefill(const PrefillArgs& a, uint32_t head_dim, uint32_t group, bool split,
+                   void* stream, void* before_attn, void* after_attn) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t b = static_cast<hipEvent_t>(before_attn);
   hipEvent_t e = static_cast<hipEvent_t>(after_attn);
   switch (head_dim) {
-    case 64: return launch_d<64>(a, group, s, b, e);
-    case 128: return launch_d<128>(a, group, s, b, e);
-    case 256: return launch_d<256>(a, group, s, b, e);
+    case 64: return launch_d<64>(a, group, split, s, b, e);
+    case 128: return launch_d<128>(a, group, split, s, b, e);
+    case 256: return launch_d<256>(a, group, split, s, b, e);
     default: return hipErrorInvalidValue;
   }
 }
