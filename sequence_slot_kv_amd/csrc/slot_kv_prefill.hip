@@ -457,7 +457,9 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) split_attn_kernel(const Pr
 
 // One wave per (row, query head) of the launch: combines the row's chunk
 // partials (max over chunks, each rescaled by 2^(m_c - max)), adds the sink
-// and writes the normalised output row.
+// and writes the normalised output row.  Lane k reads the (max, sum) of
+// chunk k (64 chunks per pass), so the weights take one round trip to
+// memory; the accumulator slices of the chunks are then read four at a time.
 template <int D, int G>
 __global__ void __launch_bounds__(kWave * kAttnWaves) split_merge_kernel(const PrefillArgs a) {
   constexpr int EPL = D / kWave;
@@ -476,24 +478,51 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) split_merge_kernel(const P
   const uint32_t nck = (tile_keys + p.split_keys - 1) / p.split_keys;
   const uint32_t first = a.s.item_off[sq] + j * a.s.n_chunks[sq] * n_tiles + tile;
   const float* ml = p.part + static_cast<size_t>(p.n_items) * 16 * D;
-  float mx = -INFINITY;  // finite after chunk 0, which holds key 0
-  for (uint32_t k = 0; k < nck; ++k) mx = fmaxf(mx, ml[(static_cast<size_t>(first + k * n_tiles) * 16 + c) * 2]);
-  float sk = -INFINITY;
-  if (p.sinks) sk = p.sinks[h] * kLog2e;
+  auto at = [&](uint32_t k) { return static_cast<size_t>(first + k * n_tiles) * 16 + c; };
+  // the maximum over the chunks (finite: chunk 0 holds key 0) and the sink
+  float mx = -INFINITY;
+  for (uint32_t k0 = 0; k0 < nck; k0 += kWave)
+    if (k0 + lane < nck) mx = fmaxf(mx, ml[at(k0 + lane) * 2]);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  const float sk = p.sinks ? p.sinks[h] * kLog2e : -INFINITY;
   mx = fmaxf(mx, sk);
-  float L = sk == -INFINITY ? 0.f : fast_exp2(sk - mx);
+  float L = 0.f;
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  for (uint32_t k = 0; k < nck; ++k) {
-    const size_t it = static_cast<size_t>(first + k * n_tiles) * 16 + c;
-    const float m = ml[it * 2];
-    const float wgt = m == -INFINITY ? 0.f : fast_exp2(m - mx);
-    L += ml[it * 2 + 1] * wgt;
-    const float* src = p.part + it * D + lane * EPL;
+  for (uint32_t k0 = 0; k0 < nck; k0 += kWave) {
+    // lane k: chunk k0 + k's weight (0 for a chunk with no key of this row)
+    float wgt = 0.f;
+    if (k0 + lane < nck) {
+      const float m = ml[at(k0 + lane) * 2];
+      wgt = m == -INFINITY ? 0.f : fast_exp2(m - mx);
+      L += ml[at(k0 + lane) * 2 + 1] * wgt;
+    }
+    const uint32_t n = min(nck - k0, static_cast<uint32_t>(kWave));
+    uint32_t k = 0;
+    for (; k + 4 <= n; k += 4) {
+      float x[4][EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] += src[e] * wgt;
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) x[q][e] = p.part[at(k0 + k + q) * D + lane * EPL + e];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float wq = __shfl(wgt, k + q);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] += x[q][e] * wq;
+      }
+    }
+    for (; k < n; ++k) {
+      const float wq = __shfl(wgt, k);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] += p.part[at(k0 + k) * D + lane * EPL + e] * wq;
+    }
   }
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) L += __shfl_xor(L, off);
+  if (sk != -INFINITY) L += fast_exp2(sk - mx);
   const float rl = 1.f / L;
   float* dst = p.out + (static_cast<size_t>(row) * p.n_heads + h) * D + lane * EPL;
 #pragma unroll
