@@ -131,8 +131,9 @@ constexpr uint32_t kPrefillRowsPerGroup = 64;
 // Split-K attention (sequences with at most kSplitMaxRows query rows per kv
 // head, as in a multi-row verify): one wave per work item (sequence, kv
 // head, key chunk, 16-row tile), items of one sequence ordered
-//   item_off[i] + (j * n_chunks[i] + chunk) * n_tiles + tile,
-// n_tiles = ceil(len * G / 16); a merge kernel then combines the chunks.
+//   item_off[i] + (chunk * n_kv_heads + j) * n_tiles + tile,
+// n_tiles = ceil(len * G / 16), so that neighbouring waves read the kv heads
+// of the same key rows; a merge kernel then combines the chunks.
 constexpr uint32_t kSplitMaxRows = 64;
 constexpr uint32_t kSplitMinKeys = 256;       // smallest chunk
 constexpr uint32_t kMaxSplitItems = 1u << 14; // per launch (bounds the partials)

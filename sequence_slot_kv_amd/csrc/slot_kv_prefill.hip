@@ -331,7 +331,8 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) prefill_attn_kernel(const 
 // A wave writes its unnormalised partial (per row: running max m in log2
 // units, sum l, and acc[D]); split_merge_kernel combines them.
 template <int D, int G>
-__global__ void __launch_bounds__(kWave * kAttnWaves) split_attn_kernel(const PrefillArgs a) {
+__global__ void __launch_bounds__(kWave * kAttnWaves) __attribute__((amdgpu_waves_per_eu(2)))
+split_attn_kernel(const PrefillArgs a) {
   constexpr int NK = D / 16;   // K float4 per lane per block
   constexpr int TD = D / 16;   // output tiles of 16 head_dim values
   constexpr int DQ = D / 4;
@@ -340,8 +341,11 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) split_attn_kernel(const Pr
   const PrefillParams& p = a.p;
   const uint32_t lane = threadIdx.x % kWave;
   const uint32_t g = lane / 16, c = lane % 16;
-  const uint32_t item = blockIdx.x * kAttnWaves + threadIdx.x / kWave;
-  if (item >= p.n_items) return;  // wave-uniform
+  // the item is the same for the whole wave: keep it (and all that follows
+  // from it) in scalar registers, so that the key loop is uniform
+  const uint32_t item =
+      __builtin_amdgcn_readfirstlane(blockIdx.x * kAttnWaves + threadIdx.x / kWave);
+  if (item >= p.n_items) return;
   uint32_t lo = 0, hi = p.n_seq;  // the sequence: last i with item_off[i] <= item
   while (hi - lo > 1) {
     const uint32_t mid = (lo + hi) / 2;
@@ -353,16 +357,17 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) split_attn_kernel(const Pr
   const uint32_t idx = item - a.s.item_off[sq];
   const uint32_t tile = idx % n_tiles;
   const uint32_t jc = idx / n_tiles;
-  const uint32_t chunk = jc % a.s.n_chunks[sq];
-  const uint32_t j = jc / a.s.n_chunks[sq];
-  const uint32_t R = tile * 16 + c;
-  const uint32_t t = R / G, h = j * G + R % G;
-  const uint32_t tq = t < T ? t : T - 1;  // rows past the last token compute on it, unused
-  const uint32_t row_pos = pos0 + tq;
+  const uint32_t j = jc % p.n_kv_heads;
+  const uint32_t chunk = jc / p.n_kv_heads;
   const uint32_t tile_keys = pos0 + min((tile * 16 + 15) / G, T - 1) + 1;
   const uint32_t k0 = chunk * p.split_keys;
   if (k0 >= tile_keys) return;  // past this tile's keys: the merge does not read it
   const uint32_t k1 = min(k0 + p.split_keys, tile_keys);
+  const uint32_t n_blk = (k1 - k0 + 15) / 16;
+  const uint32_t R = tile * 16 + c;
+  const uint32_t t = R / G, h = j * G + R % G;
+  const uint32_t tq = t < T ? t : T - 1;  // rows past the last token compute on it, unused
+  const uint32_t row_pos = pos0 + tq;
 
   float qv[DQ];
   {
@@ -377,18 +382,20 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) split_attn_kernel(const Pr
   const uint64_t slot_base = a.s.slot[sq] * p.slot_stride;
   const float* kbase = p.k_cache + slot_base + j * D;
   const float* vbase = p.v_cache + slot_base + j * D;
-  // block kb: K row kb + c, V rows kb + 4g + m; keys past the chunk re-read
-  // its last key and are masked
-  f4 nk[NK], nv[4][NV];
-  auto load = [&](uint32_t kb) {
-    const float* kr = kbase + static_cast<size_t>(min(kb + c, k1 - 1)) * p.kv_dim + 4 * g;
+  // Block b of the chunk: K row k0 + 16b + c, V rows k0 + 16b + 4g + m.
+  // Loads are issued unconditionally, so that the number in flight is known
+  // where a block is consumed: rows past the chunk (a partial last block, or
+  // the block after the last) re-read its last key, which the mask drops.
+  auto load = [&](f4 (&kr)[NK], f4 (&vr)[4][NV], uint32_t b) {
+    const uint32_t kb = k0 + 16 * b;
+    const float* kp = kbase + static_cast<size_t>(min(kb + c, k1 - 1)) * p.kv_dim + 4 * g;
 #pragma unroll
-    for (int v = 0; v < NK; ++v) nk[v] = *reinterpret_cast<const f4*>(kr + 16 * v);
+    for (int v = 0; v < NK; ++v) kr[v] = *reinterpret_cast<const f4*>(kp + 16 * v);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const float* vr = vbase + static_cast<size_t>(min(kb + 4 * g + m, k1 - 1)) * p.kv_dim + TD * c;
+      const float* vp = vbase + static_cast<size_t>(min(kb + 4 * g + m, k1 - 1)) * p.kv_dim + TD * c;
 #pragma unroll
-      for (int x = 0; x < NV; ++x) nv[m][x] = *reinterpret_cast<const f4*>(vr + 4 * x);
+      for (int x = 0; x < NV; ++x) vr[m][x] = *reinterpret_cast<const f4*>(vp + 4 * x);
     }
   };
 
@@ -396,22 +403,14 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) split_attn_kernel(const Pr
   f4 o[TD];
 #pragma unroll
   for (int u = 0; u < TD; ++u) o[u] = f4{0.f, 0.f, 0.f, 0.f};
-  load(k0);
-  for (uint32_t kb = k0; kb < k1; kb += 16) {  // wave-uniform
-    f4 ck[NK], cv[4][NV];
-#pragma unroll
-    for (int v = 0; v < NK; ++v) ck[v] = nk[v];
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int x = 0; x < NV; ++x) cv[m][x] = nv[m][x];
-    if (kb + 16 < k1) load(kb + 16);
+  auto compute = [&](const f4 (&kr)[NK], const f4 (&vr)[4][NV], uint32_t b) {
+    const uint32_t kb = k0 + 16 * b;
     f4 s = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int v = 0; v < NK; ++v)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        s = __builtin_amdgcn_mfma_f32_16x16x4f32(ck[v][e], qv[4 * v + e], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[v][e], qv[4 * v + e], s, 0, 0, 0);
     // key kb + 4g + r counts iff it is in the chunk and not after the row
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -437,9 +436,25 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) split_attn_kernel(const Pr
       for (int x = 0; x < NV; ++x)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          o[4 * x + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(cv[m][x][e], pr[m], o[4 * x + e], 0, 0, 0);
+          o[4 * x + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[m][x][e], pr[m], o[4 * x + e], 0, 0, 0);
     m_run = m_new;
+  };
+
+  // two register sets, A for even blocks and B for odd ones: the next
+  // block's loads are in flight while the current one is multiplied
+  f4 ka[NK], va[4][NV], kb_[NK], vb[4][NV];
+  load(ka, va, 0);
+  uint32_t b = 0;
+  for (; b + 2 <= n_blk; b += 2) {
+    load(kb_, vb, b + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(ka, va, b);
+    load(ka, va, b + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(kb_, vb, b + 1);
   }
+  if (b < n_blk) compute(ka, va, b);
+
   float L = l_run + __shfl_xor(l_run, 16);
   L += __shfl_xor(L, 32);
   float* acc = p.part + (static_cast<size_t>(item) * 16 + c) * D + DQ * g;
@@ -476,9 +491,10 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) split_merge_kernel(const P
   const uint32_t n_tiles = (T * G + 15) / 16;
   const uint32_t tile_keys = pos0 + min((tile * 16 + 15) / G, T - 1) + 1;
   const uint32_t nck = (tile_keys + p.split_keys - 1) / p.split_keys;
-  const uint32_t first = a.s.item_off[sq] + j * a.s.n_chunks[sq] * n_tiles + tile;
+  const uint32_t first = a.s.item_off[sq] + j * n_tiles + tile;
+  const uint32_t stride = p.n_kv_heads * n_tiles;  // from one chunk's item to the next
   const float* ml = p.part + static_cast<size_t>(p.n_items) * 16 * D;
-  auto at = [&](uint32_t k) { return static_cast<size_t>(first + k * n_tiles) * 16 + c; };
+  auto at = [&](uint32_t k) { return static_cast<size_t>(first + k * stride) * 16 + c; };
   // the maximum over the chunks (finite: chunk 0 holds key 0) and the sink
   float mx = -INFINITY;
   for (uint32_t k0 = 0; k0 < nck; k0 += kWave)
