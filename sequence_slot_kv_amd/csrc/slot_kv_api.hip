@@ -509,9 +509,44 @@ struct SeqRows {
 struct PrefillLaunch {
   size_t s0 = 0;
   uint32_t n = 0, rows = 0;
-  uint32_t split_keys = 0;  // 0: tiled attention
-  uint32_t n_items = 0;     // split-K work items
+  uint32_t split_keys = 0;  // keys per chunk; 0: whole key ranges (tiled only)
+  uint32_t n_items = 0;     // partial items
 };
+
+// Tiled workgroups of a launch (per kv head), and its partial items when cut
+// into chunks of ck keys.
+void tiled_counts(const std::vector<SeqRows>& seqs, size_t s0, uint32_t n, uint32_t G,
+                  uint32_t ck, uint64_t* groups, uint64_t* items_per_head) {
+  *groups = *items_per_head = 0;
+  for (size_t i = s0; i < s0 + n; ++i) {
+    const uint64_t tiles = (uint64_t(seqs[i].len) * G + 15) / 16;
+    const uint64_t n_ck = ck ? (uint64_t(seqs[i].pos0) + seqs[i].len + ck - 1) / ck : 1;
+    *groups += (tiles * 16 + slotkv::kPrefillRowsPerGroup - 1) / slotkv::kPrefillRowsPerGroup * n_ck;
+    *items_per_head += tiles * n_ck;
+  }
+}
+
+// Keys per chunk of a tiled launch whose workgroups are too few to fill the
+// chip: about kChunkTargetGroups workgroups, chunks a multiple of 64 keys
+// (0: no cut).
+uint32_t plan_tiled_chunks(const std::vector<SeqRows>& seqs, size_t s0, uint32_t n, uint32_t G,
+                           uint32_t n_kv_heads, uint32_t* n_items) {
+  uint64_t groups, items;
+  tiled_counts(seqs, s0, n, G, 0, &groups, &items);
+  groups *= n_kv_heads;
+  if (groups == 0 || groups >= slotkv::kChunkBelowGroups) return 0;
+  uint64_t max_keys = 0;
+  for (size_t i = s0; i < s0 + n; ++i)
+    max_keys = std::max<uint64_t>(max_keys, uint64_t(seqs[i].pos0) + seqs[i].len);
+  const uint64_t want = (slotkv::kChunkTargetGroups + groups - 1) / groups;
+  const uint64_t ck = ((max_keys + want - 1) / want + 63) / 64 * 64;
+  if (ck >= max_keys) return 0;
+  tiled_counts(seqs, s0, n, G, static_cast<uint32_t>(ck), &groups, &items);
+  items *= n_kv_heads;
+  if (items > slotkv::kMaxSplitItems) return 0;
+  *n_items = static_cast<uint32_t>(items);
+  return static_cast<uint32_t>(ck);
+}
 
 // Keys per chunk of a split-K launch: the smallest power-of-two multiple of
 // kSplitMinKeys that keeps its work items within kMaxSplitItems (0 if none).
@@ -562,7 +597,9 @@ int run_prefill(slot_kv* h, uint32_t layer, const float* q, const float* k_new,
   // one call takes one kernel: split-K only if every launch can
   for (const PrefillLaunch& pl : plan) split = split && pl.split_keys != 0;
   for (PrefillLaunch& pl : plan) {
-    if (!split) pl.split_keys = pl.n_items = 0;
+    if (!split)
+      pl.split_keys = plan_tiled_chunks(seqs, pl.s0, pl.n, G, L.n_kv_heads, &pl.n_items);
+    if (!pl.split_keys) pl.n_items = 0;
     scratch = std::max(scratch, size_t(pl.rows) * L.n_heads * D +
                                     size_t(pl.n_items) * 16 * (D + 2));
   }
@@ -600,19 +637,21 @@ int run_prefill(slot_kv* h, uint32_t layer, const float* q, const float* k_new,
       rows += r.len;
     }
     a.s.row_off[n] = rows;
-    if (split) {
-      uint32_t items = 0;
-      for (uint32_t i = 0; i < n; ++i) {
-        a.s.item_off[i] = items;
-        a.s.n_chunks[i] = (a.s.pos0[i] + a.s.len[i] + pl.split_keys - 1) / pl.split_keys;
-        items += (a.s.len[i] * G + 15) / 16 * a.s.n_chunks[i] * L.n_kv_heads;
-      }
-      a.s.item_off[n] = items;
-      p.part = h->part + size_t(pl.rows) * qd;
-      p.n_items = items;
-      p.split_keys = pl.split_keys;
-      p.n_groups = 0;
-    } else {
+    // partial items (key-chunked launches)
+    const uint32_t ck = pl.split_keys;
+    uint32_t items = 0;
+    for (uint32_t i = 0; i < n; ++i) {
+      a.s.item_off[i] = items;
+      if (ck)
+        items += (a.s.len[i] * G + 15) / 16 * ((a.s.pos0[i] + a.s.len[i] + ck - 1) / ck) *
+                 L.n_kv_heads;
+    }
+    a.s.item_off[n] = items;
+    p.part = ck ? h->part + size_t(pl.rows) * qd : nullptr;
+    p.n_items = items;
+    p.split_keys = ck;
+    p.n_groups = 0;
+    if (!split) {  // tiled workgroups, heaviest sequence first
       std::vector<uint64_t> work(n);
       for (uint32_t i = 0; i < n; ++i) {
         a.s.by_work[i] = i;
@@ -622,13 +661,14 @@ int run_prefill(slot_kv* h, uint32_t layer, const float* q, const float* k_new,
                        [&](uint32_t x, uint32_t y) { return work[x] > work[y]; });
       uint32_t groups = 0;
       for (uint32_t k = 0; k < n; ++k) {
+        const uint32_t i = a.s.by_work[k];
         a.s.grp_off[k] = groups;
-        const uint32_t tiles = (a.s.len[a.s.by_work[k]] * G + 15) / 16;
-        groups += (tiles * 16 + slotkv::kPrefillRowsPerGroup - 1) / slotkv::kPrefillRowsPerGroup;
+        const uint32_t tiles = (a.s.len[i] * G + 15) / 16;
+        const uint32_t n_ck = ck ? (a.s.pos0[i] + a.s.len[i] + ck - 1) / ck : 1;
+        groups += (tiles * 16 + slotkv::kPrefillRowsPerGroup - 1) /
+                  slotkv::kPrefillRowsPerGroup * n_ck;
       }
       a.s.grp_off[n] = groups;
-      p.part = nullptr;
-      p.n_items = p.split_keys = 0;
       p.n_groups = groups;
     }
     p.n_seq = n;

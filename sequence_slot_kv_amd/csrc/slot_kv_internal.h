@@ -94,8 +94,9 @@ struct PrefillParams {
   uint32_t n_seq;          // sequences of this launch
   uint32_t n_rows;         // token rows of this launch
   uint32_t n_groups;       // attention workgroups per kv head (all sequences)
-  uint32_t n_items;        // split-K: work items (one wave each) of this launch
-  uint32_t split_keys;     // split-K: keys per chunk (a multiple of 16)
+  uint32_t n_items;        // key-chunked: partial items of this launch
+  uint32_t split_keys;     // keys per chunk (a multiple of 64); 0: the tiled attention
+                           // runs over whole key ranges and normalises itself
   float eps;
   float qk_scale_log2;     // scale * log2(e)
   uint32_t flags;          // SLOT_KV_FLAG_*
@@ -106,16 +107,9 @@ struct PrefillSeqs {
   uint32_t pos0[kMaxSeqPerLaunch];
   uint32_t len[kMaxSeqPerLaunch];
   uint32_t row_off[kMaxSeqPerLaunch + 1];  // first row of each sequence (and the total)
-  // The attention of a launch runs one of two kernels, and each reads its
-  // own view of the last two tables.
-  union {
-    uint32_t by_work[kMaxSeqPerLaunch];    // tiled: the sequences, most attention work first
-    uint32_t n_chunks[kMaxSeqPerLaunch];   // split-K: key chunks of each sequence
-  };
-  union {
-    uint32_t grp_off[kMaxSeqPerLaunch + 1];   // tiled: first workgroup of by_work[k] (per kv head)
-    uint32_t item_off[kMaxSeqPerLaunch + 1];  // split-K: first work item of each sequence
-  };
+  uint32_t by_work[kMaxSeqPerLaunch];      // tiled: the sequences, most attention work first
+  uint32_t grp_off[kMaxSeqPerLaunch + 1];  // tiled: first workgroup of by_work[k] (per kv head)
+  uint32_t item_off[kMaxSeqPerLaunch + 1]; // key-chunked: first partial item of each sequence
 };
 
 struct PrefillArgs {
@@ -128,15 +122,21 @@ static_assert(sizeof(PrefillArgs) < 4000, "kernel arguments must stay below 4 Ki
 // Query rows per attention workgroup of a prefill (4 waves x 16 rows).
 constexpr uint32_t kPrefillRowsPerGroup = 64;
 
-// Split-K attention (sequences with at most kSplitMaxRows query rows per kv
-// head, as in a multi-row verify): one wave per work item (sequence, kv
-// head, key chunk, 16-row tile), items of one sequence ordered
+// Key-chunked attention.  The keys of a (sequence, kv head) are cut into
+// chunks of split_keys keys, and each (chunk, 16-row tile) pair leaves a
+// partial result (an item), ordered within a sequence
 //   item_off[i] + (chunk * n_kv_heads + j) * n_tiles + tile,
-// n_tiles = ceil(len * G / 16), so that neighbouring waves read the kv heads
-// of the same key rows; a merge kernel then combines the chunks.
+// n_tiles = ceil(len * G / 16), so that neighbouring items read the kv heads
+// of the same key rows; a merge kernel then combines each row's chunks.
+// Sequences with at most kSplitMaxRows query rows per kv head (a multi-row
+// verify) run one wave per item (split-K); longer ones keep the tiled
+// workgroups, which are cut into key chunks only when they are too few to
+// fill the chip (fewer than kChunkBelowGroups per launch).
 constexpr uint32_t kSplitMaxRows = 64;
-constexpr uint32_t kSplitMinKeys = 256;       // smallest chunk
+constexpr uint32_t kSplitMinKeys = 256;       // smallest split-K chunk
 constexpr uint32_t kMaxSplitItems = 1u << 14; // per launch (bounds the partials)
+constexpr uint32_t kChunkBelowGroups = 512;
+constexpr uint32_t kChunkTargetGroups = 1024;
 
 // Launches of a prefill / verify: norm + RoPE + KV write, then the
 // attention (tiled, or split-K and merge when `split`).  `before_attn` /

@@ -167,7 +167,7 @@ struct PrefillLds {
   float v[2][16][D + kLdsPad];
 };
 
-template <int D, int G>
+template <int D, int G, bool CHUNKED>
 __global__ void __launch_bounds__(kWave * kAttnWaves) prefill_attn_kernel(const PrefillArgs a) {
   constexpr int DQ = D / 4;   // head_dim values per lane group
   constexpr int TD = D / 16;  // output tiles of 16 head_dim values
@@ -180,7 +180,8 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) prefill_attn_kernel(const 
   const uint32_t lane = tid % kWave;
   const uint32_t w = tid / kWave;
   const uint32_t g = lane / 16, c = lane % 16;
-  // workgroup -> (kv head, sequence, tile group), heaviest first
+  // workgroup -> (kv head, sequence, tile group, key chunk), heaviest first
+  const uint32_t CK = CHUNKED ? p.split_keys : 0;  // 0: one chunk of all keys
   const uint32_t j = blockIdx.x % p.n_kv_heads;
   const uint32_t flat = blockIdx.x / p.n_kv_heads;  // < n_groups
   uint32_t lo = 0, hi = p.n_seq;
@@ -189,8 +190,10 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) prefill_attn_kernel(const 
     if (a.s.grp_off[mid] <= flat) lo = mid; else hi = mid;
   }
   const uint32_t sq = a.s.by_work[lo];
-  const uint32_t grp = a.s.grp_off[lo + 1] - 1 - flat;  // the sequence's last group first
   const uint32_t T = a.s.len[sq], pos0 = a.s.pos0[sq], row0 = a.s.row_off[sq];
+  const uint32_t n_ck = CK ? (pos0 + T + CK - 1) / CK : 1;
+  const uint32_t local = a.s.grp_off[lo + 1] - 1 - flat;  // the sequence's last group first
+  const uint32_t grp = local / n_ck, chunk = local - grp * n_ck;
   const uint32_t n_tiles = (T * G + 15) / 16;
   const uint32_t tile = grp * kAttnWaves + w;  // may be past the last tile: then it only stages
   const uint32_t R = tile * 16 + c;
@@ -202,6 +205,10 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) prefill_attn_kernel(const 
   const uint32_t wave_keys = pos0 + min((tile * 16 + 15) / G, T - 1) + 1;
   const uint32_t last_tile = min(grp * kAttnWaves + kAttnWaves - 1, n_tiles - 1);
   const uint32_t n_keys = pos0 + min((last_tile * 16 + 15) / G, T - 1) + 1;
+  // the workgroup's keys [k_lo, k_hi): its chunk of the keys of its last tile
+  const uint32_t k_lo = CK ? chunk * CK : 0;
+  if (k_lo >= n_keys) return;  // workgroup-uniform, before any barrier
+  const uint32_t k_hi = CK ? min(k_lo + CK, n_keys) : n_keys;
 
   float qv[DQ];
   {
@@ -226,7 +233,7 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) prefill_attn_kernel(const 
     for (int s = 0; s < NF4; ++s) {
       const uint32_t f = tid + kWave * kAttnWaves * s;
       const uint32_t row = f / (D / 4), col = 4 * (f % (D / 4));
-      const size_t at = static_cast<size_t>(min(kb + row, n_keys - 1)) * p.kv_dim + col;
+      const size_t at = static_cast<size_t>(min(kb + row, k_hi - 1)) * p.kv_dim + col;
       stk[s] = *reinterpret_cast<const f4*>(kbase + at);
       stv[s] = *reinterpret_cast<const f4*>(vbase + at);
     }
@@ -246,13 +253,13 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) prefill_attn_kernel(const 
 #pragma unroll
   for (int u = 0; u < TD; ++u) o[u] = f4{0.f, 0.f, 0.f, 0.f};
 
-  const uint32_t n_blk = (n_keys + 15) / 16;
-  fetch(0);
+  const uint32_t n_blk = (k_hi - k_lo + 15) / 16;
+  fetch(k_lo);
   stage(0);
   __syncthreads();
   for (uint32_t blk = 0; blk < n_blk; ++blk) {  // workgroup-uniform
     const uint32_t buf = blk & 1;
-    const uint32_t kb = blk * 16;
+    const uint32_t kb = k_lo + blk * 16;
     if (blk + 1 < n_blk) fetch(kb + 16);
     if (kb < wave_keys) {  // wave-uniform: blocks past the tile are all masked
       f4 s = f4{0.f, 0.f, 0.f, 0.f};
@@ -263,19 +270,21 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) prefill_attn_kernel(const 
         for (int e = 0; e < 4; ++e)
           s = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[e], qv[i + e], s, 0, 0, 0);
       }
-      // causal mask: key kb + 4g + r is visible to the row iff it is <= the
-      // row's position (every key >= n_keys is also past every row)
+      // causal mask: key kb + 4g + r counts iff it is <= the row's position
+      // and inside the workgroup's keys (keys >= n_keys are past every row)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (kb + 4 * g + r > row_pos) s[r] = -INFINITY;
+        if (kb + 4 * g + r > row_pos || (CHUNKED && kb + 4 * g + r >= k_hi)) s[r] = -INFINITY;
       float mb = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
       mb = fmaxf(mb, __shfl_xor(mb, 16));
       mb = fmaxf(mb, __shfl_xor(mb, 32));
-      const float m_new = fmaxf(m_run, mb);  // finite: key 0 is visible to every row
-      const float corr = fast_exp2(m_run - m_new);
+      const float m_new = fmaxf(m_run, mb);
+      // finite from key 0 on; a later chunk may hold no key of a row yet
+      const float m_use = (CHUNKED && m_new == -INFINITY) ? 0.f : m_new;
+      const float corr = fast_exp2(m_run - m_use);
       f4 pr;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(s[r] - m_new);
+      for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(s[r] - m_use);
       l_run = l_run * corr + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
 #pragma unroll
       for (int u = 0; u < TD; ++u) o[u] *= corr;
@@ -299,6 +308,22 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) prefill_attn_kernel(const 
   // the row's sum over its four lane groups, the sink, and the output
   float L = l_run + __shfl_xor(l_run, 16);
   L += __shfl_xor(L, 32);
+  if (CHUNKED) {  // one chunk of several: leave the partial for the merge
+    if (k_lo >= wave_keys) return;  // no key of this tile here: the merge skips it
+    const uint32_t item = a.s.item_off[sq] + (chunk * p.n_kv_heads + j) * n_tiles + tile;
+    float* acc = p.part + (static_cast<size_t>(item) * 16 + c) * D + DQ * g;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int u = 0; u < TD; u += 4)
+        *reinterpret_cast<f4*>(acc + TD * r + u) = f4{o[u][r], o[u + 1][r], o[u + 2][r], o[u + 3][r]};
+    if (g == 0) {
+      float* ml = p.part + static_cast<size_t>(p.n_items) * 16 * D + (static_cast<size_t>(item) * 16 + c) * 2;
+      ml[0] = m_run;
+      ml[1] = L;
+    }
+    return;
+  }
   float sa = 1.f;
   if (p.sinks) {
     const float sk = p.sinks[h] * kLog2e;
@@ -560,7 +585,18 @@ hipError_t launch_split(const PrefillArgs& a, hipStream_t s) {
 template <int D, int G>
 hipError_t launch_attn(const PrefillArgs& a, hipStream_t s) {
   const uint32_t blocks = a.p.n_groups * a.p.n_kv_heads;
-  hipLaunchKernelGGL((prefill_attn_kernel<D, G>), dim3(blocks), dim3(kWave * kAttnWaves), 0, s, a);
+  if (a.p.split_keys == 0) {
+    hipLaunchKernelGGL((prefill_attn_kernel<D, G, false>), dim3(blocks), dim3(kWave * kAttnWaves), 0,
+                       s, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((prefill_attn_kernel<D, G, true>), dim3(blocks), dim3(kWave * kAttnWaves), 0, s,
+                     a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const uint32_t waves = a.p.n_rows * a.p.n_heads;
+  hipLaunchKernelGGL((split_merge_kernel<D, G>), dim3((waves + kAttnWaves - 1) / kAttnWaves),
+                     dim3(kWave * kAttnWaves), 0, s, a);
   return hipGetLastError();
 }
 
