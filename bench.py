@@ -16,7 +16,9 @@ Prints ONE JSON line on stdout:
                second pass of the same K steps so that the timed region
                carries no event records) vs 8 TB/s, with the HBM traffic
                measured by rocprofv3 counters when the committed counter
-               record matches the current kernel source
+               record matches the current kernel source; a third pass writes
+               1 GiB before every step (outside the events) and reports the
+               launch time with L2 and the Infinity Cache emptied
   cpu_baseline the CPU oracle on the host cores over the same rows
 
     python bench.py [--steps K] [--warmup W] [--workload mid]
@@ -217,6 +219,21 @@ def main():
     rc, kernel_ms, launches = b.slot_kv_profile_end(kv.h)
     torch.cuda.synchronize()
     assert rc == 0 and launches == args.steps * n_layers
+    # and once more with the caches emptied before every step: a 1 GiB
+    # write (outside the event pairs) evicts the KV rows from L2 and the
+    # 256 MB Infinity Cache, so no launch can be served from there
+    flush = torch.empty(2**28, dtype=torch.float32, device="cuda")
+    cold_ms = 0.0
+    for _ in range(args.steps):
+        flush.fill_(1.0)
+        rc = b.slot_kv_profile_begin(kv.h)
+        assert rc == 0
+        step()
+        rc, ms, n = b.slot_kv_profile_end(kv.h)
+        assert rc == 0 and n == n_layers
+        cold_ms += ms
+    del flush
+    torch.cuda.synchronize()
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     kv_bytes = w.kv_bytes()
@@ -225,9 +242,10 @@ def main():
     mean_launch_ms = kernel_ms / launches
     bytes_per_launch = kv_bytes / n_layers
     achieved = bytes_per_launch / (mean_launch_ms / 1e3) / 1e9
+    cold_launch_ms = cold_ms / (args.steps * n_layers)
     traffic = measured_traffic(w.name)
     log(f"[bench] {ms_per_step * 1e3:.1f} us/step, fused kernel {mean_launch_ms * 1e3:.1f} us/launch, "
-        f"{achieved:.0f} GB/s in-kernel")
+        f"{achieved:.0f} GB/s in-kernel; {cold_launch_ms * 1e3:.1f} us/launch with caches flushed")
 
     cpu = None
     if hist is not None:
@@ -249,7 +267,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "kernel": "decode_attn_kernel", "kernel_us": mean_launch_ms * 1e3,
-                     "algorithmic_bytes_per_launch": bytes_per_launch},
+                     "algorithmic_bytes_per_launch": bytes_per_launch,
+                     "kernel_us_caches_flushed": cold_launch_ms * 1e3,
+                     "achieved_caches_flushed": bytes_per_launch / (cold_launch_ms / 1e3) / 1e9},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
