@@ -45,10 +45,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 static_assert(SLOT_KV_CHUNK % NW == 0, "a chunk splits evenly over the waves");
 
 // Lanes per key row: enough that each lane holds about 32 floats of query
-// (G heads) and as many of accumulator.  The lane's elements of a head
-// vector are d = i*4*LPK + 4*r + c (slice i, lane r of the key group,
-// component c), so the RoPE partner d + D/2 sits in the same lane, slice
-// i + NV4/2.
+// (G heads) and as many of accumulator, at most 16 (one DPP row).  The
+// lane's elements of a head vector are d = i*4*LPK + 4*r + c (slice i, lane
+// r of the key group, component c); queries reach that layout from their
+// LDS staging, where they were rotated.
 #ifndef SLOT_KV_LPK
 #define SLOT_KV_LPK 0  // 0: derive from the shape
 #endif
@@ -58,13 +58,17 @@ static_assert(SLOT_KV_CHUNK % NW == 0, "a chunk splits evenly over the waves");
 constexpr int pick_lpk(int D, int G) {
   int want = SLOT_KV_LPK ? SLOT_KV_LPK : G * D / 32;
   int lpk = want < 4 ? 4 : (want > 16 ? 16 : want);
-  while (D / (4 * lpk) < 2) lpk /= 2;
+  while (D / (4 * lpk) < 1) lpk /= 2;
   return lpk;
 }
-// Keys per key group per pipeline stage: about 8 float4 loads per lane.
-constexpr int pick_unroll(int D, int LPK) {
+// Keys per key group per pipeline stage: about 8 float4 loads per lane, and
+// at most 16 scores (G per key) per lane, which leaves G = 8 with 64 floats
+// each of query and accumulator room for two waves per SIMD.
+constexpr int pick_unroll(int D, int G, int LPK) {
   int nv4 = D / (4 * LPK);
-  return SLOT_KV_UNROLL ? SLOT_KV_UNROLL : (nv4 >= 8 ? 1 : 8 / nv4);
+  int u = nv4 >= 8 ? 1 : 8 / nv4;
+  while (u > 1 && G * u > 16) u /= 2;
+  return SLOT_KV_UNROLL ? SLOT_KV_UNROLL : u;
 }
 
 template <int CTRL>
@@ -145,17 +149,18 @@ struct alignas(16) Lds {
   uint32_t last;
 };
 
-// Occupancy the register allocation targets: shapes whose lanes hold 64
-// floats of query and 64 of accumulator get the whole register file.
+// Occupancy the register allocation targets: shapes whose lanes hold more
+// than 64 floats of query (and as many of accumulator) get the whole
+// register file.
 template <int D, int G>
 constexpr int waves_per_eu() {
-  return G * D / pick_lpk(D, G) >= 64 ? 1 : SLOT_KV_WAVES_PER_EU;
+  return G * D / pick_lpk(D, G) > 64 ? 1 : SLOT_KV_WAVES_PER_EU;
 }
 
 template <int D, int G>
 struct Shape {
   static constexpr int LPK = pick_lpk(D, G);
-  static constexpr int U = pick_unroll(D, LPK);
+  static constexpr int U = pick_unroll(D, G, LPK);
   static constexpr int NV4 = D / (4 * LPK);                  // float4 per lane per head vector
   static constexpr int NG = kWave / LPK;                     // key groups per wave
   static constexpr int SL = 4 * LPK;                         // floats per slice
@@ -163,7 +168,7 @@ struct Shape {
   static constexpr int KPW = SLOT_KV_CHUNK / NW;             // history keys per wave, at most
   static constexpr int NST = (KPW + STEP - 1) / STEP;        // stages per pass, at most
   static constexpr int SCORES = NST * NG * G * U;            // score slots per wave
-  static_assert(NV4 >= 2 && NV4 % 2 == 0, "lane layout needs an even slice count");
+  static_assert(NV4 >= 1 && D % (4 * LPK) == 0, "whole float4 slices per lane");
 };
 
 // One work unit as one wave sees it: chunk `chunk` of row b against kv head

@@ -332,3 +332,41 @@ def test_layer_stack_sampled_parity():
             k, v = kv.read_rows(l, int(w.slots[bi]), int(w.positions[bi]), 1)
             assert v.cpu().numpy().tobytes() == refs[l][bi][1].tobytes()
     kv.close()
+
+
+# ---------------------------------------------------------------- every head shape
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_decode_shapes_full_parity(D, G):
+    # Each (head_dim, group) instantiation of the decode kernel: rows of one
+    # key, rows at both sides of the 512-key chunk boundaries (split rows
+    # merged by the last workgroup), every cache cell outside 0..pos poisoned.
+    Hkv = 2
+    H = G * Hkv
+    rng = np.random.default_rng(300 + 10 * G + D)
+    n_slots, slot_ctx = 8, 1200
+    L = wl.make_layer(rng, H, Hkv, D, 1e4, G % 2 == 0)
+    positions = np.array([0, 1, 511, 512, 1023, 1199], np.uint32)
+    slots = rng.permutation(n_slots)[:positions.size].astype(np.uint32)
+    B = positions.size
+    q = rng.standard_normal((B, H * D), dtype=np.float32)
+    kn = rng.standard_normal((B, L.kv_dim), dtype=np.float32)
+    vn = rng.standard_normal((B, L.kv_dim), dtype=np.float32)
+    ck = np.full((n_slots, slot_ctx, L.kv_dim), np.nan, np.float32)
+    cv = np.full_like(ck, np.nan)
+    for s, p in zip(slots, positions):
+        ck[s, :p] = rng.standard_normal((p, L.kv_dim), dtype=np.float32)
+        cv[s, :p] = rng.standard_normal((p, L.kv_dim), dtype=np.float32)
+    kv = b.SlotKV()
+    kv.alloc(n_slots, slot_ctx, [L.kv_dim])
+    kv.set_layer(0, L)
+    upload_history(kv, 0, ck, cv)
+    out = kv.decode_attn(0, *(torch.from_numpy(x).cuda() for x in (q, kn, vn)), positions, slots)
+    out = out.cpu().numpy()
+    gk = kv.layer_view(0)[0].cpu().numpy()
+    kv.close()
+    rc, ref = oracle.decode_batch(L, ck, cv, q, kn, vn, positions, slots)
+    assert rc == 0
+    assert_close(out, ref, f"decode D={D} G={G}")
+    for s, p in zip(slots, positions):
+        assert_close(gk[s, p], ck[s, p], "written K")
