@@ -370,3 +370,33 @@ def test_decode_shapes_full_parity(D, G):
     assert_close(out, ref, f"decode D={D} G={G}")
     for s, p in zip(slots, positions):
         assert_close(gk[s, p], ck[s, p], "written K")
+
+
+def test_decode_more_rows_than_one_launch():
+    # 300 rows: the call is cut into launches of at most 256 rows, each with
+    # its own row table; every row is checked against the oracle.
+    rng = np.random.default_rng(400)
+    H, Hkv, D = 8, 2, 64
+    n_slots, slot_ctx, B = 300, 640, 300
+    L = wl.make_layer(rng, H, Hkv, D, 1e4, True)
+    positions = rng.integers(0, slot_ctx, size=B).astype(np.uint32)
+    positions[:3] = [0, 511, slot_ctx - 1]
+    slots = rng.permutation(n_slots)[:B].astype(np.uint32)
+    q = rng.standard_normal((B, H * D), dtype=np.float32)
+    kn = rng.standard_normal((B, L.kv_dim), dtype=np.float32)
+    vn = rng.standard_normal((B, L.kv_dim), dtype=np.float32)
+    ck = rng.standard_normal((n_slots, slot_ctx, L.kv_dim), dtype=np.float32)
+    cv = rng.standard_normal((n_slots, slot_ctx, L.kv_dim), dtype=np.float32)
+    kv = b.SlotKV()
+    kv.alloc(n_slots, slot_ctx, [L.kv_dim])
+    kv.set_layer(0, L)
+    upload_history(kv, 0, ck, cv)
+    b.slot_kv_profile_begin(kv.h)
+    out = kv.decode_attn(0, *(torch.from_numpy(x).cuda() for x in (q, kn, vn)), positions, slots)
+    rc, _, launches = b.slot_kv_profile_end(kv.h)
+    assert rc == 0 and launches == 2
+    out = out.cpu().numpy()
+    kv.close()
+    rc, ref = oracle.decode_batch(L, ck, cv, q, kn, vn, positions, slots)
+    assert rc == 0
+    assert_close(out, ref, "300-row decode")
