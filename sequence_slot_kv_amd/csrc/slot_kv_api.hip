@@ -556,11 +556,11 @@ uint32_t plan_split(const std::vector<SeqRows>& seqs, size_t s0, uint32_t n, uin
   for (size_t i = s0; i < s0 + n; ++i)
     max_keys = std::max<uint64_t>(max_keys, uint64_t(seqs[i].pos0) + seqs[i].len);
   for (uint64_t ck = slotkv::kSplitMinKeys;; ck *= 2) {
-    uint64_t items = 0;
+    uint64_t items = 0;  // one per workgroup of kSplitChunksPerGroup chunks
     for (size_t i = s0; i < s0 + n; ++i) {
       const uint64_t tiles = (uint64_t(seqs[i].len) * G + 15) / 16;
-      const uint64_t chunks = (uint64_t(seqs[i].pos0) + seqs[i].len + ck - 1) / ck;
-      items += tiles * chunks * n_kv_heads;
+      items += tiles * slotkv::split_groups(seqs[i].pos0 + seqs[i].len, static_cast<uint32_t>(ck)) *
+               n_kv_heads;
     }
     if (items <= slotkv::kMaxSplitItems) {
       *n_items = static_cast<uint32_t>(items);
@@ -642,9 +642,10 @@ int run_prefill(slot_kv* h, uint32_t layer, const float* q, const float* k_new,
     uint32_t items = 0;
     for (uint32_t i = 0; i < n; ++i) {
       a.s.item_off[i] = items;
-      if (ck)
-        items += (a.s.len[i] * G + 15) / 16 * ((a.s.pos0[i] + a.s.len[i] + ck - 1) / ck) *
-                 L.n_kv_heads;
+      const uint32_t keys = a.s.pos0[i] + a.s.len[i];
+      if (ck)  // split-K: per group of chunks; chunked tiled: per chunk
+        items += (a.s.len[i] * G + 15) / 16 *
+                 (split ? slotkv::split_groups(keys, ck) : (keys + ck - 1) / ck) * L.n_kv_heads;
     }
     a.s.item_off[n] = items;
     p.part = ck ? h->part + size_t(pl.rows) * qd : nullptr;

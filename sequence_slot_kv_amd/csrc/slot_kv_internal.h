@@ -133,6 +133,14 @@ constexpr uint32_t kPrefillRowsPerGroup = 64;
 // workgroups, which are cut into key chunks only when they are too few to
 // fill the chip (fewer than kChunkBelowGroups per launch).
 constexpr uint32_t kSplitMaxRows = 64;
+// Split-K workgroups take four consecutive chunks of one (sequence, kv head,
+// tile), ordered item_off[i] + (j * n_tiles + tile) * groups + group, and
+// leave one partial each.
+constexpr uint32_t kSplitChunksPerGroup = 4;
+__host__ __device__ inline uint32_t split_groups(uint32_t keys, uint32_t split_keys) {
+  const uint32_t chunks = (keys + split_keys - 1) / split_keys;
+  return (chunks + kSplitChunksPerGroup - 1) / kSplitChunksPerGroup;
+}
 constexpr uint32_t kSplitMinKeys = 256;       // smallest split-K chunk
 constexpr uint32_t kMaxSplitItems = 1u << 14; // per launch (bounds the partials)
 constexpr uint32_t kChunkBelowGroups = 512;

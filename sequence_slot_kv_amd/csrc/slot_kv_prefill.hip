@@ -353,24 +353,43 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) prefill_attn_kernel(const 
 // order of the score product is permuted so that each K load instruction
 // reads 64 contiguous bytes per row: lane (c, g) multiplies
 // d = 16v + 4g + e at MFMA (v, e), for K row c and for its query row c.
-// A wave writes its unnormalised partial (per row: running max m in log2
-// units, sum l, and acc[D]); split_merge_kernel combines them.
+// The four waves of a workgroup take four consecutive chunks of the same
+// (sequence, kv head, tile) and combine their results through LDS, so that
+// one unnormalised partial per workgroup (per row: running max m in log2
+// units, sum l, and acc[D]) goes to memory; split_merge_kernel combines the
+// partials of a row.
+// Two waves per SIMD where the registers allow it without spilling (head_dim
+// up to 128); head_dim 256 takes the whole register file.
+template <int D>
+constexpr int split_waves_per_eu() { return D <= 128 ? 2 : 1; }
+
+// LDS of a split-K workgroup: waves 1..3 hand their results to wave 0,
+// element-major ([float][lane]) so that the 16-byte stores of a wave fall on
+// consecutive banks.
+template <int D>
+struct SplitLds {
+  f4 acc[kAttnWaves - 1][D / 16][kWave];
+  float m[kAttnWaves - 1][kWave];
+  float l[kAttnWaves - 1][kWave];
+};
+
 template <int D, int G>
-__global__ void __launch_bounds__(kWave * kAttnWaves) __attribute__((amdgpu_waves_per_eu(2)))
-split_attn_kernel(const PrefillArgs a) {
+__global__ void __launch_bounds__(kWave * kAttnWaves)
+__attribute__((amdgpu_waves_per_eu(split_waves_per_eu<D>()))) split_attn_kernel(const PrefillArgs a) {
   constexpr int NK = D / 16;   // K float4 per lane per block
   constexpr int TD = D / 16;   // output tiles of 16 head_dim values
   constexpr int DQ = D / 4;
   constexpr int NV = TD / 4;   // V float4 per lane per key of a lane group
+  __shared__ SplitLds<D> sh;
   if (a.magic != kArgsMagic) return;  // argument block not delivered whole
   const PrefillParams& p = a.p;
   const uint32_t lane = threadIdx.x % kWave;
+  const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const uint32_t g = lane / 16, c = lane % 16;
-  // the item is the same for the whole wave: keep it (and all that follows
-  // from it) in scalar registers, so that the key loop is uniform
-  const uint32_t item =
-      __builtin_amdgcn_readfirstlane(blockIdx.x * kAttnWaves + threadIdx.x / kWave);
-  if (item >= p.n_items) return;
+  // workgroup -> (sequence, kv head j, tile, chunk group); wave w takes chunk
+  // 4 * group + w.  All of it is uniform: scalar registers, uniform loops.
+  const uint32_t item = blockIdx.x;  // one partial per workgroup
+  if (item >= p.n_items) return;     // workgroup-uniform, before any barrier
   uint32_t lo = 0, hi = p.n_seq;  // the sequence: last i with item_off[i] <= item
   while (hi - lo > 1) {
     const uint32_t mid = (lo + hi) / 2;
@@ -379,16 +398,17 @@ split_attn_kernel(const PrefillArgs a) {
   const uint32_t sq = lo;
   const uint32_t T = a.s.len[sq], pos0 = a.s.pos0[sq], row0 = a.s.row_off[sq];
   const uint32_t n_tiles = (T * G + 15) / 16;
+  const uint32_t n_grp = split_groups(pos0 + T, p.split_keys);
   const uint32_t idx = item - a.s.item_off[sq];
-  const uint32_t tile = idx % n_tiles;
-  const uint32_t jc = idx / n_tiles;
-  const uint32_t j = jc % p.n_kv_heads;
-  const uint32_t chunk = jc / p.n_kv_heads;
+  const uint32_t grp = idx % n_grp;
+  const uint32_t ut = idx / n_grp;
+  const uint32_t tile = ut % n_tiles;
+  const uint32_t j = ut / n_tiles;
   const uint32_t tile_keys = pos0 + min((tile * 16 + 15) / G, T - 1) + 1;
-  const uint32_t k0 = chunk * p.split_keys;
-  if (k0 >= tile_keys) return;  // past this tile's keys: the merge does not read it
-  const uint32_t k1 = min(k0 + p.split_keys, tile_keys);
-  const uint32_t n_blk = (k1 - k0 + 15) / 16;
+  const uint32_t k0 = (grp * kAttnWaves + w) * p.split_keys;
+  const bool active = k0 < tile_keys;  // wave-uniform: else nothing of this tile here
+  const uint32_t k1 = active ? min(k0 + p.split_keys, tile_keys) : k0 + 1;
+  const uint32_t n_blk = active ? (k1 - k0 + 15) / 16 : 0;
   const uint32_t R = tile * 16 + c;
   const uint32_t t = R / G, h = j * G + R % G;
   const uint32_t tq = t < T ? t : T - 1;  // rows past the last token compute on it, unused
@@ -411,11 +431,16 @@ split_attn_kernel(const PrefillArgs a) {
   // Loads are issued unconditionally, so that the number in flight is known
   // where a block is consumed: rows past the chunk (a partial last block, or
   // the block after the last) re-read its last key, which the mask drops.
-  auto load = [&](f4 (&kr)[NK], f4 (&vr)[4][NV], uint32_t b) {
+  // (an inactive wave issues no load: its loop runs no block, and its
+  // prologue loads are skipped below)
+  auto load_k = [&](f4 (&kr)[NK], uint32_t b) {
     const uint32_t kb = k0 + 16 * b;
     const float* kp = kbase + static_cast<size_t>(min(kb + c, k1 - 1)) * p.kv_dim + 4 * g;
 #pragma unroll
     for (int v = 0; v < NK; ++v) kr[v] = *reinterpret_cast<const f4*>(kp + 16 * v);
+  };
+  auto load_v = [&](f4 (&vr)[4][NV], uint32_t b) {
+    const uint32_t kb = k0 + 16 * b;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const float* vp = vbase + static_cast<size_t>(min(kb + 4 * g + m, k1 - 1)) * p.kv_dim + TD * c;
@@ -428,7 +453,10 @@ split_attn_kernel(const PrefillArgs a) {
   f4 o[TD];
 #pragma unroll
   for (int u = 0; u < TD; ++u) o[u] = f4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const f4 (&kr)[NK], const f4 (&vr)[4][NV], uint32_t b) {
+  // scores of block b (from its K rows), then its softmax weights
+  f4 pr;
+  float corr;
+  auto scores = [&](const f4 (&kr)[NK], uint32_t b) {
     const uint32_t kb = k0 + 16 * b;
     f4 s = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -448,11 +476,14 @@ split_attn_kernel(const PrefillArgs a) {
     const float m_new = fmaxf(m_run, mb);
     // a row may have no key yet in this chunk: keep everything at zero
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float corr = fast_exp2(m_run - m_use);
-    f4 pr;
+    corr = fast_exp2(m_run - m_use);
 #pragma unroll
     for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(s[r] - m_use);
     l_run = l_run * corr + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+    m_run = m_new;
+  };
+  // the weighted V rows of the block whose scores were taken last
+  auto accumulate = [&](const f4 (&vr)[4][NV]) {
 #pragma unroll
     for (int u = 0; u < TD; ++u) o[u] *= corr;
 #pragma unroll
@@ -462,26 +493,71 @@ split_attn_kernel(const PrefillArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           o[4 * x + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[m][x][e], pr[m], o[4 * x + e], 0, 0, 0);
-    m_run = m_new;
   };
 
-  // two register sets, A for even blocks and B for odd ones: the next
-  // block's loads are in flight while the current one is multiplied
+  // Two register sets, A for even blocks and B for odd ones.  A set's K
+  // rows are reloaded (for the block two ahead) as soon as its scores are
+  // taken and its V rows as soon as they are accumulated, so about three
+  // half-blocks are in flight while a block is multiplied.
   f4 ka[NK], va[4][NV], kb_[NK], vb[4][NV];
-  load(ka, va, 0);
+  if (active) {
+    load_k(ka, 0);
+    load_v(va, 0);
+    load_k(kb_, 1);
+    load_v(vb, 1);
+  }
   uint32_t b = 0;
   for (; b + 2 <= n_blk; b += 2) {
-    load(kb_, vb, b + 1);
     __builtin_amdgcn_sched_barrier(0);
-    compute(ka, va, b);
-    load(ka, va, b + 2);
+    scores(ka, b);
     __builtin_amdgcn_sched_barrier(0);
-    compute(kb_, vb, b + 1);
+    load_k(ka, b + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    accumulate(va);
+    __builtin_amdgcn_sched_barrier(0);
+    load_v(va, b + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    scores(kb_, b + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_k(kb_, b + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    accumulate(vb);
+    __builtin_amdgcn_sched_barrier(0);
+    load_v(vb, b + 3);
   }
-  if (b < n_blk) compute(ka, va, b);
+  if (b < n_blk) {
+    scores(ka, b);
+    accumulate(va);
+  }
 
   float L = l_run + __shfl_xor(l_run, 16);
   L += __shfl_xor(L, 32);
+  // waves 1..3 hand (acc, m, l) to wave 0, which rescales all four to their
+  // common maximum (an empty chunk, m = -inf, weighs 0) and adds them in
+  // wave order
+  if (w > 0) {
+#pragma unroll
+    for (int u = 0; u < TD; ++u) sh.acc[w - 1][u][lane] = o[u];
+    sh.m[w - 1][lane] = m_run;
+    sh.l[w - 1][lane] = L;
+  }
+  __syncthreads();
+  if (w > 0) return;
+  float mx = m_run;
+#pragma unroll
+  for (int v = 0; v < kAttnWaves - 1; ++v) mx = fmaxf(mx, sh.m[v][lane]);
+  const float base = mx == -INFINITY ? 0.f : mx;  // every chunk empty: all stays zero
+  const float s0 = fast_exp2(m_run - base);
+  L *= s0;
+#pragma unroll
+  for (int u = 0; u < TD; ++u) o[u] *= s0;
+#pragma unroll
+  for (int v = 0; v < kAttnWaves - 1; ++v) {
+    const float sv = fast_exp2(sh.m[v][lane] - base);
+    L += sh.l[v][lane] * sv;
+#pragma unroll
+    for (int u = 0; u < TD; ++u) o[u] += sh.acc[v][u][lane] * sv;
+  }
   float* acc = p.part + (static_cast<size_t>(item) * 16 + c) * D + DQ * g;
 #pragma unroll
   for (int r = 0; r < 4; ++r)
@@ -490,7 +566,7 @@ split_attn_kernel(const PrefillArgs a) {
       *reinterpret_cast<f4*>(acc + TD * r + u) = f4{o[u][r], o[u + 1][r], o[u + 2][r], o[u + 3][r]};
   if (g == 0) {
     float* ml = p.part + static_cast<size_t>(p.n_items) * 16 * D + (static_cast<size_t>(item) * 16 + c) * 2;
-    ml[0] = m_run;
+    ml[0] = mx;
     ml[1] = L;
   }
 }
@@ -515,9 +591,14 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) split_merge_kernel(const P
   const uint32_t j = h / G, R = t * G + h % G, tile = R / 16, c = R % 16;
   const uint32_t n_tiles = (T * G + 15) / 16;
   const uint32_t tile_keys = pos0 + min((tile * 16 + 15) / G, T - 1) + 1;
-  const uint32_t nck = (tile_keys + p.split_keys - 1) / p.split_keys;
-  const uint32_t first = a.s.item_off[sq] + j * n_tiles + tile;
-  const uint32_t stride = p.n_kv_heads * n_tiles;  // from one chunk's item to the next
+  // split-K partials are per group of kAttnWaves chunks (j-major items);
+  // chunked tiled ones per chunk (chunk-major items)
+  const bool grouped = p.n_groups == 0;
+  const uint32_t span = grouped ? p.split_keys * kAttnWaves : p.split_keys;
+  const uint32_t nck = (tile_keys + span - 1) / span;
+  const uint32_t first = grouped ? a.s.item_off[sq] + (j * n_tiles + tile) * split_groups(pos0 + T, p.split_keys)
+                                 : a.s.item_off[sq] + j * n_tiles + tile;
+  const uint32_t stride = grouped ? 1 : p.n_kv_heads * n_tiles;  // from one partial to the next
   const float* ml = p.part + static_cast<size_t>(p.n_items) * 16 * D;
   auto at = [&](uint32_t k) { return static_cast<size_t>(first + k * stride) * 16 + c; };
   // the maximum over the chunks (finite: chunk 0 holds key 0) and the sink
@@ -572,8 +653,7 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) split_merge_kernel(const P
 
 template <int D, int G>
 hipError_t launch_split(const PrefillArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((split_attn_kernel<D, G>), dim3((a.p.n_items + kAttnWaves - 1) / kAttnWaves),
-                     dim3(kWave * kAttnWaves), 0, s, a);
+  hipLaunchKernelGGL((split_attn_kernel<D, G>), dim3(a.p.n_items), dim3(kWave * kAttnWaves), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint32_t waves = a.p.n_rows * a.p.n_heads;
