@@ -674,6 +674,12 @@ int run_prefill(slot_kv* h, uint32_t layer, const float* q, const float* k_new,
     }
     p.n_seq = n;
     p.n_rows = rows;
+    // prep: one vector per wave while that keeps the workgroups few (up to
+    // about 2048, 8 per CU); more per wave for long calls
+    {
+      const uint32_t n_vec4 = (L.n_heads + L.n_kv_heads + 3) / 4;
+      p.prep_vpw = std::max<uint32_t>(1, std::min<uint32_t>(n_vec4, rows * n_vec4 / 2048));
+    }
     p.q = q + first_row * qd;
     p.k_new = k_new + static_cast<size_t>(first_row) * L.kv_dim;
     p.v_new = v_new + static_cast<size_t>(first_row) * L.kv_dim;

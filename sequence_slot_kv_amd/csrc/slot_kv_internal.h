@@ -100,6 +100,7 @@ struct PrefillParams {
   float eps;
   float qk_scale_log2;     // scale * log2(e)
   uint32_t flags;          // SLOT_KV_FLAG_*
+  uint32_t prep_vpw;       // head vectors per wave of the prep kernel
 };
 
 struct PrefillSeqs {

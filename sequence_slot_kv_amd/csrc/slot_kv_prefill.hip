@@ -5,11 +5,10 @@
 // one-token step run over the tokens in order; the other system's batched
 // verify of ks[i] consecutive rows for each of n_seqs sequences).
 //
-// Two launches on the caller's stream:
-//   prep  one workgroup per token row: cos / sin of the row's angles once in
-//         LDS, then one wave per head vector: RMSNorm and RoPE; a query head
-//         goes to a scratch buffer (times scale*log2(e)), a key head and its
-//         value row go into the slot.
+// Launches on the caller's stream:
+//   prep  one wave per head vector of every token row: RMSNorm and RoPE; a
+//         query head goes to a scratch buffer (times scale*log2(e)), a key
+//         head and its value row go into the slot.
 //   attn  causal attention of every row over its slot's positions
 //         0 .. pos0+t, now all in the cache.  Many query rows meet each key
 //         block, so this is a dense contraction and runs on the matrix cores:
@@ -52,18 +51,26 @@ __device__ __forceinline__ uint32_t seq_of_row(const PrefillArgs& a, uint32_t ro
   return lo;
 }
 
-// One workgroup per token row.  Lane l of a wave holds elements
-// l*EPL .. l*EPL+EPL-1 of a head vector, so the RoPE partner d +- D/2 of an
-// element sits in lane l ^ 32 and both use angle (l & 31)*EPL + e; with
-// interleaved pairs the partner d ^ 1 is the neighbouring element of the lane
-// (lane l ^ 1 when a lane holds one) and the angle is d / 2.
+// A workgroup takes 4 * prep_vpw head vectors of a token row (the row's
+// n_heads query heads, then its n_kv_heads key heads), wave w the vectors
+// w, w + 4, ...; prep_vpw is 1 for calls of a few hundred rows, so that they
+// spread over the whole chip, and larger for long ones.  The workgroup first puts
+// the cos / sin of the row's D/2 angles in LDS.  Lane l holds elements
+// l*EPL .. l*EPL+EPL-1 of the vector; the RoPE partner d +- D/2 of an
+// element sits in lane l ^ 32 with the same angle, and with interleaved
+// pairs the partner d ^ 1 is the neighbouring element of the lane (lane
+// l ^ 1 when a lane holds one) and the angle that of d / 2.
 template <int D>
 __global__ void __launch_bounds__(kWave * kPrepWaves) prefill_prep_kernel(const PrefillArgs a) {
   constexpr int EPL = D / kWave;
   __shared__ float cs[D / 2], sn[D / 2];
   if (a.magic != kArgsMagic) return;  // argument block not delivered whole
   const PrefillParams& p = a.p;
-  const uint32_t row = blockIdx.x;  // < n_rows
+  const uint32_t n_vec = p.n_heads + p.n_kv_heads;
+  const uint32_t per_wg = kPrepWaves * p.prep_vpw;
+  const uint32_t per_row = (n_vec + per_wg - 1) / per_wg;
+  const uint32_t row = blockIdx.x / per_row;  // < n_rows
+  const uint32_t v0 = (blockIdx.x - row * per_row) * per_wg + threadIdx.x / kWave;
   const uint32_t i = seq_of_row(a, row);
   const uint32_t t = row - a.s.row_off[i];
   const uint32_t pos = a.s.pos0[i] + t;
@@ -78,14 +85,14 @@ __global__ void __launch_bounds__(kWave * kPrepWaves) prefill_prep_kernel(const 
   __syncthreads();
   const uint32_t lane = threadIdx.x % kWave;
   const uint64_t at_row = a.s.slot[i] * p.slot_stride + static_cast<uint64_t>(pos) * p.kv_dim;
-  for (uint32_t v = threadIdx.x / kWave; v < p.n_heads + p.n_kv_heads; v += kPrepWaves) {
+  const float one = (p.flags & SLOT_KV_FLAG_NORM_ONE_PLUS_W) ? 1.f : 0.f;
+  const bool inter = p.flags & SLOT_KV_FLAG_ROPE_INTERLEAVED;  // uniform
+  for (uint32_t v = v0; v < min(v0 + per_wg, n_vec); v += kPrepWaves) {  // wave-uniform
     const bool is_q = v < p.n_heads;  // wave-uniform
     const uint32_t kvh = v - p.n_heads;
     const float* src = is_q ? p.q + (static_cast<size_t>(row) * p.n_heads + v) * D
                             : p.k_new + static_cast<size_t>(row) * p.kv_dim + kvh * D;
     const float* w = is_q ? p.q_norm_w : p.k_norm_w;
-    const float one = (p.flags & SLOT_KV_FLAG_NORM_ONE_PLUS_W) ? 1.f : 0.f;
-    const bool inter = p.flags & SLOT_KV_FLAG_ROPE_INTERLEAVED;  // uniform
     float x[EPL];
     float ss = 0.f;
 #pragma unroll
@@ -683,7 +690,10 @@ hipError_t launch_attn(const PrefillArgs& a, hipStream_t s) {
 template <int D>
 hipError_t launch_d(const PrefillArgs& a, uint32_t G, bool split, hipStream_t s,
                     hipEvent_t before, hipEvent_t after) {
-  hipLaunchKernelGGL((prefill_prep_kernel<D>), dim3(a.p.n_rows), dim3(kWave * kPrepWaves), 0, s, a);
+  const uint32_t per_wg = kPrepWaves * a.p.prep_vpw;
+  const uint32_t per_row = (a.p.n_heads + a.p.n_kv_heads + per_wg - 1) / per_wg;
+  hipLaunchKernelGGL((prefill_prep_kernel<D>), dim3(a.p.n_rows * per_row), dim3(kWave * kPrepWaves), 0,
+                     s, a);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && before) e = hipEventRecord(before, s);
   if (e != hipSuccess) return e;
