@@ -199,8 +199,14 @@ int slot_decode_attn(slot_kv *h, uint32_t layer, const float *q,
  *   out    device [T][n_heads*head_dim]; must not overlap q, k_new or v_new
  *   stream hipStream_t (NULL = the null stream)
  * Requires history rows 0..pos0-1 of the slot to hold the sequence's keys and
- * values.  The handle keeps a scratch buffer of T*n_heads*head_dim floats for
- * the rotated queries (grown on demand).  T == 0 is a no-op.  Errors:
+ * values.  The handle keeps a scratch buffer (grown on demand, freed with
+ * the handle) for the rotated queries, T*n_heads*head_dim floats, and, when
+ * the keys are cut into chunks, the chunks' partial results: at most 16,384
+ * items of 16*(head_dim+2) floats per launch.  Calls with at most 64 query
+ * rows per kv head (T * n_heads / n_kv_heads <= 64) run the split-K kernel;
+ * longer ones the tiled kernel, cut into key chunks when it would have
+ * fewer than 512 workgroups.  Results do not depend on which is taken
+ * beyond f32 rounding.  T == 0 is a no-op.  Errors:
  * ENOTALLOC, EINVAL (layer unconfigured or head shape unsupported, NULL
  * pointer), ERANGE (slot >= n_slots or pos0 + T > slot_ctx), ENOMEM, EDEVICE.
  * Nothing is written when an error is returned. */
@@ -218,10 +224,13 @@ int slot_prefill_attn(slot_kv *h, uint32_t layer, const float *q,
  *   slots, pos0, ks  host [n_seq]; copied before the call returns
  *   q, out  device [sum ks][n_heads*head_dim]   k_new, v_new  device [sum ks][kv_dim]
  * Sequences with ks[i] == 0 contribute no rows (their slot and position are
- * still checked).  n_seq == 0 is a no-op.  Errors: ENOTALLOC, EINVAL (layer
- * unconfigured or head shape unsupported, NULL pointer), ERANGE (a slot >=
- * n_slots or pos0[i] + ks[i] > slot_ctx), EDUP (a slot repeated), ENOMEM,
- * EDEVICE.  Nothing is written when an error is returned. */
+ * still checked).  Scratch and kernel choice are those of slot_prefill_attn,
+ * with the split-K kernel taken when every sequence has at most 64 query rows
+ * per kv head; one launch per 128 sequences.  n_seq == 0 is a no-op.
+ * Errors: ENOTALLOC, EINVAL (layer unconfigured or head shape unsupported,
+ * NULL pointer), ERANGE (a slot >= n_slots or pos0[i] + ks[i] > slot_ctx),
+ * EDUP (a slot repeated), ENOMEM, EDEVICE.  Nothing is written when an error
+ * is returned. */
 int slot_verify_attn(slot_kv *h, uint32_t layer, const float *q,
                      const float *k_new, const float *v_new, const uint32_t *slots,
                      const uint32_t *pos0, const uint32_t *ks, uint32_t n_seq,
@@ -229,7 +238,8 @@ int slot_verify_attn(slot_kv *h, uint32_t layer, const float *q,
 
 /* Device pointers of layer `layer`'s K and V buffers ([n_slots][slot_ctx]
  * [kv_dim] floats each; owned by the handle, valid until the next
- * slot_kv_alloc or slot_kv_destroy).  Errors: ENOTALLOC, EINVAL. */
+ * slot_kv_alloc / slot_state_alloc or slot_kv_destroy).  Errors: ENOTALLOC,
+ * EINVAL. */
 int slot_kv_layer_ptrs(const slot_kv *h, uint32_t layer, float **k, float **v);
 
 /* Copy n_rows consecutive K and V rows (kv_dim floats each) from device
