@@ -64,7 +64,10 @@ MFMA_F32_PEAK_TFLOPS = 157.3
 PREFILL_METRIC = "slot prefill tokens/s and attention TFLOP/s (f32 matrix cores)"
 VERIFY_METRIC = "multi-row verify rows/s and achieved KV HBM GB/s (% of peak)"
 STATE_METRIC = "slot resets/s on admit and achieved HBM write GB/s (% of peak)"
-KERNEL_SRC = os.path.join(ROOT, "sequence_slot_kv_amd", "csrc", "slot_kv_kernels.hip")
+CSRC = os.path.join(ROOT, "sequence_slot_kv_amd", "csrc")
+KERNEL_SRC = os.path.join(CSRC, "slot_kv_kernels.hip")
+PREFILL_SRC = os.path.join(CSRC, "slot_kv_prefill.hip")
+STATE_SRC = os.path.join(CSRC, "slot_kv_state.hip")
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
@@ -72,21 +75,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_hash(src: str = KERNEL_SRC) -> str:
+    with open(src, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of the fused kernel from the committed rocprofv3
-    counter record, or None when there is none for this workload or the
-    kernel source changed since it was taken."""
+def measured_traffic(workload: str, src: str = KERNEL_SRC):
+    """HBM bytes per launch of the workload's dominant kernel from the
+    committed rocprofv3 counter record, or None when there is none for this
+    workload or the kernel source `src` changed since it was taken."""
     try:
         rec = json.load(open(TRAFFIC_RECORD))
     except (OSError, ValueError):
         return None
     entry = rec.get(workload)
-    if not entry or entry.get("kernel_sha256_16") != kernel_hash():
+    if not entry or entry.get("kernel_sha256_16") != kernel_hash(src):
         return None
     return entry.get("hbm_bytes_per_launch")
 
@@ -437,8 +440,9 @@ def verify_bench(args, w, b):
                    "n_kv_heads": L.n_kv_heads, "head_dim": L.head_dim, "seed": w.seed},
         "kv_bytes_per_step": w.kv_bytes(),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "kernel": "prefill_attn_kernel", "kernel_us": attn_us},
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(w.name, PREFILL_SRC),
+                     "kernel": "split_attn_kernel + split_merge_kernel", "kernel_us": attn_us},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
@@ -513,7 +517,8 @@ def state_bench(args, w, b):
                    "ssm_state_len": w.ssm_state_len[0], "seed": w.seed},
         "write_bytes_per_step": w.write_bytes(),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(w.name, STATE_SRC),
                      "kernel": "state_reset_kernel", "kernel_us": k_us},
         "cpu_baseline": cpu,
     }
