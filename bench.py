@@ -68,6 +68,9 @@ CSRC = os.path.join(ROOT, "sequence_slot_kv_amd", "csrc")
 KERNEL_SRC = os.path.join(CSRC, "slot_kv_kernels.hip")
 PREFILL_SRC = os.path.join(CSRC, "slot_kv_prefill.hip")
 STATE_SRC = os.path.join(CSRC, "slot_kv_state.hip")
+# launch-shaping constants (chunk size, waves per workgroup, row tables) that
+# every kernel is built with
+INTERNAL_H = os.path.join(CSRC, "slot_kv_internal.h")
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
@@ -76,8 +79,13 @@ def log(*a):
 
 
 def kernel_hash(src: str = KERNEL_SRC) -> str:
-    with open(src, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel's source file and of the internal header it is built
+    with: a counter record stays valid only while both are unchanged."""
+    h = hashlib.sha256()
+    for path in (src, INTERNAL_H):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str, src: str = KERNEL_SRC):

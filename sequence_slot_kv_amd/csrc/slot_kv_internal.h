@@ -8,7 +8,7 @@
 #include "slot_kv.h"
 
 #ifndef SLOT_KV_CHUNK
-#define SLOT_KV_CHUNK 512  // keys per split-K chunk (a multiple of 64)
+#define SLOT_KV_CHUNK 1024  // keys per split-K chunk (a multiple of 64)
 #endif
 #ifndef SLOT_KV_WG_WAVES
 #define SLOT_KV_WG_WAVES 4  // waves of one workgroup sharing a chunk
@@ -28,6 +28,38 @@ struct LaunchRows {
   uint8_t tail_row[kMaxRowsPerLaunch];          // rows owning a partial chunk, longest first
 };
 static_assert(offsetof(LaunchRows, tail_row) % 4 == 0, "tail_row is read through 32-bit words");
+
+#if defined(__HIPCC__)
+#define SLOTKV_HD __host__ __device__
+#else
+#define SLOTKV_HD
+#endif
+
+// Byte k of a row table, through its aligned word (on the device the read
+// stays a scalar load).
+SLOTKV_HD inline uint32_t row_byte(const uint8_t* table, uint32_t k) {
+  const uint32_t word = reinterpret_cast<const uint32_t*>(table)[k / 4];
+  return (word >> (8 * (k % 4))) & 0xffu;
+}
+
+// Row and chunk of queue item `item` (< n_full + the rows' partial chunks).
+SLOTKV_HD inline void locate_item(const LaunchRows& rows, uint32_t n_rows, uint32_t n_full,
+                                  uint32_t chunk, uint32_t item, uint32_t* row,
+                                  uint32_t* chunk_index) {
+  if (item < n_full) {
+    // full chunk: the last row whose first full chunk is <= item
+    uint32_t blo = 0, bhi = n_rows;
+    while (bhi - blo > 1) {
+      const uint32_t mid = (blo + bhi) / 2;
+      if (rows.full_prefix[mid] <= item) blo = mid; else bhi = mid;
+    }
+    *row = blo;
+    *chunk_index = item - rows.full_prefix[blo];
+  } else {
+    *row = row_byte(rows.tail_row, item - n_full);
+    *chunk_index = rows.pos[*row] / chunk;  // the partial last chunk
+  }
+}
 
 // Kernel-side parameters of one decode launch (rows 0..n_rows-1 of it).
 struct AttnParams {
@@ -138,7 +170,7 @@ constexpr uint32_t kSplitMaxRows = 64;
 // tile), ordered item_off[i] + (j * n_tiles + tile) * groups + group, and
 // leave one partial each.
 constexpr uint32_t kSplitChunksPerGroup = 4;
-__host__ __device__ inline uint32_t split_groups(uint32_t keys, uint32_t split_keys) {
+SLOTKV_HD inline uint32_t split_groups(uint32_t keys, uint32_t split_keys) {
   const uint32_t chunks = (keys + split_keys - 1) / split_keys;
   return (chunks + kSplitChunksPerGroup - 1) / kSplitChunksPerGroup;
 }

@@ -188,23 +188,7 @@ __device__ __forceinline__ UnitId locate_unit(const AttnArgs& a, uint32_t unit) 
   const AttnParams& p = a.p;
   UnitId id;
   id.j = unit % p.n_kv_heads;
-  const uint32_t item = unit / p.n_kv_heads;
-  if (item < p.n_full) {
-    // full chunk: the last row whose first full chunk is <= item
-    uint32_t blo = 0, bhi = p.n_rows;
-    while (bhi - blo > 1) {
-      const uint32_t mid = (blo + bhi) / 2;
-      if (a.rows.full_prefix[mid] <= item) blo = mid; else bhi = mid;
-    }
-    id.b = blo;
-    id.chunk = item - a.rows.full_prefix[id.b];
-  } else {
-    // the byte through its aligned word, so that the read stays a scalar load
-    const uint32_t t = item - p.n_full;
-    const uint32_t word = reinterpret_cast<const uint32_t*>(a.rows.tail_row)[t / 4];
-    id.b = (word >> (8 * (t % 4))) & 0xffu;
-    id.chunk = a.rows.pos[id.b] / p.chunk;  // the partial last chunk
-  }
+  locate_item(a.rows, p.n_rows, p.n_full, p.chunk, unit / p.n_kv_heads, &id.b, &id.chunk);
   return id;
 }
 

@@ -42,11 +42,12 @@ def _handle(n_slots, slot_ctx, L, ck, cv):
 @pytest.mark.parametrize("H,Hkv,D", [(4, 2, 64), (8, 2, 128), (4, 2, 256)])
 def test_decode_with_flags(flags, H, Hkv, D):
     rng = np.random.default_rng(50 + flags + D)
-    n_slots, slot_ctx, B = 6, 700, 5   # rows up to two 512-key chunks
+    C = b.slot_kv_chunk_keys()
+    n_slots, slot_ctx, B = 6, C + 188, 5   # rows of one and of two split-K chunks
     L = _layer(rng, H, Hkv, D, flags, sinks=True)
     ck, cv = _cache(rng, n_slots, slot_ctx, L.kv_dim)
     slots = rng.permutation(n_slots)[:B].astype(np.uint32)
-    positions = np.array([0, 1, 37, 511, 699], np.uint32)
+    positions = np.array([0, 1, 37, C - 1, C + 187], np.uint32)
     q = rng.standard_normal((B, H * D), dtype=np.float32)
     kn = rng.standard_normal((B, L.kv_dim), dtype=np.float32)
     vn = rng.standard_normal((B, L.kv_dim), dtype=np.float32)

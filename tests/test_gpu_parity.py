@@ -339,14 +339,15 @@ def test_layer_stack_sampled_parity():
 @pytest.mark.parametrize("G", [1, 2, 4, 8])
 def test_decode_shapes_full_parity(D, G):
     # Each (head_dim, group) instantiation of the decode kernel: rows of one
-    # key, rows at both sides of the 512-key chunk boundaries (split rows
+    # key, rows at both sides of the split-K chunk boundaries (split rows
     # merged by the last workgroup), every cache cell outside 0..pos poisoned.
     Hkv = 2
     H = G * Hkv
     rng = np.random.default_rng(300 + 10 * G + D)
-    n_slots, slot_ctx = 8, 1200
+    C = b.slot_kv_chunk_keys()
+    n_slots, slot_ctx = 8, 2 * C + 176
     L = wl.make_layer(rng, H, Hkv, D, 1e4, G % 2 == 0)
-    positions = np.array([0, 1, 511, 512, 1023, 1199], np.uint32)
+    positions = np.array([0, 1, C - 1, C, 2 * C - 1, 2 * C + 175], np.uint32)
     slots = rng.permutation(n_slots)[:positions.size].astype(np.uint32)
     B = positions.size
     q = rng.standard_normal((B, H * D), dtype=np.float32)
@@ -377,10 +378,11 @@ def test_decode_more_rows_than_one_launch():
     # its own row table; every row is checked against the oracle.
     rng = np.random.default_rng(400)
     H, Hkv, D = 8, 2, 64
-    n_slots, slot_ctx, B = 300, 640, 300
+    C = b.slot_kv_chunk_keys()
+    n_slots, slot_ctx, B = 300, C + 128, 300  # rows of one and of two split-K chunks
     L = wl.make_layer(rng, H, Hkv, D, 1e4, True)
     positions = rng.integers(0, slot_ctx, size=B).astype(np.uint32)
-    positions[:3] = [0, 511, slot_ctx - 1]
+    positions[:3] = [0, C - 1, slot_ctx - 1]
     slots = rng.permutation(n_slots)[:B].astype(np.uint32)
     q = rng.standard_normal((B, H * D), dtype=np.float32)
     kn = rng.standard_normal((B, L.kv_dim), dtype=np.float32)

@@ -1,0 +1,105 @@
+"""Host logic of the decode kernel's work queue (no GPU).
+
+The decode kernel cuts each row b of a call into ceil((pos_b + 1) / C) key
+chunks and each chunk into one unit per kv head; workgroups take the units
+in queue order.  Whatever the order, every (row, chunk) must be queued
+exactly once, or a part of some row's history would be skipped or counted
+twice.  This compiles the library's plain C++ planner (slot_kv_plan.cpp)
+with a small driver that walks the queue through the same lookup the kernel
+uses (locate_item) and checks coverage and the stated order: every full
+chunk, row by row, then each row's shorter last chunk, longest first.
+"""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "sequence_slot_kv_amd", "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+
+DRIVER = r"""
+#include <cstdio>
+#include <vector>
+#include "slot_kv_internal.h"
+int main() {
+  unsigned n, chunk;
+  if (std::scanf("%u %u", &n, &chunk) != 2) return 2;
+  std::vector<uint32_t> pos(n), slot(n);
+  for (unsigned b = 0; b < n; ++b) { if (std::scanf("%u", &pos[b]) != 1) return 2; slot[b] = b; }
+  static slotkv::LaunchRows rows;
+  slotkv::LaunchWork w = slotkv::fill_rows(rows, pos.data(), slot.data(), n, chunk);
+  std::printf("%u %u %u\n", w.n_full, w.n_items, w.max_chunks);
+  for (uint32_t it = 0; it < w.n_items; ++it) {
+    uint32_t b, c;
+    slotkv::locate_item(rows, n, w.n_full, chunk, it, &b, &c);
+    std::printf("%u %u\n", b, c);
+  }
+  return 0;
+}
+"""
+
+
+@pytest.fixture(scope="module")
+def planner(tmp_path_factory):
+    d = tmp_path_factory.mktemp("plan")
+    src = d / "driver.cpp"
+    src.write_text(DRIVER)
+    exe = d / "driver"
+    subprocess.run(["g++", "-O1", "-std=c++17", "-I", INCLUDE, "-I", CSRC, str(src),
+                    os.path.join(CSRC, "slot_kv_plan.cpp"), "-o", str(exe)],
+                   check=True, capture_output=True)
+
+    def run(positions, chunk):
+        inp = f"{len(positions)} {chunk}\n" + " ".join(str(int(p)) for p in positions) + "\n"
+        r = subprocess.run([str(exe)], input=inp, capture_output=True, text=True, check=True)
+        lines = r.stdout.split("\n")
+        n_full, n_items, max_chunks = map(int, lines[0].split())
+        items = [tuple(map(int, ln.split())) for ln in lines[1:1 + n_items]]
+        return n_full, max_chunks, items
+    return run
+
+
+def check_plan(positions, chunk, run):
+    positions = np.asarray(positions, dtype=np.int64)
+    n_full, max_chunks, items = run(positions, chunk)
+    n_chunks = positions // chunk + 1
+    tail = (positions + 1) % chunk
+    # coverage: every (row, chunk) exactly once
+    want = sorted((b, c) for b in range(len(positions)) for c in range(n_chunks[b]))
+    assert sorted(items) == want
+    assert max_chunks == (n_chunks.max() if len(positions) else 0)
+    assert n_full == int(((positions + 1) // chunk).sum())
+    full, late = items[:n_full], items[n_full:]
+    # full chunks: row-major, each row's chunks in order
+    assert full == sorted(full)
+    for b, c in full:
+        assert (c + 1) * chunk <= positions[b] + 1
+    # then every partial last chunk, longest first (ties in row order)
+    for b, c in late:
+        assert c == n_chunks[b] - 1 and tail[b] > 0
+    assert [b for b, _ in late] == sorted((b for b, _ in late), key=lambda b: (-tail[b], b))
+
+
+def test_plan_mixed_lengths(planner):
+    rng = np.random.default_rng(11)
+    pos = np.floor(np.exp(rng.uniform(0, np.log(32768), 16))).astype(np.int64).clip(1, 32767)
+    for C in (512, 1024):
+        check_plan(pos, C, planner)
+
+
+def test_plan_uniform_rows(planner):
+    rng = np.random.default_rng(12)
+    for C in (512, 1024):
+        check_plan(rng.integers(1, 4096, 64), C, planner)
+
+
+def test_plan_edges(planner):
+    # pos 0, exact multiples of the chunk (no partial chunk), one key short
+    # of a multiple, the largest launch
+    check_plan([0, 511, 512, 1023, 8 * 512 - 1, 8 * 512, 9 * 512 - 1, 9 * 512, 65535], 512, planner)
+    check_plan([0], 512, planner)
+    rng = np.random.default_rng(13)
+    check_plan(rng.integers(0, 1 << 17, 256), 512, planner)
+    check_plan(rng.integers(0, 64, 256), 64, planner)
