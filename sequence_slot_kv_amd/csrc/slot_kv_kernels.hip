@@ -5,7 +5,8 @@
 //
 // One persistent launch does the whole step.  The work is cut into units
 // (row b, chunk c of C keys, kv head j); the NW waves of a workgroup split a
-// unit's keys, wave w taking [c*C + w*C/NW, c*C + (w+1)*C/NW).  Workgroups
+// unit's keys evenly (whole pipeline stages each; C/NW keys per wave in a
+// full chunk).  Workgroups
 // pull units from an agent-scope queue (full chunks first, then partial
 // chunks longest first) and keep it one unit ahead, so that:
 //   - the next unit's query heads (and new key) are normalised, rotated and
@@ -205,9 +206,13 @@ __device__ __forceinline__ UnitPlan plan_unit(const AttnArgs& a, const UnitId& i
   u.n_chunks = u.pos / p.chunk + 1;
   const uint32_t c0 = u.chunk * p.chunk;
   const uint32_t t_end = min(c0 + p.chunk, u.pos);
-  const uint32_t per_wave = p.chunk / NW;
-  u.k_begin = min(c0 + w * per_wave, t_end);
-  u.len = min(c0 + (w + 1) * per_wave, t_end) - u.k_begin;
+  // The chunk's history keys, in pipeline stages of STEP keys, split as
+  // evenly as whole stages allow over the NW waves: a short last chunk keeps
+  // every wave busy (a full chunk gives each wave C/NW keys).
+  const uint32_t n_keys = t_end - c0;
+  const uint32_t steps = (n_keys + S::STEP - 1) / S::STEP;
+  u.k_begin = c0 + min(steps * w / NW * S::STEP, n_keys);
+  u.len = c0 + min(steps * (w + 1) / NW * S::STEP, n_keys) - u.k_begin;
   u.n_full = u.len / S::STEP;
   // stages per pass, rounded up to an even count (the stages past the keys
   // are masked) so that each pass ends in the same buffer
