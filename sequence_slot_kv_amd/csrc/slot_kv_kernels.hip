@@ -6,11 +6,11 @@
 // One persistent launch does the whole step.  The work is cut into units
 // (row b, chunk c of C keys, kv head j); the NW waves of a workgroup split a
 // unit's keys evenly (whole pipeline stages each; C/NW keys per wave in a
-// full chunk).  Workgroups
-// pull units from an agent-scope queue (full chunks first, then partial
-// chunks longest first) and keep it one unit ahead, so that:
+// full chunk).  Workgroups pull units from an agent-scope queue (full
+// chunks first, then partial chunks longest first), asking for the next one
+// when the current unit's second pass starts, so that:
 //   - the next unit's query heads (and new key) are normalised, rotated and
-//     staged in LDS while the current unit streams; the unit that holds a
+//     staged in LDS before the current unit ends; the unit that holds a
 //     row's last chunk also writes the row's KV entry -- rotated key and
 //     v_new at (slot*slot_ctx + pos)*kv_dim -- from that staging step;
 //   - the next unit's first K stage is in flight while the current unit
@@ -414,10 +414,10 @@ __device__ __forceinline__ void merge_row(const AttnParams& p, uint32_t b, uint3
 
 // Persistent decode kernel: as many workgroups as are resident at once.
 // Workgroup g starts with unit g, then takes units from an agent-scope queue.
-// Each unit asks the queue for the one after it as it starts; wave 0 posts
-// the answer in an LDS mailbox after its first K stages and the other waves
-// read it there, so every workgroup holds at most one unit it has not begun,
-// and only for the second half of a unit.  Units are ordered full chunks
+// Each unit asks the queue for the one after it when its second pass starts;
+// wave 0 posts the answer in an LDS mailbox before its last V stage and the
+// other waves read it there, so every workgroup holds at most one unit it has
+// not begun, and only while its second pass runs.  Units are ordered full chunks
 // first, then partial chunks longest first, so the work left at the end is
 // short.  The last workgroup to exit returns the queue to zero for the next
 // launch.  No workgroup ever waits for another.  A row of one chunk is
@@ -457,10 +457,16 @@ __global__ void __launch_bounds__(kThreads)
 
   for (uint32_t it = 0;; ++it) {  // workgroup-uniform
     const uint32_t par = it & 1;
-    // the unit after this one: asked for now, read after the first K stages
+    // The unit after this one is asked for when pass 2 starts and read before
+    // the last V stage is consumed: the atomic's round trip hides behind the
+    // V stages, and a workgroup holds a unit it has not begun only for the
+    // end of the current one, so that few units sit reserved when the queue
+    // runs dry.
     uint32_t ticket = 0;
-    if (tid == 0)
-      ticket = __hip_atomic_fetch_add(&p.sched[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    auto ask_next = [&]() {
+      if (tid == 0)
+        ticket = __hip_atomic_fetch_add(&p.sched[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
     uint32_t nxt = kNoUnit;
     bool has_next = false;
     UnitId un{};
@@ -478,7 +484,7 @@ __global__ void __launch_bounds__(kThreads)
       has_next = nxt < p.n_units;
       if (has_next) {
         un = locate_unit(a, nxt);
-        prep_issue<D, G>(a, un, w, lane, praw);  // consumed after pass 1
+        prep_issue<D, G>(a, un, w, lane, praw);  // consumed after the wave merge
       }
     };
 
@@ -588,9 +594,7 @@ __global__ void __launch_bounds__(kThreads)
     // stages; stage index qi < n_st is K stage qi, qi >= n_st is V stage
     // qi - n_st.  n_st is even, so each pass starts in A.  The last V stage
     // is consumed with nothing behind it; the next unit's first K stage goes
-    // out once this unit's results are stored.  The staging of the next
-    // unit's queries sits on both sides of the branch so that its wait for
-    // their loads only covers the loads issued before them.
+    // out once this unit's results are stored.
     const uint32_t n_st = u.n_st;
     if (n_st > 0) {  // wave-uniform
       // pass 1; the next unit is taken between the first two stages (loads
@@ -598,7 +602,6 @@ __global__ void __launch_bounds__(kThreads)
       // leaves the stage in flight alone)
       load_stage<D, G>(p, u, gi, lo, B, 1);
       score(A, 0);
-      take_next();
       load_stage<D, G>(p, u, gi, lo, A, 2);  // V stage 0 when n_st == 2
       score(B, 1);
       for (uint32_t st = 2; st < n_st; st += 2) {
@@ -608,7 +611,7 @@ __global__ void __launch_bounds__(kThreads)
         score(B, st + 1);
       }
       finish_max();
-      if (has_next) prep_finish<D, G>(a, un, w, lane, praw, pconst, prep, par ^ 1u);
+      ask_next();
       uint32_t st = 0;
       for (; st + 2 < n_st; st += 2) {  // pass 2 while two more stages follow
         load_stage<D, G>(p, u, gi, lo, B, n_st + st + 1);
@@ -618,11 +621,12 @@ __global__ void __launch_bounds__(kThreads)
       }
       load_stage<D, G>(p, u, gi, lo, B, n_st + st + 1);  // the last stage
       accumulate(A, st);
+      take_next();
       accumulate(B, st + 1);
     } else {
+      ask_next();
       take_next();
       finish_max();
-      if (has_next) prep_finish<D, G>(a, un, w, lane, praw, pconst, prep, par ^ 1u);
     }
     if (u.new_key && gi == 0) {
       f4 vn[NV4];
@@ -710,6 +714,8 @@ __global__ void __launch_bounds__(kThreads)
 #endif
       }
     }
+    // the next unit's queries: their raw loads went out with take_next
+    if (has_next) prep_finish<D, G>(a, un, w, lane, praw, pconst, prep, par ^ 1u);
     // the next unit's first K stage into A
     auto prefetch_next = [&]() {
       if (has_next) {
