@@ -23,7 +23,8 @@
 // LDS), merge; a row of one chunk is finished with its sink; a longer row's
 // chunk leaves an unnormalised partial (acc, max, sum) through agent-coherent
 // stores and the last workgroup of that (row, kv head) -- an agent-scope
-// counter decides -- merges the row's partials in chunk order.
+// counter, bumped one unit later when the stores are long complete, decides
+// -- merges the row's partials in chunk order.
 // Chunk boundaries depend only on the row's position, every merge runs in a
 // fixed order and no result depends on which workgroup ran a unit, so a
 // row's result does not depend on the rest of the batch.
@@ -454,6 +455,11 @@ __global__ void __launch_bounds__(kThreads)
   prep_issue<D, G>(a, first, w, lane, praw);
   prep_finish<D, G>(a, first, w, lane, praw, pconst, prep, 0);
   __syncthreads();
+  // The split-row partial this workgroup stored last, whose counter increment
+  // is still due (workgroup-uniform).  It is made one unit later, when the
+  // stores have long completed, so no unit waits for its own stores.
+  bool pending = false;
+  uint32_t pend_b = 0, pend_j = 0, pend_n = 0;
 
   for (uint32_t it = 0;; ++it) {  // workgroup-uniform
     const uint32_t par = it & 1;
@@ -672,7 +678,23 @@ __global__ void __launch_bounds__(kThreads)
         sh.l[w][g] = l[g];
       }
     }
+#if SLOT_KV_FUSED_MERGE
+    // The previous unit's partial stores were issued a whole unit ago; once
+    // every wave has waited for them (nothing else of note is in flight
+    // here) they are visible on every XCD, and the counter increment after
+    // the barrier publishes them.  Its result is read at the end of this unit.
+    if (pending) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+#endif
     __syncthreads();
+#if SLOT_KV_FUSED_MERGE
+    uint32_t done_prev = 0;
+    if (pending && tid == 0)
+      done_prev = __hip_atomic_fetch_add(&p.counters[pend_b * p.n_kv_heads + pend_j], 1u,
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#endif
     const uint32_t h0 = u.j * G;
     const bool split = u.n_chunks > 1;
     for (uint32_t e = tid; e < G * D; e += kThreads) {
@@ -723,36 +745,24 @@ __global__ void __launch_bounds__(kThreads)
         if (nu.n_st > 0) load_stage<D, G>(p, nu, gi, lo, A, 0);
       }
     };
+    prefetch_next();
 #if SLOT_KV_FUSED_MERGE
-    if (split) {  // workgroup-uniform
-      // The partials above are agent-coherent stores; once every wave's
-      // stores have completed (waitcnt) they are visible on every XCD, so
-      // the counter increment after the barrier publishes them.  The last
-      // workgroup of the (row, kv head) merges the row's chunks in order.
-      // No history load is in flight here, so the wait costs only the stores.
-      // The next unit's first K stage goes out while the counter's round
-      // trip is pending.
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      uint32_t done = 0;
-      if (tid == 0)
-        done = __hip_atomic_fetch_add(&p.counters[u.b * p.n_kv_heads + u.j], 1u,
-                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      prefetch_next();
-      if (tid == 0) sh.last = (done == u.n_chunks - 1) ? 1u : 0u;
+    if (pending) {  // workgroup-uniform
+      // the last workgroup of the previous partial's (row, kv head) merges
+      // the row's chunks in order
+      if (tid == 0) sh.last = (done_prev == pend_n - 1) ? 1u : 0u;
       __syncthreads();
       if (sh.last) {
-        merge_row<D, G>(p, u.b, u.j, u.n_chunks, tid, kThreads);
+        merge_row<D, G>(p, pend_b, pend_j, pend_n, tid, kThreads);
         if (tid == 0)  // ready for the next launch
-          __hip_atomic_store(&p.counters[u.b * p.n_kv_heads + u.j], 0u, __ATOMIC_RELAXED,
+          __hip_atomic_store(&p.counters[pend_b * p.n_kv_heads + pend_j], 0u, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
       }
-    } else {
-      prefetch_next();
     }
-#else
-    prefetch_next();
+    pending = split;
+    pend_b = u.b;
+    pend_j = u.j;
+    pend_n = u.n_chunks;
 #endif
     if (tid == 0)  // every wave read it before the merge barrier
       __hip_atomic_store(&mbox[par], kNoUnit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -760,6 +770,25 @@ __global__ void __launch_bounds__(kThreads)
     if (!has_next) break;
     u = plan_unit<D, G>(a, un, w);
   }
+#if SLOT_KV_FUSED_MERGE
+  if (pending) {  // the last unit's partial: publish it now
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t done = __hip_atomic_fetch_add(&p.counters[pend_b * p.n_kv_heads + pend_j], 1u,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sh.last = (done == pend_n - 1) ? 1u : 0u;
+    }
+    __syncthreads();
+    if (sh.last) {
+      merge_row<D, G>(p, pend_b, pend_j, pend_n, tid, kThreads);
+      if (tid == 0)
+        __hip_atomic_store(&p.counters[pend_b * p.n_kv_heads + pend_j], 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+#endif
 
   if (tid == 0) {
     // Every queue fetch of this workgroup has returned (its value ended the
