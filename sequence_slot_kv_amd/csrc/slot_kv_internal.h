@@ -11,7 +11,7 @@
 #define SLOT_KV_CHUNK 1024  // keys per split-K chunk (a multiple of 64)
 #endif
 #ifndef SLOT_KV_WG_WAVES
-#define SLOT_KV_WG_WAVES 4  // waves of one workgroup sharing a chunk
+#define SLOT_KV_WG_WAVES 0  // waves of one decode workgroup; 0: by head group size
 #endif
 
 namespace slotkv {

@@ -38,13 +38,10 @@ namespace {
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
-constexpr int NW = SLOT_KV_WG_WAVES;
-constexpr int kThreads = kWave * NW;
 constexpr float kLog2e = 1.4426950408889634f;
 #ifndef SLOT_KV_WAVES_PER_EU
 #define SLOT_KV_WAVES_PER_EU 2  // occupancy the register budget is fitted to
 #endif
-static_assert(SLOT_KV_CHUNK % NW == 0, "a chunk splits evenly over the waves");
 
 // Lanes per key row: enough that each lane holds about 32 floats of query
 // (G heads) and as many of accumulator, at most 16 (one DPP row).  The
@@ -143,8 +140,17 @@ __device__ __forceinline__ uint32_t mbox_wait(const uint32_t* slot) {
   return __builtin_amdgcn_readfirstlane(v);
 }
 
+// Waves per workgroup.  Eight waves share a unit's keys; G = 8 keeps four,
+// since its lanes hold twice the query and accumulator state and the larger
+// workgroups measured slower there.
+template <int G>
+constexpr int wg_waves() {
+  return SLOT_KV_WG_WAVES ? SLOT_KV_WG_WAVES : (G >= 8 ? 4 : 8);
+}
+
 template <int D, int G>
 struct alignas(16) Lds {
+  static constexpr int NW = wg_waves<G>();
   float acc[NW][G][D];
   float m[NW][G];
   float l[NW][G];
@@ -161,6 +167,7 @@ constexpr int waves_per_eu() {
 
 template <int D, int G>
 struct Shape {
+  static constexpr int NW = wg_waves<G>();                   // waves per workgroup
   static constexpr int LPK = pick_lpk(D, G);
   static constexpr int U = pick_unroll(D, G, LPK);
   static constexpr int NV4 = D / (4 * LPK);                  // float4 per lane per head vector
@@ -171,6 +178,7 @@ struct Shape {
   static constexpr int NST = (KPW + STEP - 1) / STEP;        // stages per pass, at most
   static constexpr int SCORES = NST * NG * G * U;            // score slots per wave
   static_assert(NV4 >= 1 && D % (4 * LPK) == 0, "whole float4 slices per lane");
+  static_assert(SLOT_KV_CHUNK % NW == 0, "a chunk splits evenly over the waves");
 };
 
 // One work unit as one wave sees it: chunk `chunk` of row b against kv head
@@ -197,6 +205,7 @@ __device__ __forceinline__ UnitId locate_unit(const AttnArgs& a, uint32_t unit) 
 template <int D, int G>
 __device__ __forceinline__ UnitPlan plan_unit(const AttnArgs& a, const UnitId& id, uint32_t w) {
   using S = Shape<D, G>;
+  constexpr int NW = S::NW;
   const AttnParams& p = a.p;
   UnitPlan u;
   u.b = id.b;
@@ -269,6 +278,7 @@ struct alignas(16) PrepLds {
 };
 template <int D, int G>
 struct PrepRaw {
+  static constexpr int NW = wg_waves<G>();
   static constexpr int EPL = D / kWave;
   static constexpr int SLOTS = (G + 1 + NW - 1) / NW;
   float x[SLOTS][EPL];
@@ -317,7 +327,7 @@ __device__ __forceinline__ void prep_issue(const AttnArgs& a, const UnitId& id, 
   const AttnParams& p = a.p;
 #pragma unroll
   for (int s = 0; s < R::SLOTS; ++s) {
-    const uint32_t v = w + s * NW;
+    const uint32_t v = w + s * R::NW;
     if (!prep_has<D, G>(a, id, v)) continue;  // wave-uniform
     const float* src = v < G ? p.q + (static_cast<size_t>(id.b) * p.n_heads + id.j * G + v) * D
                              : p.k_new + static_cast<size_t>(id.b) * p.kv_dim + id.j * D;
@@ -342,7 +352,7 @@ __device__ __forceinline__ void prep_finish(const AttnArgs& a, const UnitId& id,
   const float fpos = static_cast<float>(pos);
 #pragma unroll
   for (int s = 0; s < R::SLOTS; ++s) {
-    const uint32_t v = w + s * NW;
+    const uint32_t v = w + s * R::NW;
     if (!prep_has<D, G>(a, id, v)) continue;  // wave-uniform
     // norm with weights wts, then RoPE at pos (two inlined copies, so that
     // each reads its weights straight from registers)
@@ -425,9 +435,10 @@ __device__ __forceinline__ void merge_row(const AttnParams& p, uint32_t b, uint3
 // finished here; a longer row leaves one unnormalised partial per chunk,
 // merged by the row's last workgroup (or by merge_kernel).
 template <int D, int G>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kWave * wg_waves<G>())
     __attribute__((amdgpu_waves_per_eu(waves_per_eu<D, G>()))) decode_attn_kernel(const AttnArgs a) {
   using S = Shape<D, G>;
+  constexpr int NW = S::NW, kThreads = kWave * NW;
   constexpr int LPK = S::LPK, U = S::U, NV4 = S::NV4, NG = S::NG, SL = S::SL, STEP = S::STEP;
   __shared__ Lds<D, G> sh;
   __shared__ __attribute__((aligned(16))) float sc_lds[NW][S::SCORES];
@@ -853,7 +864,7 @@ __global__ void __launch_bounds__(256) merge_kernel(const AttnArgs a) {
 
 template <int D, int G>
 hipError_t launch_shape(const AttnArgs& a, uint32_t blocks, hipStream_t s, hipEvent_t mark) {
-  hipLaunchKernelGGL((decode_attn_kernel<D, G>), dim3(blocks), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((decode_attn_kernel<D, G>), dim3(blocks), dim3(kWave * wg_waves<G>()), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && mark) e = hipEventRecord(mark, s);
   if (e != hipSuccess || a.p.max_chunks <= 1 || SLOT_KV_FUSED_MERGE) return e;
@@ -869,7 +880,7 @@ uint32_t resident_shape() {
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_attn_kernel<D, G>,
-                                                     kThreads, 0) != hipSuccess)
+                                                     kWave * wg_waves<G>(), 0) != hipSuccess)
       return 0;
     cached = static_cast<uint32_t>(per_cu > 0 ? per_cu : 1) * static_cast<uint32_t>(cus);
   }
