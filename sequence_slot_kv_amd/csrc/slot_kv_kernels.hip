@@ -614,9 +614,7 @@ __global__ void __launch_bounds__(kWave * wg_waves<G>())
     // out once this unit's results are stored.
     const uint32_t n_st = u.n_st;
     if (n_st > 0) {  // wave-uniform
-      // pass 1; the next unit is taken between the first two stages (loads
-      // follow it on every path, so that its wait for the raw queries later
-      // leaves the stage in flight alone)
+      // pass 1
       load_stage<D, G>(p, u, gi, lo, B, 1);
       score(A, 0);
       load_stage<D, G>(p, u, gi, lo, A, 2);  // V stage 0 when n_st == 2
