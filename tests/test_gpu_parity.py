@@ -344,10 +344,12 @@ def test_decode_shapes_full_parity(D, G):
     Hkv = 2
     H = G * Hkv
     rng = np.random.default_rng(300 + 10 * G + D)
+    # Rows whose last chunk holds a few keys leave some of the waves that
+    # split a chunk with no keys, others with one partial stage.
     C = b.slot_kv_chunk_keys()
-    n_slots, slot_ctx = 8, 2 * C + 176
+    n_slots, slot_ctx = 12, 2 * C + 176
     L = wl.make_layer(rng, H, Hkv, D, 1e4, G % 2 == 0)
-    positions = np.array([0, 1, C - 1, C, 2 * C - 1, 2 * C + 175], np.uint32)
+    positions = np.array([0, 1, 53, C - 1, C, C + 1, C + 8, 2 * C - 1, 2 * C + 175], np.uint32)
     slots = rng.permutation(n_slots)[:positions.size].astype(np.uint32)
     B = positions.size
     q = rng.standard_normal((B, H * D), dtype=np.float32)
