@@ -13,8 +13,9 @@
 //     staged in LDS before the current unit ends; the unit that holds a
 //     row's last chunk also writes the row's KV entry -- rotated key and
 //     v_new at (slot*slot_ctx + pos)*kv_dim -- from that staging step;
-//   - the next unit's first K stage is in flight while the current unit
-//     waits for its split-row counter.
+//   - the next unit's first K stage is in flight while the current unit's
+//     epilogue (the wave merge, its partial's stores, the merge of a row
+//     whose counter the previous partial completed) runs.
 // Per unit and wave, two passes stream the history rows once each with
 // 128-bit non-temporal loads, double-buffered: pass 1 reads K, computes the
 // scores (LPK lanes per key row, DPP reductions) into LDS and the running
