@@ -648,6 +648,14 @@ int run_prefill(slot_kv* h, uint32_t layer, const float* q, const float* k_new,
                  (split ? slotkv::split_groups(keys, ck) : (keys + ck - 1) / ck) * L.n_kv_heads;
     }
     a.s.item_off[n] = items;
+    if (split) {  // each (sequence, kv head, tile) has one last group
+      uint32_t last = 0;
+      for (uint32_t i = 0; i < n; ++i) {
+        a.s.grp_off[i] = last;
+        last += (a.s.len[i] * G + 15) / 16 * L.n_kv_heads;
+      }
+      a.s.grp_off[n] = last;
+    }
     p.part = ck ? h->part + size_t(pl.rows) * qd : nullptr;
     p.n_items = items;
     p.split_keys = ck;

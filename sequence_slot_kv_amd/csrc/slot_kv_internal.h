@@ -141,7 +141,8 @@ struct PrefillSeqs {
   uint32_t len[kMaxSeqPerLaunch];
   uint32_t row_off[kMaxSeqPerLaunch + 1];  // first row of each sequence (and the total)
   uint32_t by_work[kMaxSeqPerLaunch];      // tiled: the sequences, most attention work first
-  uint32_t grp_off[kMaxSeqPerLaunch + 1];  // tiled: first workgroup of by_work[k] (per kv head)
+  uint32_t grp_off[kMaxSeqPerLaunch + 1];  // tiled: first workgroup of by_work[k] (per kv head);
+                                           // split-K: the last-group items of sequences before i
   uint32_t item_off[kMaxSeqPerLaunch + 1]; // key-chunked: first partial item of each sequence
 };
 
@@ -173,6 +174,32 @@ constexpr uint32_t kSplitChunksPerGroup = 4;
 SLOTKV_HD inline uint32_t split_groups(uint32_t keys, uint32_t split_keys) {
   const uint32_t chunks = (keys + split_keys - 1) / split_keys;
   return (chunks + kSplitChunksPerGroup - 1) / kSplitChunksPerGroup;
+}
+
+// Split-K launches: the partial item that workgroup `block` (< n_items)
+// computes.  Items stay sequence-major, (kv head, tile) then group, but the
+// workgroups take every group of whole chunk spans first and each tile's last
+// group after them; seqs.grp_off[i] counts the last groups of the sequences
+// before i.
+SLOTKV_HD inline uint32_t split_item_of_block(const PrefillSeqs& seqs, uint32_t n_seq,
+                                              uint32_t n_items, uint32_t split_keys,
+                                              uint32_t block) {
+  const uint32_t n_whole = n_items - seqs.grp_off[n_seq];
+  const bool whole = block < n_whole;
+  const uint32_t f = whole ? block : block - n_whole;
+  // the sequence: the last i whose first such item is <= f
+  uint32_t lo = 0, hi = n_seq;
+  while (hi - lo > 1) {
+    const uint32_t mid = (lo + hi) / 2;
+    const uint32_t first = whole ? seqs.item_off[mid] - seqs.grp_off[mid] : seqs.grp_off[mid];
+    if (first <= f) lo = mid; else hi = mid;
+  }
+  const uint32_t ng = split_groups(seqs.pos0[lo] + seqs.len[lo], split_keys);
+  if (whole) {
+    const uint32_t r = f - (seqs.item_off[lo] - seqs.grp_off[lo]);
+    return seqs.item_off[lo] + r / (ng - 1) * ng + r % (ng - 1);
+  }
+  return seqs.item_off[lo] + (f - seqs.grp_off[lo]) * ng + ng - 1;
 }
 constexpr uint32_t kSplitMinKeys = 256;       // smallest split-K chunk
 constexpr uint32_t kMaxSplitItems = 1u << 14; // per launch (bounds the partials)

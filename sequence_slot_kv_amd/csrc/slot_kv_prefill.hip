@@ -395,8 +395,10 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_eu<D>()))) split_attn_kernel(
   const uint32_t g = lane / 16, c = lane % 16;
   // workgroup -> (sequence, kv head j, tile, chunk group); wave w takes chunk
   // 4 * group + w.  All of it is uniform: scalar registers, uniform loops.
-  const uint32_t item = blockIdx.x;  // one partial per workgroup
-  if (item >= p.n_items) return;     // workgroup-uniform, before any barrier
+  // Workgroups run the groups of whole chunk spans first and every tile's
+  // last (shorter) group after them, so the end of the grid holds short work.
+  if (blockIdx.x >= p.n_items) return;  // workgroup-uniform, before any barrier
+  const uint32_t item = split_item_of_block(a.s, p.n_seq, p.n_items, p.split_keys, blockIdx.x);
   uint32_t lo = 0, hi = p.n_seq;  // the sequence: last i with item_off[i] <= item
   while (hi - lo > 1) {
     const uint32_t mid = (lo + hi) / 2;

@@ -8,6 +8,10 @@ twice.  This compiles the library's plain C++ planner (slot_kv_plan.cpp)
 with a small driver that walks the queue through the same lookup the kernel
 uses (locate_item) and checks coverage and the stated order: every full
 chunk, row by row, then each row's shorter last chunk, longest first.
+
+The split-K kernel of prefill / verify maps its workgroups to partial items
+the same way (split_item_of_block): the mapping must be a bijection onto the
+items, with every group of whole chunk spans before any tile's last group.
 """
 import os
 import subprocess
@@ -103,3 +107,69 @@ def test_plan_edges(planner):
     rng = np.random.default_rng(13)
     check_plan(rng.integers(0, 1 << 17, 256), 512, planner)
     check_plan(rng.integers(0, 64, 256), 64, planner)
+
+
+SPLIT_DRIVER = r"""
+#include <cstdio>
+#include "slot_kv_internal.h"
+using namespace slotkv;
+int main() {
+  unsigned n, G, hkv, sk;
+  if (std::scanf("%u %u %u %u", &n, &G, &hkv, &sk) != 4 || n > kMaxSeqPerLaunch) return 2;
+  static PrefillSeqs s;
+  uint32_t items = 0, last = 0;
+  for (unsigned i = 0; i < n; ++i) {
+    if (std::scanf("%u %u", &s.pos0[i], &s.len[i]) != 2) return 2;
+    const uint32_t tiles = (s.len[i] * G + 15) / 16;
+    s.item_off[i] = items;
+    s.grp_off[i] = last;
+    items += tiles * split_groups(s.pos0[i] + s.len[i], sk) * hkv;
+    last += tiles * hkv;
+  }
+  s.item_off[n] = items;
+  s.grp_off[n] = last;
+  std::printf("%u %u\n", items, last);
+  for (uint32_t b = 0; b < items; ++b) std::printf("%u\n", split_item_of_block(s, n, items, sk, b));
+  return 0;
+}
+"""
+
+
+@pytest.fixture(scope="module")
+def split_map(tmp_path_factory):
+    d = tmp_path_factory.mktemp("split")
+    src = d / "split.cpp"
+    src.write_text(SPLIT_DRIVER)
+    exe = d / "split"
+    subprocess.run(["g++", "-O1", "-std=c++17", "-I", INCLUDE, "-I", CSRC, str(src), "-o", str(exe)],
+                   check=True, capture_output=True)
+
+    def run(seqs, G, hkv, sk):
+        inp = f"{len(seqs)} {G} {hkv} {sk}\n" + " ".join(f"{p} {t}" for p, t in seqs) + "\n"
+        r = subprocess.run([str(exe)], input=inp, capture_output=True, text=True, check=True)
+        lines = r.stdout.split()
+        items, last = int(lines[0]), int(lines[1])
+        return items, last, [int(x) for x in lines[2:2 + items]]
+    return run
+
+
+def _groups(keys, sk):
+    return ((keys + sk - 1) // sk + 3) // 4  # four chunks of sk keys per group
+
+
+def test_split_item_mapping(split_map):
+    rng = np.random.default_rng(21)
+    for G, hkv, sk in ((4, 8, 256), (8, 4, 512), (1, 2, 256), (2, 8, 1024)):
+        seqs = [(int(rng.integers(0, 40000)), int(rng.integers(1, 64 // G + 1)))
+                for _ in range(int(rng.integers(1, 129)))]
+        items, last, order = split_map(seqs, G, hkv, sk)
+        assert sorted(order) == list(range(items)), "a bijection onto the items"
+        # which items are a tile's last group
+        is_last = []
+        for p0, t in seqs:
+            ng = _groups(p0 + t, sk)
+            for _ in range((t * G + 15) // 16 * hkv):
+                is_last += [g == ng - 1 for g in range(ng)]
+        assert len(is_last) == items and sum(is_last) == last
+        flags = [is_last[i] for i in order]
+        assert flags == sorted(flags), "whole-span groups first, last groups after"
