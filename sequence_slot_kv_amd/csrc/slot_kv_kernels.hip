@@ -176,7 +176,8 @@ struct Shape {
   static constexpr int SL = 4 * LPK;                         // floats per slice
   static constexpr int STEP = NG * U;                        // keys per wave per stage
   static constexpr int KPW = SLOT_KV_CHUNK / NW;             // history keys per wave, at most
-  static constexpr int NST = (KPW + STEP - 1) / STEP;        // stages per pass, at most
+  // stages per pass, at most: a wave's share of a chunk, padded to even
+  static constexpr int NST = ((KPW + STEP - 1) / STEP + 1) & ~1;
   static constexpr int SCORES = NST * NG * G * U;            // score slots per wave
   static_assert(NV4 >= 1 && D % (4 * LPK) == 0, "whole float4 slices per lane");
   static_assert(SLOT_KV_CHUNK % NW == 0, "a chunk splits evenly over the waves");
