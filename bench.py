@@ -2,24 +2,27 @@
 """Benchmark of the batched slot-KV decode-attention step on one MI355X.
 
 One "step" is one pass of the whole hot path over one batch: host validation
-and staging, the fused norm + RoPE + KV-write + split-K attention kernel, and
-the merge of split rows (``slot_decode_attn``), for every layer of the
-workload.  Default workload: 1 layer, 32 query / 8 kv heads of 128, 64 slots
-x 4096 positions, B = 64 rows at seeded positions U{1..4095}.
+and staging, the fused norm + RoPE + KV-write + split-K attention + merge
+kernel (``slot_decode_attn``), for every layer of the workload.  Default
+workload: 1 layer, 32 query / 8 kv heads of 128, 64 slots x 4096 positions,
+B = 64 rows at seeded positions U{1..4095}.
 
 Prints ONE JSON line on stdout:
   value        rows/s (B / step time), inputs resident in HBM
   kv_gbps      algorithmic KV bytes per step / step time, where the KV bytes
                are sum_b (pos_b + 1) * kv_dim * 4 for K and again for V
-  roofline     the fused kernel's achieved GB/s (KV bytes per launch / mean
-               launch time from HIP events on the launch stream, taken in a
-               second pass of the same K steps so that the timed region
-               carries no event records) vs 8 TB/s, with the HBM traffic
-               measured by rocprofv3 counters when the committed counter
-               record matches the current kernel source; a third pass writes
-               1 GiB before every step (outside the events) and reports the
-               launch time with L2 and the Infinity Cache emptied
-  cpu_baseline the CPU oracle on the host cores over the same rows
+  roofline     the fused kernel's achieved GB/s vs 8 TB/s: KV bytes per
+               launch / mean launch time, the time from HIP events recorded
+               on the launch stream around the timed region (K steps back to
+               back, so it also holds the short gaps between launches);
+               beside it the mean of per-launch event pairs (which also span
+               the dispatch in front of each launch), the launch time with
+               L2 and the Infinity Cache emptied before every step, the
+               rocprofv3 kernel average and the HBM traffic from rocprofv3
+               counters, the last two only when the committed records were
+               taken from the current kernel sources
+  cpu_baseline the CPU oracle on the host over rows of the same step: one
+               thread, and as many threads as the job's CPU share
 
     python bench.py [--steps K] [--warmup W] [--workload mid]
 
@@ -72,6 +75,7 @@ STATE_SRC = os.path.join(CSRC, "slot_kv_state.hip")
 # every kernel is built with
 INTERNAL_H = os.path.join(CSRC, "slot_kv_internal.h")
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_counters.json")
+TRACE_RECORD = os.path.join(ROOT, "profiles", "kernel_trace.json")
 
 
 def log(*a):
@@ -80,7 +84,7 @@ def log(*a):
 
 def kernel_hash(src: str = KERNEL_SRC) -> str:
     """Hash of a kernel's source file and of the internal header it is built
-    with: a counter record stays valid only while both are unchanged."""
+    with: a profiler record stays valid only while both are unchanged."""
     h = hashlib.sha256()
     for path in (src, INTERNAL_H):
         with open(path, "rb") as f:
@@ -88,43 +92,99 @@ def kernel_hash(src: str = KERNEL_SRC) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, src: str = KERNEL_SRC):
-    """HBM bytes per launch of the workload's dominant kernel from the
-    committed rocprofv3 counter record, or None when there is none for this
-    workload or the kernel source `src` changed since it was taken."""
+def _record(path: str, workload: str, src: str):
     try:
-        rec = json.load(open(TRAFFIC_RECORD))
+        rec = json.load(open(path))
     except (OSError, ValueError):
         return None
     entry = rec.get(workload)
     if not entry or entry.get("kernel_sha256_16") != kernel_hash(src):
         return None
-    return entry.get("hbm_bytes_per_launch")
+    return entry
 
 
-def cpu_baseline(w, hist, target_cpu_s: float = 12.0):
+def measured_traffic(workload: str, src: str = KERNEL_SRC):
+    """HBM bytes per launch of the workload's dominant kernel from the
+    committed rocprofv3 counter record, or None when there is none for this
+    workload or the kernel source `src` changed since it was taken."""
+    entry = _record(TRAFFIC_RECORD, workload, src)
+    return None if entry is None else entry.get("hbm_bytes_per_launch")
+
+
+def rocprof_kernel_us(workload: str, src: str = KERNEL_SRC):
+    """Mean duration (us) of the workload's dominant kernel in the committed
+    rocprofv3 kernel trace, or None when the kernel source changed since."""
+    entry = _record(TRACE_RECORD, workload, src)
+    return None if entry is None else entry.get("avg_us")
+
+
+def cpu_share() -> tuple:
+    """(threads for the multi-threaded oracle leg, CPUs visible, where the
+    count comes from): the CPUs this process may run on, cut to the job's CPU
+    share when the environment states one in OMP_NUM_THREADS."""
+    visible = len(os.sched_getaffinity(0))
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    if share.isdigit() and 0 < int(share) < visible:
+        return int(share), visible, "the job's CPU share, from OMP_NUM_THREADS"
+    return visible, visible, "every CPU visible"
+
+
+def cpu_rows(w, sample_max: int = 8, seed: int = 5):
+    """Rows the oracle is timed on: every row of the 64-row workload, else a
+    seeded sample that holds the longest and the shortest row."""
+    import numpy as np
+    if w.B <= 64 and len(w.layers) == 1:
+        return list(range(w.B)), False
+    rng = np.random.default_rng(seed)
+    pick = {int(np.argmax(w.positions)), int(np.argmin(w.positions))}
+    rest = [i for i in range(w.B) if i not in pick]
+    pick.update(int(i) for i in rng.choice(rest, size=min(sample_max - 2, len(rest)),
+                                           replace=False))
+    return sorted(pick), True
+
+
+def cpu_baseline(w, rows, sampled, hist, target_s: float = 6.0):
+    """The oracle on (row, layer) tasks of one step, rows given, timed twice:
+    on one thread, then on the job's CPU share of threads (ctypes releases the
+    GIL, so the threads run in parallel); each leg repeats the tasks until
+    about target_s seconds of wall time have passed."""
     import oracle
-    threads = max(1, min(len(os.sched_getaffinity(0)), 16))
-    rows = list(range(w.B))
+    tasks = [(bi, l) for bi in rows for l in range(len(w.layers))]
 
-    def one(bi):
-        L, li = w.layers[0], w.inputs[0]
-        hk, hv = hist[bi]
+    def one(t):
+        bi, l = t
+        L, li = w.layers[l], w.inputs[l]
+        hk, hv = hist[(bi, l)]
         oracle.decode_row(L, int(w.positions[bi]), li.q[bi], li.k_new[bi], li.v_new[bi], hk, hv)
 
-    done, t0 = 0, time.perf_counter()
-    with cf.ThreadPoolExecutor(threads) as ex:
-        while True:
-            list(ex.map(one, rows))
-            done += len(rows)
-            wall = time.perf_counter() - t0
-            if wall * threads >= target_cpu_s or done >= 40 * len(rows):
-                break
-    rows_per_s = done / wall
-    return {"value": rows_per_s, "unit": "rows/s", "cores": threads, "kind": "oracle",
-            "sample": f"all {w.B} rows of the step (layer 0), {done // w.B} passes, "
-                      f"{wall:.1f} s wall on {threads} threads",
-            "kv_gbps": rows_per_s / w.B * w.kv_bytes(0) / 1e9}
+    def leg(threads, batch):
+        passes, t0 = 0, time.perf_counter()
+        with cf.ThreadPoolExecutor(threads) as ex:
+            while True:
+                list(ex.map(one, tasks * batch))
+                passes += batch
+                wall = time.perf_counter() - t0
+                if wall >= target_s:
+                    return passes, wall
+
+    n_threads, visible, why = cpu_share()
+    keys = sum(int(w.positions[bi]) + 1 for bi in rows)
+    kv_bytes = sum(keys * L.kv_dim * 8 for L in w.layers)  # per pass of every row and layer
+    p1, t1 = leg(1, 1)
+    # several passes per submission, about a quarter of the leg each, so that
+    # the threads rarely wait on the longest row at the end of a pass
+    batch = max(1, round(target_s / 4 * n_threads / (t1 / p1)))
+    pn, tn = leg(n_threads, batch)
+    what = (f"a seeded sample of {len(rows)} of the step's {w.B} rows (the longest and shortest "
+            f"among them)" if sampled else f"all {w.B} rows of the step")
+    if len(w.layers) > 1:
+        what += f", each through all {len(w.layers)} layers"
+    return {"value": len(rows) * pn / tn, "unit": "rows/s", "cores": n_threads, "kind": "oracle",
+            "sample": f"{what}; {n_threads} threads ({why}; {visible} CPUs visible): "
+                      f"{pn} passes in {tn:.1f} s; 1 thread: {p1} passes in {t1:.1f} s",
+            "value_1_thread": len(rows) * p1 / t1, "cores_visible": visible,
+            "kv_gbps": kv_bytes * pn / tn / 1e9, "kv_gbps_1_thread": kv_bytes * p1 / t1 / 1e9,
+            "sampled": sampled}
 
 
 def main():
@@ -145,7 +205,6 @@ def main():
               "slot with no exchange, so more GPUs are not exercised here", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
     from sequence_slot_kv_amd import binding as b
     from sequence_slot_kv_amd import workloads as wl
@@ -167,7 +226,13 @@ def main():
         return verify_bench(args, wl.VERIFY_WORKLOADS[args.workload](), b)
     if args.workload.startswith("state"):
         return state_bench(args, wl.STATE_WORKLOADS[args.workload](), b)
-    w = wl.WORKLOADS[args.workload]()
+    return decode_bench(args, wl.WORKLOADS[args.workload](), b)
+
+
+def decode_bench(args, w, b):
+    import numpy as np
+    import torch
+    from sequence_slot_kv_amd import workloads as wl
     n_layers = len(w.layers)
     log(f"[bench] workload {w.name}: B={w.B} n_slots={w.n_slots} slot_ctx={w.slot_ctx} "
         f"layers={n_layers} kv_bytes/step={w.kv_bytes()}")
@@ -189,45 +254,55 @@ def main():
     torch.cuda.synchronize()
     log("[bench] history filled")
 
-    hist = None
-    if not args.no_cpu_baseline:  # snapshot layer-0 history before any step runs
+    hist, cpu_rows_, sampled = None, None, False
+    if not args.no_cpu_baseline:  # snapshot the timed rows' history before any step runs
+        cpu_rows_, sampled = cpu_rows(w)
         hist = {}
-        for bi in range(w.B):
+        for bi in cpu_rows_:
             p = int(w.positions[bi])
-            if p == 0:
-                z = np.zeros((0, w.layers[0].kv_dim), np.float32)
-                hist[bi] = (z, z)
-            else:
-                k, v = kv.read_rows(0, int(w.slots[bi]), 0, p)
-                hist[bi] = (k.cpu().numpy(), v.cpu().numpy())
+            for l, P in enumerate(w.layers):
+                if p == 0:
+                    z = np.zeros((0, P.kv_dim), np.float32)
+                    hist[(bi, l)] = (z, z)
+                else:
+                    k, v = kv.read_rows(l, int(w.slots[bi]), 0, p)
+                    hist[(bi, l)] = (k.cpu().numpy(), v.cpu().numpy())
 
     ins = [tuple(torch.from_numpy(a).cuda() for a in (li.q, li.k_new, li.v_new)) for li in w.inputs]
     outs = [torch.empty_like(x[0]) for x in ins]
     positions, slots = w.positions, w.slots
+    stream = torch.cuda.current_stream()  # the library launches on this stream
 
     def step():
         for l in range(n_layers):
             q, kn, vn = ins[l]
-            kv.decode_attn(l, q, kn, vn, positions, slots, out=outs[l])
+            kv.decode_attn(l, q, kn, vn, positions, slots, out=outs[l], stream=stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps, nothing else enqueued
+    # timed region: K steps, nothing else enqueued; HIP events on the launch
+    # stream bracket it
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for _ in range(args.steps):
         step()
+    ev1.record(stream)
+    t_enq = time.perf_counter()  # the host's share: validation, staging, launch calls
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    # the fused kernel's own duration: the same K steps again, with the
-    # library recording a HIP event pair around every launch on its stream
+    region_ms = ev0.elapsed_time(ev1)
+    # per-launch event pairs (the library records one around every launch on
+    # its stream; the start event sits before the launch, so a pair also
+    # spans the dispatch), in a second pass of the same K steps
     rc = b.slot_kv_profile_begin(kv.h)
     assert rc == 0
     for _ in range(args.steps):
         step()
-    rc, kernel_ms, launches = b.slot_kv_profile_end(kv.h)
+    rc, pair_ms, launches = b.slot_kv_profile_end(kv.h)
     torch.cuda.synchronize()
     assert rc == 0 and launches == args.steps * n_layers
     # and once more with the caches emptied before every step: a 1 GiB
@@ -250,18 +325,24 @@ def main():
     kv_bytes = w.kv_bytes()
     rows_per_s = w.B / (ms_per_step / 1e3)
     kv_gbps = kv_bytes / (ms_per_step / 1e3) / 1e9
-    mean_launch_ms = kernel_ms / launches
+    n_launch = args.steps * n_layers
+    launch_ms = region_ms / n_launch
     bytes_per_launch = kv_bytes / n_layers
-    achieved = bytes_per_launch / (mean_launch_ms / 1e3) / 1e9
-    cold_launch_ms = cold_ms / (args.steps * n_layers)
+    achieved = bytes_per_launch / (launch_ms / 1e3) / 1e9
+    cold_launch_ms = cold_ms / n_launch
     traffic = measured_traffic(w.name)
-    log(f"[bench] {ms_per_step * 1e3:.1f} us/step, fused kernel {mean_launch_ms * 1e3:.1f} us/launch, "
-        f"{achieved:.0f} GB/s in-kernel; {cold_launch_ms * 1e3:.1f} us/launch with caches flushed")
+    prof_us = rocprof_kernel_us(w.name)
+    host_us = (t_enq - t0) * 1e6 / args.steps
+    log(f"[bench] host enqueue {host_us:.1f} us/step")
+    log(f"[bench] {ms_per_step * 1e3:.1f} us/step; fused kernel {launch_ms * 1e3:.1f} us/launch "
+        f"(events over the timed region), {achieved:.0f} GB/s; event pairs "
+        f"{pair_ms / n_launch * 1e3:.1f} us; {cold_launch_ms * 1e3:.1f} us/launch with caches "
+        f"flushed; rocprofv3 record {prof_us}")
 
     cpu = None
     if hist is not None:
         log("[bench] timing the CPU oracle")
-        cpu = cpu_baseline(w, hist)
+        cpu = cpu_baseline(w, cpu_rows_, sampled, hist)
 
     res = {
         "metric": METRIC, "value": rows_per_s, "unit": "rows/s", "n_gpus": 1,
@@ -275,10 +356,15 @@ def main():
                    "chunk_keys": b.slot_kv_chunk_keys()},
         "kv_bytes_per_step": kv_bytes, "kv_gbps": kv_gbps,
         "kv_pct_of_hbm_peak": 100.0 * kv_gbps / HBM_PEAK_GBPS,
+        "host_enqueue_us_per_step": host_us,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": "decode_attn_kernel", "kernel_us": mean_launch_ms * 1e3,
+                     "kernel": "decode_attn_kernel", "kernel_us": launch_ms * 1e3,
+                     "kernel_us_from": "HIP events on the launch stream around the timed "
+                                       "region, per launch",
                      "algorithmic_bytes_per_launch": bytes_per_launch,
+                     "kernel_us_event_pairs": pair_ms / n_launch * 1e3,
+                     "kernel_us_rocprof": prof_us,
                      "kernel_us_caches_flushed": cold_launch_ms * 1e3,
                      "achieved_caches_flushed": bytes_per_launch / (cold_launch_ms / 1e3) / 1e9},
         "cpu_baseline": cpu,

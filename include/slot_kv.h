@@ -60,7 +60,8 @@ void slot_kv_destroy(slot_kv *h);
  * and fills them with zeros.  kv_dims is a host array of n_layers counts of
  * floats per KV row.  Idempotent: any previous allocation of this handle is
  * freed first (layer configurations are dropped with it).
- * Errors: EINVAL (zero sizes, NULL kv_dims, size overflow), ENOMEM, EDEVICE.
+ * Errors: EINVAL (zero sizes, NULL kv_dims, a buffer of more than 2^64 - 1
+ * bytes; checked before any HIP call), ENOMEM, EDEVICE.
  * The same as slot_state_alloc with no ssm layers. */
 int slot_kv_alloc(slot_kv *h, uint32_t n_slots, uint32_t slot_ctx,
                   const uint32_t *kv_dims, uint32_t n_layers);
@@ -78,8 +79,9 @@ int slot_kv_alloc(slot_kv *h, uint32_t n_slots, uint32_t slot_ctx,
  * What the SSM kernels keep in the buffers is theirs to define; this library
  * lays them out, addresses them and zeroes them.  Idempotent: any previous
  * allocation of the handle (KV and state, and the layer configurations) is
- * freed first.  Errors: EINVAL (zero sizes, NULL arrays, one slot's state
- * above 2^31 tiles of 8 KiB), ENOMEM, EDEVICE. */
+ * freed first.  Errors: EINVAL (zero sizes, NULL arrays, a buffer of more
+ * than 2^64 - 1 bytes, one slot's state above 2^31 tiles of 8 KiB; all
+ * checked before any HIP call), ENOMEM, EDEVICE. */
 int slot_state_alloc(slot_kv *h, uint32_t n_slots, uint32_t slot_ctx,
                      const uint32_t *kv_dims, uint32_t n_attn_layers,
                      const uint32_t *conv_state_len, const uint32_t *ssm_state_len,

@@ -56,8 +56,8 @@ struct slot_kv {
   uint32_t state_tiles_per_slot = 0;
   float* part = nullptr;         // partial results of split rows (acc, then max/sum)
   size_t part_cap = 0;           // floats
-  uint32_t* counters = nullptr;  // work queue [2], then per (row, kv head) chunk counters;
-                                 // all zero between launches
+  uint64_t* counters = nullptr;  // work queue [1], then per (row, kv head) chunk counters;
+                                 // epoch-tagged words, zeroed when allocated
   size_t counters_cap = 0;       // entries
   AttnArgs args;                 // kernel arguments of the decode launch being built
   slotkv::PrefillArgs pargs;     // kernel arguments of the prefill launch being built
@@ -98,6 +98,17 @@ void free_scratch(slot_kv* h) {
   h->prof_events.clear();
   h->prof_used = 0;
   h->profiling = false;
+}
+
+// Bytes of an f32 buffer of a * b * c floats; false when the product passes
+// 2^64 - 1 (nothing is written to *bytes then).
+bool buffer_bytes(uint64_t a, uint64_t b, uint64_t c, uint64_t* bytes) {
+  uint64_t n = 0;
+  if (__builtin_mul_overflow(a, b, &n) || __builtin_mul_overflow(n, c, &n) ||
+      __builtin_mul_overflow(n, uint64_t(sizeof(float)), &n))
+    return false;
+  if (bytes) *bytes = n;
+  return true;
 }
 
 int check_layer(const slot_kv* h, uint32_t layer) {
@@ -145,8 +156,9 @@ int prof_pair(slot_kv* h, hipEvent_t* e0, hipEvent_t* e1) {
   return SLOT_KV_OK;
 }
 
-// The work-queue counters start at zero; the kernel returns them to zero, so
-// they are cleared only when (re)allocated.
+// The work-queue and split-row counter words carry a launch epoch (see
+// kEpochShift), so they are cleared only when (re)allocated: zero is epoch 0,
+// older than every launch's.
 int ensure_counters(slot_kv* h, size_t entries) {
   if (h->counters_cap >= entries) return SLOT_KV_OK;
   if (hipDeviceSynchronize() != hipSuccess) return SLOT_KV_EDEVICE;
@@ -154,13 +166,13 @@ int ensure_counters(slot_kv* h, size_t entries) {
   h->counters = nullptr;
   h->counters_cap = 0;
   void* c = nullptr;
-  if (hipMalloc(&c, entries * sizeof(uint32_t)) != hipSuccess) return SLOT_KV_ENOMEM;
-  if (hipMemset(c, 0, entries * sizeof(uint32_t)) != hipSuccess ||
+  if (hipMalloc(&c, entries * sizeof(uint64_t)) != hipSuccess) return SLOT_KV_ENOMEM;
+  if (hipMemset(c, 0, entries * sizeof(uint64_t)) != hipSuccess ||
       hipDeviceSynchronize() != hipSuccess) {
     (void)hipFree(c);
     return SLOT_KV_EDEVICE;
   }
-  h->counters = static_cast<uint32_t*>(c);
+  h->counters = static_cast<uint64_t*>(c);
   h->counters_cap = entries;
   return SLOT_KV_OK;
 }
@@ -190,12 +202,19 @@ int slot_state_alloc(slot_kv* h, uint32_t n_slots, uint32_t slot_ctx, const uint
     return SLOT_KV_EINVAL;
   if (n_attn_layers && !kv_dims) return SLOT_KV_EINVAL;
   if (n_ssm_layers && (!conv_state_len || !ssm_state_len)) return SLOT_KV_EINVAL;
-  // Byte sizes are products of 32-bit factors (times 4), so they fit 64 bits.
+  // Every buffer's byte size is checked here, before any HIP call: a K/V
+  // buffer is n_slots * slot_ctx * kv_dim * 4 bytes, three 32-bit factors
+  // whose product can pass 2^64 (and would wrap to a small allocation that
+  // the offsets then overrun); a state buffer is n_slots * len * 4.
   for (uint32_t L = 0; L < n_attn_layers; ++L)
-    if (kv_dims[L] == 0) return SLOT_KV_EINVAL;
+    if (kv_dims[L] == 0 || !buffer_bytes(n_slots, slot_ctx, kv_dims[L], nullptr))
+      return SLOT_KV_EINVAL;
   uint64_t tiles = 0;
   for (uint32_t L = 0; L < n_ssm_layers; ++L) {
     if (conv_state_len[L] == 0 || ssm_state_len[L] == 0) return SLOT_KV_EINVAL;
+    if (!buffer_bytes(n_slots, 1, conv_state_len[L], nullptr) ||
+        !buffer_bytes(n_slots, 1, ssm_state_len[L], nullptr))
+      return SLOT_KV_EINVAL;
     tiles += slotkv::reset_tiles(conv_state_len[L]) + slotkv::reset_tiles(ssm_state_len[L]);
   }
   // one slot's reset must fit one grid (and tile0 must fit 32 bits)
@@ -223,9 +242,9 @@ int slot_state_alloc(slot_kv* h, uint32_t n_slots, uint32_t slot_ctx, const uint
     return hipMemset(p, 0, bytes) == hipSuccess ? SLOT_KV_OK : SLOT_KV_EDEVICE;
   };
   h->layers.resize(n_attn_layers);
-  const uint64_t rows = static_cast<uint64_t>(n_slots) * slot_ctx;
   for (uint32_t L = 0; L < n_attn_layers; ++L) {
-    const uint64_t bytes = rows * kv_dims[L] * sizeof(float);
+    uint64_t bytes = 0;
+    (void)buffer_bytes(n_slots, slot_ctx, kv_dims[L], &bytes);  // checked above
     h->layers[L].kv_dim = kv_dims[L];
     int rc = zeroed(bytes, &h->layers[L].k);
     if (!rc) rc = zeroed(bytes, &h->layers[L].v);
@@ -238,8 +257,11 @@ int slot_state_alloc(slot_kv* h, uint32_t n_slots, uint32_t slot_ctx, const uint
     SsmLayer& S = h->ssm[L];
     S.conv_len = conv_state_len[L];
     S.ssm_len = ssm_state_len[L];
-    int rc = zeroed(uint64_t(n_slots) * S.conv_len * sizeof(float), &S.conv);
-    if (!rc) rc = zeroed(uint64_t(n_slots) * S.ssm_len * sizeof(float), &S.ssm);
+    uint64_t conv_bytes = 0, ssm_bytes = 0;  // checked above
+    (void)buffer_bytes(n_slots, 1, S.conv_len, &conv_bytes);
+    (void)buffer_bytes(n_slots, 1, S.ssm_len, &ssm_bytes);
+    int rc = zeroed(conv_bytes, &S.conv);
+    if (!rc) rc = zeroed(ssm_bytes, &S.ssm);
     if (rc) return fail(rc);
     segs.push_back({S.conv, S.conv_len, tile0, 0});
     tile0 += static_cast<uint32_t>(slotkv::reset_tiles(S.conv_len));
@@ -439,12 +461,14 @@ int slot_decode_attn(slot_kv* h, uint32_t layer, const float* q, const float* k_
       items += nc;
       max_chunks = std::max(max_chunks, nc);
     }
-    if (items * L.n_kv_heads >= (uint64_t(1) << 31)) return SLOT_KV_EINVAL;
+    // a launch's units are counted below the epoch bits of the queue word
+    // (no cache that fits a GPU's memory comes near this)
+    if (items * L.n_kv_heads > slotkv::kCountMask) return SLOT_KV_EINVAL;
     part_floats = std::max(part_floats, static_cast<size_t>(n * max_chunks) * L.n_heads * (D + 2));
   }
   rc = ensure_partials(h, part_floats);
   if (rc) return rc;
-  rc = ensure_counters(h, 2 + static_cast<size_t>(R) * L.n_kv_heads);
+  rc = ensure_counters(h, 1 + static_cast<size_t>(R) * L.n_kv_heads);
   if (rc) return rc;
   const uint32_t resident = slotkv::resident_blocks(L.head_dim, G);
   if (resident == 0) return SLOT_KV_EDEVICE;
@@ -456,7 +480,7 @@ int slot_decode_attn(slot_kv* h, uint32_t layer, const float* q, const float* k_
   p.k_cache = L.k;
   p.v_cache = L.v;
   p.sched = h->counters;
-  p.counters = h->counters + 2;
+  p.counters = h->counters + 1;
   p.q_norm_w = L.params;
   p.k_norm_w = L.params + D;
   p.inv_freq = L.params + 2 * D;
@@ -483,6 +507,9 @@ int slot_decode_attn(slot_kv* h, uint32_t layer, const float* q, const float* k_
     p.out = out + r0 * qd;
     p.part_acc = h->part;
     p.part_ml = h->part + static_cast<size_t>(n) * work.max_chunks * L.n_heads * D;
+    const uint64_t epoch = slotkv::next_epoch();
+    if (epoch == 0) return SLOT_KV_EDEVICE;  // 2^40 launches in one process
+    p.epoch_tag = epoch << slotkv::kEpochShift;
 
     hipEvent_t ev_start = nullptr, ev_end = nullptr;
     rc = prof_pair(h, &ev_start, &ev_end);

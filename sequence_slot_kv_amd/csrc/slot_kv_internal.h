@@ -61,6 +61,88 @@ SLOTKV_HD inline void locate_item(const LaunchRows& rows, uint32_t n_rows, uint3
   }
 }
 
+// ---------------------------------------------------------------- decode kernel shape
+// The decode kernel's per-shape constants, visible to host code so that the
+// bound of its LDS score buffer can be checked for every shape and chunk
+// size on the CPU.
+#ifndef SLOT_KV_LPK
+#define SLOT_KV_LPK 0  // lanes per key row; 0: derive from the shape
+#endif
+#ifndef SLOT_KV_UNROLL
+#define SLOT_KV_UNROLL 0  // keys per key group per stage; 0: derive from the shape
+#endif
+constexpr int kWaveLanes = 64;
+
+// Waves per workgroup.  Eight waves share a unit's keys; G = 8 keeps four,
+// since its lanes hold twice the query and accumulator state and the larger
+// workgroups measured slower there.
+constexpr int decode_waves(int G) {
+  return SLOT_KV_WG_WAVES ? SLOT_KV_WG_WAVES : (G >= 8 ? 4 : 8);
+}
+// Lanes per key row: enough that each lane holds about 32 floats of query
+// (G heads) and as many of accumulator, at most 16 (one DPP row).
+constexpr int decode_lpk(int D, int G) {
+  const int want = SLOT_KV_LPK ? SLOT_KV_LPK : G * D / 32;
+  int lpk = want < 4 ? 4 : (want > 16 ? 16 : want);
+  while (D / (4 * lpk) < 1) lpk /= 2;
+  return lpk;
+}
+// Keys per key group per pipeline stage: about 8 float4 loads per lane, and
+// at most 16 scores (G per key) per lane, which leaves G = 8 with 64 floats
+// each of query and accumulator room for two waves per SIMD.
+constexpr int decode_unroll(int D, int G) {
+  const int nv4 = D / (4 * decode_lpk(D, G));
+  int u = nv4 >= 8 ? 1 : 8 / nv4;
+  while (u > 1 && G * u > 16) u /= 2;
+  return SLOT_KV_UNROLL ? SLOT_KV_UNROLL : u;
+}
+// Keys one wave streams per pipeline stage.
+constexpr int decode_step(int D, int G) {
+  return kWaveLanes / decode_lpk(D, G) * decode_unroll(D, G);
+}
+// Stages per pass that the LDS score buffer of one wave holds: a wave's
+// share of a full chunk of `chunk` keys, padded to even as the stage count
+// of every pass is.
+constexpr int decode_stage_bound(int D, int G, int chunk) {
+  const int kpw = chunk / decode_waves(G);
+  const int step = decode_step(D, G);
+  return ((kpw + step - 1) / step + 1) & ~1;
+}
+
+// The history keys [begin, begin + len) of a chunk that wave w of nw streams
+// when the chunk holds n_keys (<= chunk) history keys: the chunk's stages of
+// `step` keys split as evenly as whole stages allow, so a short last chunk
+// keeps every wave busy (a full chunk gives each wave chunk / nw keys).
+// n_st counts the wave's stages per pass, rounded up to even (the stages past
+// n_full whole ones are masked) so that each pass ends in the same buffer.
+struct WaveKeys {
+  uint32_t begin, len, n_full, n_st;
+};
+SLOTKV_HD constexpr inline WaveKeys wave_keys(uint32_t n_keys, uint32_t step, uint32_t nw,
+                                              uint32_t w) {
+  const uint32_t steps = (n_keys + step - 1) / step;
+  const uint32_t k0 = steps * w / nw * step;
+  const uint32_t k1 = steps * (w + 1) / nw * step;
+  WaveKeys r{};
+  r.begin = k0 < n_keys ? k0 : n_keys;
+  r.len = (k1 < n_keys ? k1 : n_keys) - r.begin;
+  r.n_full = r.len / step;
+  const uint32_t n_st = r.n_full + (r.len % step != 0 ? 1u : 0u);
+  r.n_st = (n_st + 1) & ~1u;
+  return r;
+}
+
+// Work-queue and split-row counter words are 64-bit: the launch's epoch in
+// the bits from kEpochShift up, a count below.  Every launch takes a new
+// epoch, larger than any earlier one in the process, and raises a word to
+// its own epoch (an atomic max of epoch << kEpochShift, which sets the count
+// to zero when the word still holds an older epoch) before the first
+// increment it makes; so no launch needs the words cleared, and a word left
+// behind by any earlier launch, finished or not, is never counted on.
+constexpr uint32_t kEpochShift = 24;
+constexpr uint64_t kCountMask = (uint64_t(1) << kEpochShift) - 1;
+constexpr uint64_t kMaxEpoch = (uint64_t(1) << (64 - kEpochShift)) - 1;
+
 // Kernel-side parameters of one decode launch (rows 0..n_rows-1 of it).
 struct AttnParams {
   float* k_cache;          // layer K buffer [n_slots][slot_ctx][kv_dim]
@@ -71,8 +153,9 @@ struct AttnParams {
   float* out;              // [n_rows][n_heads*D]
   float* part_acc;         // [n_rows][max_chunks][n_heads][D]  unnormalised partial outputs
   float* part_ml;          // [n_rows][max_chunks][n_heads][2]  max (log2 units), sum
-  uint32_t* sched;         // [2]: next dynamic work unit, exited workgroups; zero between launches
-  uint32_t* counters;      // [n_rows][n_kv_heads] chunks finished; zero between launches
+  uint64_t* sched;         // [1]: the work queue (epoch | dynamic units handed out)
+  uint64_t* counters;      // [n_rows][n_kv_heads]: (epoch | chunks finished) of split rows
+  uint64_t epoch_tag;      // this launch's epoch << kEpochShift
   const float* q_norm_w;   // [D]
   const float* k_norm_w;   // [D]
   const float* inv_freq;   // [D/2]
@@ -83,7 +166,7 @@ struct AttnParams {
   uint32_t n_heads;
   uint32_t n_rows;
   uint32_t n_full;         // full-chunk items
-  uint32_t n_units;        // (full + partial items) * n_kv_heads
+  uint32_t n_units;        // (full + partial items) * n_kv_heads, below 2^kEpochShift
   uint32_t max_chunks;     // largest chunk count of a row (partial-result stride)
   uint32_t chunk;
   float eps;
@@ -227,11 +310,15 @@ struct LaunchWork {
 LaunchWork fill_rows(LaunchRows& rows, const uint32_t* positions, const uint32_t* slots,
                      uint32_t n, uint32_t chunk);
 
-// Launch of the fused decode kernel with `blocks` persistent workgroups, then
-// (when a row spans several chunks) of the partial merge.  `after_decode` (a
-// hipEvent_t or null) is recorded between the two.  Returns a hipError_t value.
+// Launch of the fused decode kernel with `blocks` persistent workgroups;
+// `after_decode` (a hipEvent_t or null) is recorded after it.  Returns a
+// hipError_t value.
 int launch_decode(const AttnArgs& a, uint32_t head_dim, uint32_t group, uint32_t blocks,
                   void* stream, void* after_decode);
+// The next launch epoch (1, 2, ...; shared by every handle and device of
+// the process, so that it grows on every word it is used with), or 0 once
+// kMaxEpoch has been handed out.
+uint64_t next_epoch();
 // Workgroups of the decode kernel for this shape that are resident at once
 // on the current device (0 on error).
 uint32_t resident_blocks(uint32_t head_dim, uint32_t group);

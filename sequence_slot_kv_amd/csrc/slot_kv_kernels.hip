@@ -38,38 +38,16 @@ namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWave = 64;
+constexpr int kWave = kWaveLanes;
 constexpr float kLog2e = 1.4426950408889634f;
 #ifndef SLOT_KV_WAVES_PER_EU
 #define SLOT_KV_WAVES_PER_EU 2  // occupancy the register budget is fitted to
 #endif
 
-// Lanes per key row: enough that each lane holds about 32 floats of query
-// (G heads) and as many of accumulator, at most 16 (one DPP row).  The
-// lane's elements of a head vector are d = i*4*LPK + 4*r + c (slice i, lane
-// r of the key group, component c); queries reach that layout from their
-// LDS staging, where they were rotated.
-#ifndef SLOT_KV_LPK
-#define SLOT_KV_LPK 0  // 0: derive from the shape
-#endif
-#ifndef SLOT_KV_UNROLL
-#define SLOT_KV_UNROLL 0  // 0: derive from the shape
-#endif
-constexpr int pick_lpk(int D, int G) {
-  int want = SLOT_KV_LPK ? SLOT_KV_LPK : G * D / 32;
-  int lpk = want < 4 ? 4 : (want > 16 ? 16 : want);
-  while (D / (4 * lpk) < 1) lpk /= 2;
-  return lpk;
-}
-// Keys per key group per pipeline stage: about 8 float4 loads per lane, and
-// at most 16 scores (G per key) per lane, which leaves G = 8 with 64 floats
-// each of query and accumulator room for two waves per SIMD.
-constexpr int pick_unroll(int D, int G, int LPK) {
-  int nv4 = D / (4 * LPK);
-  int u = nv4 >= 8 ? 1 : 8 / nv4;
-  while (u > 1 && G * u > 16) u /= 2;
-  return SLOT_KV_UNROLL ? SLOT_KV_UNROLL : u;
-}
+// Lanes per key row (LPK) and keys per key group per stage come from
+// decode_lpk / decode_unroll.  The lane's elements of a head vector are
+// d = i*4*LPK + 4*r + c (slice i, lane r of the key group, component c);
+// queries reach that layout from their LDS staging, where they were rotated.
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
@@ -95,9 +73,6 @@ __device__ __forceinline__ float dot4(f4 a, f4 b) {
 }
 
 __device__ __forceinline__ f4 ld4(const float* p) { return *reinterpret_cast<const f4*>(p); }
-#ifndef SLOT_KV_FUSED_MERGE
-#define SLOT_KV_FUSED_MERGE 1  // merge split rows inside the decode kernel
-#endif
 #ifndef SLOT_KV_NT_LOADS
 #define SLOT_KV_NT_LOADS 1  // stream history rows past the caches
 #endif
@@ -122,6 +97,19 @@ __device__ __forceinline__ float load_agent(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Increment of an epoch-tagged queue or counter word (see kEpochShift): with
+// `raise`, the word is first lifted to this launch's epoch, which restarts
+// its count at zero if an older launch left it; returns the count before the
+// increment.  Both atomics come from one lane in program order, so they
+// reach the word in that order.
+__device__ __forceinline__ uint32_t epoch_increment(uint64_t* word, uint64_t epoch_tag,
+                                                    bool raise) {
+  if (raise) (void)__hip_atomic_fetch_max(word, epoch_tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t old = __hip_atomic_fetch_add(word, uint64_t(1), __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+  return static_cast<uint32_t>(old & kCountMask);
+}
+
 // max without the NaN canonicalisation of fmaxf (inputs are never NaN here).
 __device__ __forceinline__ float max_nc(float a, float b) { return a > b ? a : b; }
 
@@ -141,12 +129,9 @@ __device__ __forceinline__ uint32_t mbox_wait(const uint32_t* slot) {
   return __builtin_amdgcn_readfirstlane(v);
 }
 
-// Waves per workgroup.  Eight waves share a unit's keys; G = 8 keeps four,
-// since its lanes hold twice the query and accumulator state and the larger
-// workgroups measured slower there.
 template <int G>
 constexpr int wg_waves() {
-  return SLOT_KV_WG_WAVES ? SLOT_KV_WG_WAVES : (G >= 8 ? 4 : 8);
+  return decode_waves(G);
 }
 
 template <int D, int G>
@@ -163,24 +148,38 @@ struct alignas(16) Lds {
 // register file.
 template <int D, int G>
 constexpr int waves_per_eu() {
-  return G * D / pick_lpk(D, G) > 64 ? 1 : SLOT_KV_WAVES_PER_EU;
+  return G * D / decode_lpk(D, G) > 64 ? 1 : SLOT_KV_WAVES_PER_EU;
+}
+
+// The most stages per pass that any wave of a unit takes, over every count
+// of history keys a chunk can hold.
+constexpr uint32_t max_wave_stages(int D, int G, int chunk) {
+  uint32_t most = 0;
+  for (uint32_t n = 0; n <= static_cast<uint32_t>(chunk); ++n)
+    for (uint32_t w = 0; w < static_cast<uint32_t>(decode_waves(G)); ++w) {
+      const uint32_t st = wave_keys(n, decode_step(D, G), decode_waves(G), w).n_st;
+      most = st > most ? st : most;
+    }
+  return most;
 }
 
 template <int D, int G>
 struct Shape {
-  static constexpr int NW = wg_waves<G>();                   // waves per workgroup
-  static constexpr int LPK = pick_lpk(D, G);
-  static constexpr int U = pick_unroll(D, G, LPK);
+  static constexpr int NW = decode_waves(G);                 // waves per workgroup
+  static constexpr int LPK = decode_lpk(D, G);
+  static constexpr int U = decode_unroll(D, G);
   static constexpr int NV4 = D / (4 * LPK);                  // float4 per lane per head vector
   static constexpr int NG = kWave / LPK;                     // key groups per wave
   static constexpr int SL = 4 * LPK;                         // floats per slice
   static constexpr int STEP = NG * U;                        // keys per wave per stage
-  static constexpr int KPW = SLOT_KV_CHUNK / NW;             // history keys per wave, at most
-  // stages per pass, at most: a wave's share of a chunk, padded to even
-  static constexpr int NST = ((KPW + STEP - 1) / STEP + 1) & ~1;
+  // stages per pass the wave's LDS score buffer holds
+  static constexpr int NST = decode_stage_bound(D, G, SLOT_KV_CHUNK);
   static constexpr int SCORES = NST * NG * G * U;            // score slots per wave
+  static_assert(STEP == decode_step(D, G), "one stage size");
   static_assert(NV4 >= 1 && D % (4 * LPK) == 0, "whole float4 slices per lane");
   static_assert(SLOT_KV_CHUNK % NW == 0, "a chunk splits evenly over the waves");
+  static_assert(max_wave_stages(D, G, SLOT_KV_CHUNK) <= static_cast<uint32_t>(NST),
+                "no wave's stages outgrow its LDS score buffer");
 };
 
 // One work unit as one wave sees it: chunk `chunk` of row b against kv head
@@ -218,18 +217,11 @@ __device__ __forceinline__ UnitPlan plan_unit(const AttnArgs& a, const UnitId& i
   u.n_chunks = u.pos / p.chunk + 1;
   const uint32_t c0 = u.chunk * p.chunk;
   const uint32_t t_end = min(c0 + p.chunk, u.pos);
-  // The chunk's history keys, in pipeline stages of STEP keys, split as
-  // evenly as whole stages allow over the NW waves: a short last chunk keeps
-  // every wave busy (a full chunk gives each wave C/NW keys).
-  const uint32_t n_keys = t_end - c0;
-  const uint32_t steps = (n_keys + S::STEP - 1) / S::STEP;
-  u.k_begin = c0 + min(steps * w / NW * S::STEP, n_keys);
-  u.len = c0 + min(steps * (w + 1) / NW * S::STEP, n_keys) - u.k_begin;
-  u.n_full = u.len / S::STEP;
-  // stages per pass, rounded up to an even count (the stages past the keys
-  // are masked) so that each pass ends in the same buffer
-  const uint32_t n_st = u.n_full + (u.len % S::STEP != 0 ? 1u : 0u);
-  u.n_st = (n_st + 1) & ~1u;
+  const WaveKeys wk = wave_keys(t_end - c0, S::STEP, NW, w);
+  u.k_begin = c0 + wk.begin;
+  u.len = wk.len;
+  u.n_full = wk.n_full;
+  u.n_st = wk.n_st;
   u.new_key = (w == 0) && (u.chunk == u.n_chunks - 1);
   return u;
 }
@@ -432,10 +424,11 @@ __device__ __forceinline__ void merge_row(const AttnParams& p, uint32_t b, uint3
 // other waves read it there, so every workgroup holds at most one unit it has
 // not begun, and only while its second pass runs.  Units are ordered full chunks
 // first, then partial chunks longest first, so the work left at the end is
-// short.  The last workgroup to exit returns the queue to zero for the next
-// launch.  No workgroup ever waits for another.  A row of one chunk is
-// finished here; a longer row leaves one unnormalised partial per chunk,
-// merged by the row's last workgroup (or by merge_kernel).
+// short.  The queue word and the split rows' counters carry the launch's
+// epoch, so no launch has to leave them cleared for the next.  No workgroup
+// ever waits for another.  A row of one chunk is finished here; a longer row
+// leaves one unnormalised partial per chunk, merged by the row's last
+// workgroup.
 template <int D, int G>
 __global__ void __launch_bounds__(kWave * wg_waves<G>())
     __attribute__((amdgpu_waves_per_eu(waves_per_eu<D, G>()))) decode_attn_kernel(const AttnArgs a) {
@@ -482,9 +475,10 @@ __global__ void __launch_bounds__(kWave * wg_waves<G>())
     // end of the current one, so that few units sit reserved when the queue
     // runs dry.
     uint32_t ticket = 0;
+    // (The workgroup's first ask lifts the queue word to this launch's epoch;
+    // its later asks find it there.)
     auto ask_next = [&]() {
-      if (tid == 0)
-        ticket = __hip_atomic_fetch_add(&p.sched[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) ticket = epoch_increment(p.sched, p.epoch_tag, it == 0);
     };
     uint32_t nxt = kNoUnit;
     bool has_next = false;
@@ -689,23 +683,25 @@ __global__ void __launch_bounds__(kWave * wg_waves<G>())
         sh.l[w][g] = l[g];
       }
     }
-#if SLOT_KV_FUSED_MERGE
-    // The previous unit's partial stores were issued a whole unit ago; once
-    // every wave has waited for them (nothing else of note is in flight
-    // here) they are visible on every XCD, and the counter increment after
-    // the barrier publishes them.  Its result is read at the end of this unit.
+    // Publication of the previous unit's partial.  Its stores are agent-scope
+    // atomic stores, written through to the level all XCDs share, and were
+    // issued a whole unit ago; every wave waits for them to be acknowledged
+    // (nothing else of note is in flight here), the barrier then orders all
+    // waves' completed stores before the counter increment that one lane
+    // issues after it.  The merging workgroup reads the partials only after
+    // the increment that completes the count has returned, with agent-scope
+    // atomic loads, which read that shared level.  This is the lowering of an
+    // agent-scope release / acquire pair without the L2 writeback and
+    // invalidate, which only non-atomic data would need.  The increment's
+    // result is read at the end of this unit.
     if (pending) {
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __builtin_amdgcn_s_waitcnt(0);
     }
-#endif
     __syncthreads();
-#if SLOT_KV_FUSED_MERGE
     uint32_t done_prev = 0;
     if (pending && tid == 0)
-      done_prev = __hip_atomic_fetch_add(&p.counters[pend_b * p.n_kv_heads + pend_j], 1u,
-                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#endif
+      done_prev = epoch_increment(&p.counters[pend_b * p.n_kv_heads + pend_j], p.epoch_tag, true);
     const uint32_t h0 = u.j * G;
     const bool split = u.n_chunks > 1;
     for (uint32_t e = tid; e < G * D; e += kThreads) {
@@ -732,19 +728,11 @@ __global__ void __launch_bounds__(kWave * wg_waves<G>())
         p.out[(static_cast<size_t>(u.b) * p.n_heads + h0 + g) * D + d] = Acc * (sa / L);
       } else {
         const size_t ph = (static_cast<size_t>(u.b) * p.max_chunks + u.chunk) * p.n_heads + h0 + g;
-#if SLOT_KV_FUSED_MERGE
         store_agent(&p.part_acc[ph * D + d], Acc);
         if (d == 0) {
           store_agent(&p.part_ml[ph * 2 + 0], M);
           store_agent(&p.part_ml[ph * 2 + 1], L);
         }
-#else
-        p.part_acc[ph * D + d] = Acc;
-        if (d == 0) {
-          p.part_ml[ph * 2 + 0] = M;
-          p.part_ml[ph * 2 + 1] = L;
-        }
-#endif
       }
     }
     // the next unit's queries: their raw loads went out with take_next
@@ -757,59 +745,34 @@ __global__ void __launch_bounds__(kWave * wg_waves<G>())
       }
     };
     prefetch_next();
-#if SLOT_KV_FUSED_MERGE
     if (pending) {  // workgroup-uniform
       // the last workgroup of the previous partial's (row, kv head) merges
       // the row's chunks in order
       if (tid == 0) sh.last = (done_prev == pend_n - 1) ? 1u : 0u;
       __syncthreads();
-      if (sh.last) {
-        merge_row<D, G>(p, pend_b, pend_j, pend_n, tid, kThreads);
-        if (tid == 0)  // ready for the next launch
-          __hip_atomic_store(&p.counters[pend_b * p.n_kv_heads + pend_j], 0u, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-      }
+      if (sh.last) merge_row<D, G>(p, pend_b, pend_j, pend_n, tid, kThreads);
     }
     pending = split;
     pend_b = u.b;
     pend_j = u.j;
     pend_n = u.n_chunks;
-#endif
     if (tid == 0)  // every wave read it before the merge barrier
       __hip_atomic_store(&mbox[par], kNoUnit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     __syncthreads();  // LDS free for the next unit
     if (!has_next) break;
     u = plan_unit<D, G>(a, un, w);
   }
-#if SLOT_KV_FUSED_MERGE
-  if (pending) {  // the last unit's partial: publish it now
+  if (pending) {  // the last unit's partial: publish it now (as above)
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
-      const uint32_t done = __hip_atomic_fetch_add(&p.counters[pend_b * p.n_kv_heads + pend_j], 1u,
-                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t done =
+          epoch_increment(&p.counters[pend_b * p.n_kv_heads + pend_j], p.epoch_tag, true);
       sh.last = (done == pend_n - 1) ? 1u : 0u;
     }
     __syncthreads();
-    if (sh.last) {
-      merge_row<D, G>(p, pend_b, pend_j, pend_n, tid, kThreads);
-      if (tid == 0)
-        __hip_atomic_store(&p.counters[pend_b * p.n_kv_heads + pend_j], 0u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-#endif
-
-  if (tid == 0) {
-    // Every queue fetch of this workgroup has returned (its value ended the
-    // loop), so it is complete before this increment is issued.
-    const uint32_t exited = __hip_atomic_fetch_add(&p.sched[1], 1u, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-    if (exited == n_blocks - 1) {
-      __hip_atomic_store(&p.sched[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&p.sched[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (sh.last) merge_row<D, G>(p, pend_b, pend_j, pend_n, tid, kThreads);
   }
 }
 
@@ -849,27 +812,12 @@ __device__ __forceinline__ void merge_row(const AttnParams& p, uint32_t b, uint3
   }
 }
 
-// Stand-alone merge (when the decode kernel does not merge): one workgroup
-// per (row, kv head).
-template <int D, int G>
-__global__ void __launch_bounds__(256) merge_kernel(const AttnArgs a) {
-  if (a.magic != kArgsMagic) return;
-  const AttnParams& p = a.p;
-  const uint32_t b = blockIdx.x / p.n_kv_heads, j = blockIdx.x % p.n_kv_heads;
-  if (b >= p.n_rows) return;
-  const uint32_t n_chunks = a.rows.pos[b] / p.chunk + 1;
-  if (n_chunks == 1) return;  // finished by the decode kernel
-  merge_row<D, G>(p, b, j, n_chunks, threadIdx.x, 256);
-}
-
 template <int D, int G>
 hipError_t launch_shape(const AttnArgs& a, uint32_t blocks, hipStream_t s, hipEvent_t mark) {
   hipLaunchKernelGGL((decode_attn_kernel<D, G>), dim3(blocks), dim3(kWave * wg_waves<G>()), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && mark) e = hipEventRecord(mark, s);
-  if (e != hipSuccess || a.p.max_chunks <= 1 || SLOT_KV_FUSED_MERGE) return e;
-  hipLaunchKernelGGL((merge_kernel<D, G>), dim3(a.p.n_rows * a.p.n_kv_heads), dim3(256), 0, s, a);
-  return hipGetLastError();
+  return e;
 }
 
 template <int D, int G>

@@ -5,6 +5,7 @@
 // max(slots), slot_ctx > max(positions); each row owns its slot, so a slot
 // named twice in one batch is rejected (two rows would race on its rows).
 #include <algorithm>
+#include <atomic>
 #include <vector>
 
 #include "slot_kv.h"
@@ -51,6 +52,15 @@ LaunchWork fill_rows(LaunchRows& rows, const uint32_t* positions, const uint32_t
   for (uint32_t t = 0; t < n_tails; ++t) rows.tail_row[t] = static_cast<uint8_t>(tails[t]);
   work.n_items = work.n_full + n_tails;
   return work;
+}
+
+uint64_t next_epoch() {
+  static std::atomic<uint64_t> last{0};
+  uint64_t e = last.load(std::memory_order_relaxed);
+  do {
+    if (e >= kMaxEpoch) return 0;
+  } while (!last.compare_exchange_weak(e, e + 1, std::memory_order_relaxed));
+  return e + 1;
 }
 
 }  // namespace slotkv

@@ -82,6 +82,40 @@ def test_unallocated_handle_paths():
     assert b._lib.slot_kv_create(None) == b.SLOT_KV_EINVAL
 
 
+def test_alloc_size_overflow_is_einval_before_any_device_call():
+    # "Forward Cuda Gemma", allocSlotKv; "Forward Cuda", slot state: a K/V
+    # buffer holds n_slots * slot_ctx * kv_dim floats, a state buffer
+    # n_slots * len.  A byte size past 2^64 - 1 would wrap to a small
+    # allocation that the 64-bit offsets then overrun, so it is rejected
+    # with EINVAL before any HIP call (here, with no GPU, any device call
+    # would return EDEVICE instead).
+    u = lambda a: np.asarray(a, np.uint32)  # noqa: E731
+    p = lambda a: a.ctypes.data_as(b._u32p)  # noqa: E731
+    h = b.slot_kv_create()
+    try:
+        dims = u([2**30])
+        # 2^16 * 2^16 * 2^30 * 4 = 2^64: wraps to 0 in 64-bit arithmetic
+        assert b._lib.slot_kv_alloc(h, 65536, 65536, p(dims), 1) == b.SLOT_KV_EINVAL
+        two = u([128, 2**30])  # the second layer overflows: nothing is allocated
+        assert b._lib.slot_kv_alloc(h, 65536, 65536, p(two), 2) == b.SLOT_KV_EINVAL
+        assert b._lib.slot_kv_alloc(h, 2**32 - 1, 2**32 - 1, p(u([2**31])), 1) == b.SLOT_KV_EINVAL
+        # the state analogues: n_slots * len * 4 past 2^64 - 1
+        ok, big = u([8]), u([2**31])
+        assert b._lib.slot_state_alloc(h, 2**32 - 1, 1, None, 0, p(big), p(ok),
+                                       1) == b.SLOT_KV_EINVAL
+        assert b._lib.slot_state_alloc(h, 2**32 - 1, 1, None, 0, p(ok), p(big),
+                                       1) == b.SLOT_KV_EINVAL
+        assert b._lib.slot_state_alloc(h, 2**32 - 1, 2, p(dims), 1, p(ok), p(ok),
+                                       1) == b.SLOT_KV_EINVAL  # attention part overflows
+        assert b.slot_kv_offset_bytes(h, 0, 0, 0)[0] == b.SLOT_KV_ENOTALLOC  # nothing kept
+        # one float short of the wrap passes the size check and reaches the
+        # device (which this host does not have, or which cannot hold it)
+        rc = b._lib.slot_kv_alloc(h, 65535, 65536, p(dims), 1)
+        assert rc in (b.SLOT_KV_EDEVICE, b.SLOT_KV_ENOMEM)
+    finally:
+        b.slot_kv_destroy(h)
+
+
 @pytest.mark.parametrize("seed", range(20))
 def test_check_batch_agrees_with_oracle(seed):
     # Host validation of the library against the oracle's preconditions on

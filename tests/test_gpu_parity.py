@@ -262,8 +262,9 @@ def test_mid_batch_equals_serial_bit_exact(mid_setup):
 # ---------------------------------------------------------------- many short
 def test_many_short_full_parity_with_poison():
     # 256 rows, 26 of them at pos 0 in reused slots whose later rows hold
-    # stale data: every cell a row may not read is poisoned (qNaN, then
-    # +-1e30); outputs stay finite and equal the oracle's.
+    # stale data: every cell a row may not read, from its own position on, is
+    # poisoned (qNaN, then +-1e30); outputs stay finite and equal the
+    # oracle's, and the poison outside the written rows survives the step.
     w = wl.many_short()
     _say(f"many: B={w.B} pos0 rows={(w.positions == 0).sum()}")
     kv = handle_for(w)
@@ -275,17 +276,33 @@ def test_many_short_full_parity_with_poison():
     used = np.zeros(w.n_slots, bool)
     used[w.slots] = True
     for poison in (float("nan"), 1e30, -1e30):
+        # the row at pos itself too: the step must overwrite it, and must not
+        # read what it held
         for bi in range(w.B):
             s, p = int(w.slots[bi]), int(w.positions[bi])
-            kbuf[s, p + 1:] = poison
-            vbuf[s, p + 1:] = poison
+            kbuf[s, p:] = poison
+            vbuf[s, p:] = poison
         idle = torch.from_numpy(np.nonzero(~used)[0]).cuda()
         if idle.numel():
             kbuf[idle] = poison
             vbuf[idle] = poison
+        k_snap, v_snap = kbuf.clone(), vbuf.clone()
         out = kv.decode_attn(0, q, k_new, v_new, w.positions, w.slots).cpu().numpy()
         for bi in range(w.B):
             assert_close(out[bi], ref[bi][2], f"many row {bi} poison {poison}")
+        # every poisoned cell still holds the poison: exactly the B written
+        # rows changed, bit for bit; those rows hold the rotated key (within
+        # tolerance) and v_new's bytes
+        changed = {tuple(x) for x in
+                   ((kbuf.view(torch.int32) != k_snap.view(torch.int32)).any(-1) |
+                    (vbuf.view(torch.int32) != v_snap.view(torch.int32)).any(-1))
+                   .nonzero().cpu().tolist()}
+        assert changed == {(int(s), int(p)) for s, p in zip(w.slots, w.positions)}
+        del k_snap, v_snap
+        for bi in range(w.B):
+            s, p = int(w.slots[bi]), int(w.positions[bi])
+            assert vbuf[s, p].cpu().numpy().tobytes() == ref[bi][1].tobytes()
+            assert_close(kbuf[s, p].cpu().numpy(), ref[bi][0], f"many K row {bi}")
     kv.close()
 
 
