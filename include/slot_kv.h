@@ -42,6 +42,7 @@ extern "C" {
 #define SLOT_KV_ENOMEM (-4)    /* a device or pinned-host allocation failed          */
 #define SLOT_KV_EDUP (-5)      /* one slot named by two rows of a batch              */
 #define SLOT_KV_EDEVICE (-6)   /* HIP runtime or launch error                        */
+#define SLOT_KV_ESCRATCH (-7)  /* more scratch than slot_decode_attn_noalloc's array  */
 
 typedef struct slot_kv slot_kv; /* opaque; owns all slot KV device memory */
 
@@ -188,6 +189,31 @@ int slot_decode_attn(slot_kv *h, uint32_t layer, const float *q,
                      const float *k_new, const float *v_new,
                      const uint32_t *positions, const uint32_t *slots,
                      uint32_t B, float *out, void *stream);
+
+/* For callers that cannot allocate device memory during the call: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same step as slot_decode_attn, with the same arguments, kernels,
+ * results (bit for bit) and errors, but the call makes no allocation of any
+ * kind and no synchronisation: its scratch (the split rows' partial results
+ * and the work queue's counters) lives in one fixed array per GPU, 64 MiB,
+ * reserved when the library's code is loaded on that GPU and held until the
+ * process ends.  The array's address is looked up when slot_kv_alloc (or
+ * slot_state_alloc) runs on the device.  Limit: the partials of a launch
+ * (256 rows; rows * (largest chunk count of those rows) * n_heads *
+ * (head_dim + 2) floats, a row at position p counting p / slot_kv_chunk_keys()
+ * + 1 chunks) must fit 64 MiB - 256 KiB, and n_kv_heads * 256 + 1 counter
+ * words 256 KiB (n_kv_heads <= 127); a larger call returns SLOT_KV_ESCRATCH
+ * before anything is enqueued.  The counters carry a per-launch epoch, so
+ * nothing in the array needs clearing between calls.  Every call on one GPU,
+ * from any handle, shares the array: calls that can run at the same time on
+ * one GPU (different streams) race and give wrong results; calls on one
+ * stream are ordered.  Launches are not recorded by slot_kv_profile_*.
+ * Errors: those of slot_decode_attn, SLOT_KV_ESCRATCH, and EDEVICE when the
+ * array's address could not be looked up. */
+int slot_decode_attn_noalloc(slot_kv *h, uint32_t layer, const float *q,
+                             const float *k_new, const float *v_new,
+                             const uint32_t *positions, const uint32_t *slots,
+                             uint32_t B, float *out, void *stream);
 
 /* "Forward Cuda", batched prefill that writes the KV cache into a slot's
  * per-sequence region; "Forward Cuda Gemma", prefillBatched, defined there as

@@ -25,10 +25,12 @@ SLOT_KV_ENOTALLOC = -3
 SLOT_KV_ENOMEM = -4
 SLOT_KV_EDUP = -5
 SLOT_KV_EDEVICE = -6
+SLOT_KV_ESCRATCH = -7
 
 # Every symbol include/slot_kv.h declares.
 EXPORTS = ("slot_kv_create", "slot_kv_destroy", "slot_kv_alloc", "slot_kv_set_layer",
            "slot_kv_set_layer_flags", "slot_kv_offset_bytes", "slot_reset", "slot_decode_attn",
+           "slot_decode_attn_noalloc",
            "slot_prefill_attn",
            "slot_verify_attn", "slot_state_alloc", "slot_conv_offset_bytes",
            "slot_ssm_offset_bytes", "slot_state_ptrs", "slot_reset_batch",
@@ -68,6 +70,7 @@ _lib.slot_ssm_offset_bytes.argtypes = [_vp, _u32, _u32, ctypes.POINTER(ctypes.c_
 _lib.slot_state_ptrs.argtypes = [_vp, _u32, ctypes.POINTER(_vp), ctypes.POINTER(_vp)]
 _lib.slot_kv_set_layer_flags.argtypes = [_vp, _u32, _u32]
 _lib.slot_decode_attn.argtypes = [_vp, _u32, _vp, _vp, _vp, _u32p, _u32p, _u32, _vp, _vp]
+_lib.slot_decode_attn_noalloc.argtypes = _lib.slot_decode_attn.argtypes
 _lib.slot_prefill_attn.argtypes = [_vp, _u32, _vp, _vp, _vp, _u32, _u32, _u32, _vp, _vp]
 _lib.slot_verify_attn.argtypes = [_vp, _u32, _vp, _vp, _vp, _u32p, _u32p, _u32p, _u32, _vp, _vp]
 _lib.slot_kv_layer_ptrs.argtypes = [_vp, _u32, ctypes.POINTER(_vp), ctypes.POINTER(_vp)]
@@ -228,6 +231,20 @@ def slot_decode_attn(h, layer, q, k_new, v_new, positions, slots, out, stream=No
     ptrs = [_dev_ptr(t, n) for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (out, "out"))]
     return _lib.slot_decode_attn(h, layer, ptrs[0], ptrs[1], ptrs[2], _ptr_u32(pos), _ptr_u32(sl),
                                  B, ptrs[3], _stream_handle(stream))
+
+
+def slot_decode_attn_noalloc(h, layer, q, k_new, v_new, positions, slots, out,
+                             stream=None) -> int:
+    """Raw call of the allocation-free decode (scratch in the library's fixed
+    per-GPU array); same arguments as slot_decode_attn."""
+    pos = _host_u32(positions)
+    sl = _host_u32(slots)
+    if pos.shape != sl.shape or pos.ndim != 1:
+        return SLOT_KV_EINVAL
+    B = int(pos.shape[0])
+    ptrs = [_dev_ptr(t, n) for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (out, "out"))]
+    return _lib.slot_decode_attn_noalloc(h, layer, ptrs[0], ptrs[1], ptrs[2], _ptr_u32(pos),
+                                         _ptr_u32(sl), B, ptrs[3], _stream_handle(stream))
 
 
 def slot_prefill_attn(h, layer, q, k_new, v_new, slot, pos0, out, stream=None) -> int:

@@ -16,6 +16,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -177,6 +178,40 @@ int ensure_counters(slot_kv* h, size_t entries) {
   return SLOT_KV_OK;
 }
 
+// ---------------------------------------------------------------- fixed scratch
+// The scratch of slot_decode_attn_noalloc: one array per device, held until
+// the process ends, shared by every call on that device.  Its first
+// kScratchCounterBytes hold the queue word and the split-row counters
+// (epoch-tagged, so they start valid at zero and are never cleared), the rest
+// the partials.  Host code never uses the array's name as an address: the
+// address comes from hipGetSymbolAddress, looked up once per device.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr size_t kScratchCounterBytes = size_t(256) << 10;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};  // per device; null until looked up
+
+// Looks up this device's scratch address (the device is current); once per
+// device.
+void scratch_setup(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev]) return;
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess && ptr)
+    g_scratch_ptr[dev] = ptr;
+  else
+    (void)hipGetLastError();  // the allocation-free decode then returns EDEVICE
+}
+
+void* scratch_of(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -227,6 +262,7 @@ int slot_state_alloc(slot_kv* h, uint32_t n_slots, uint32_t slot_ctx, const uint
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return SLOT_KV_EDEVICE;
   h->device = dev;
+  scratch_setup(dev);  // the allocation-free decode's scratch on this device
   // Everything is allocated into h's vectors as it goes, so a failure part
   // way frees exactly what was made.
   auto fail = [h](int rc) {
@@ -435,23 +471,31 @@ int slot_kv_check_batch(uint32_t n_slots, uint32_t slot_ctx, const uint32_t* pos
 
 uint32_t slot_kv_chunk_keys(void) { return SLOT_KV_CHUNK; }
 
-int slot_decode_attn(slot_kv* h, uint32_t layer, const float* q, const float* k_new,
-                     const float* v_new, const uint32_t* positions, const uint32_t* slots,
-                     uint32_t B, float* out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Scratch a decode call needs: the partials of its largest launch (floats)
+// and the queue word plus the per-(row, kv head) counters (64-bit words).
+struct DecodeNeeds {
+  size_t part_floats = 0;
+  size_t counter_words = 0;
+};
+
+// Validates a decode call (nothing is enqueued) and sizes its scratch.
+int plan_decode(const slot_kv* h, uint32_t layer, const float* q, const float* k_new,
+                const float* v_new, const uint32_t* positions, const uint32_t* slots,
+                uint32_t B, const float* out, DecodeNeeds* needs) {
   int rc = check_layer(h, layer);
   if (rc) return rc;
-  LayerState& L = h->layers[layer];
+  const LayerState& L = h->layers[layer];
   if (!L.configured) return SLOT_KV_EINVAL;
   if (B == 0) return SLOT_KV_OK;
   if (!q || !k_new || !v_new || !out) return SLOT_KV_EINVAL;
   rc = slotkv::check_batch(h->n_slots, h->slot_ctx, positions, slots, B);
   if (rc) return rc;
   const uint32_t C = SLOT_KV_CHUNK;
-  const size_t D = L.head_dim;
   const uint32_t R = slotkv::kMaxRowsPerLaunch;
-  const uint32_t G = L.n_heads / L.n_kv_heads;
-
-  // Size the scratch for the largest launch before enqueueing anything.
   size_t part_floats = 0;
   for (uint32_t r0 = 0; r0 < B; r0 += R) {
     const uint32_t n = std::min(B - r0, R);
@@ -464,12 +508,26 @@ int slot_decode_attn(slot_kv* h, uint32_t layer, const float* q, const float* k_
     // a launch's units are counted below the epoch bits of the queue word
     // (no cache that fits a GPU's memory comes near this)
     if (items * L.n_kv_heads > slotkv::kCountMask) return SLOT_KV_EINVAL;
-    part_floats = std::max(part_floats, static_cast<size_t>(n * max_chunks) * L.n_heads * (D + 2));
+    part_floats = std::max(part_floats,
+                           static_cast<size_t>(n * max_chunks) * L.n_heads * (L.head_dim + 2));
   }
-  rc = ensure_partials(h, part_floats);
-  if (rc) return rc;
-  rc = ensure_counters(h, 1 + static_cast<size_t>(R) * L.n_kv_heads);
-  if (rc) return rc;
+  needs->part_floats = part_floats;
+  needs->counter_words = 1 + static_cast<size_t>(R) * L.n_kv_heads;
+  return SLOT_KV_OK;
+}
+
+// Enqueues a validated decode call (B > 0): one launch of the fused kernel
+// per kMaxRowsPerLaunch rows, its partials in `part` and its queue word and
+// counters in `counters` (scratch sized by plan_decode).  With `profile`, the
+// handle's event pairs are recorded around each launch.
+int run_decode(slot_kv* h, uint32_t layer, const float* q, const float* k_new,
+               const float* v_new, const uint32_t* positions, const uint32_t* slots, uint32_t B,
+               float* out, void* stream, float* part, uint64_t* counters, bool profile) {
+  const LayerState& L = h->layers[layer];
+  const uint32_t C = SLOT_KV_CHUNK;
+  const size_t D = L.head_dim;
+  const uint32_t R = slotkv::kMaxRowsPerLaunch;
+  const uint32_t G = L.n_heads / L.n_kv_heads;
   const uint32_t resident = slotkv::resident_blocks(L.head_dim, G);
   if (resident == 0) return SLOT_KV_EDEVICE;
 
@@ -479,8 +537,8 @@ int slot_decode_attn(slot_kv* h, uint32_t layer, const float* q, const float* k_
   AttnParams& p = a.p;
   p.k_cache = L.k;
   p.v_cache = L.v;
-  p.sched = h->counters;
-  p.counters = h->counters + 1;
+  p.sched = counters;
+  p.counters = counters + 1;
   p.q_norm_w = L.params;
   p.k_norm_w = L.params + D;
   p.inv_freq = L.params + 2 * D;
@@ -505,21 +563,58 @@ int slot_decode_attn(slot_kv* h, uint32_t layer, const float* q, const float* k_
     p.k_new = k_new + static_cast<size_t>(r0) * L.kv_dim;
     p.v_new = v_new + static_cast<size_t>(r0) * L.kv_dim;
     p.out = out + r0 * qd;
-    p.part_acc = h->part;
-    p.part_ml = h->part + static_cast<size_t>(n) * work.max_chunks * L.n_heads * D;
+    p.part_acc = part;
+    p.part_ml = part + static_cast<size_t>(n) * work.max_chunks * L.n_heads * D;
     const uint64_t epoch = slotkv::next_epoch();
     if (epoch == 0) return SLOT_KV_EDEVICE;  // 2^40 launches in one process
     p.epoch_tag = epoch << slotkv::kEpochShift;
 
     hipEvent_t ev_start = nullptr, ev_end = nullptr;
-    rc = prof_pair(h, &ev_start, &ev_end);
-    if (rc) return rc;
+    if (profile) {
+      const int rc = prof_pair(h, &ev_start, &ev_end);
+      if (rc) return rc;
+    }
     if (ev_start && hipEventRecord(ev_start, s) != hipSuccess) return SLOT_KV_EDEVICE;
     const uint32_t blocks = std::min(p.n_units, resident);
     if (slotkv::launch_decode(a, L.head_dim, G, blocks, stream, ev_end) != hipSuccess)
       return SLOT_KV_EDEVICE;
   }
   return SLOT_KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int slot_decode_attn(slot_kv* h, uint32_t layer, const float* q, const float* k_new,
+                     const float* v_new, const uint32_t* positions, const uint32_t* slots,
+                     uint32_t B, float* out, void* stream) {
+  DecodeNeeds needs;
+  int rc = plan_decode(h, layer, q, k_new, v_new, positions, slots, B, out, &needs);
+  if (rc || B == 0) return rc;
+  // Size the scratch for the largest launch before enqueueing anything.
+  rc = ensure_partials(h, needs.part_floats);
+  if (rc) return rc;
+  rc = ensure_counters(h, needs.counter_words);
+  if (rc) return rc;
+  return run_decode(h, layer, q, k_new, v_new, positions, slots, B, out, stream, h->part,
+                    h->counters, h->profiling);
+}
+
+int slot_decode_attn_noalloc(slot_kv* h, uint32_t layer, const float* q, const float* k_new,
+                             const float* v_new, const uint32_t* positions,
+                             const uint32_t* slots, uint32_t B, float* out, void* stream) {
+  DecodeNeeds needs;
+  int rc = plan_decode(h, layer, q, k_new, v_new, positions, slots, B, out, &needs);
+  if (rc || B == 0) return rc;
+  if (needs.counter_words * sizeof(uint64_t) > kScratchCounterBytes ||
+      needs.part_floats * sizeof(float) > kScratchBytes - kScratchCounterBytes)
+    return SLOT_KV_ESCRATCH;
+  unsigned char* base = static_cast<unsigned char*>(scratch_of(h->device));
+  if (!base) return SLOT_KV_EDEVICE;  // the look-up at allocation failed
+  return run_decode(h, layer, q, k_new, v_new, positions, slots, B, out, stream,
+                    reinterpret_cast<float*>(base + kScratchCounterBytes),
+                    reinterpret_cast<uint64_t*>(base), false);
 }
 
 namespace {
@@ -856,6 +951,7 @@ const char* slot_kv_strerror(int status) {
     case SLOT_KV_ENOMEM: return "out of memory";
     case SLOT_KV_EDUP: return "slot used by two rows of one batch";
     case SLOT_KV_EDEVICE: return "HIP device error";
+    case SLOT_KV_ESCRATCH: return "call needs more scratch than the fixed array holds";
     default: return "unknown status";
   }
 }

@@ -296,9 +296,12 @@ constexpr uint32_t kChunkTargetGroups = 1024;
 int launch_prefill(const PrefillArgs& a, uint32_t head_dim, uint32_t group, bool split,
                    void* stream, void* before_attn, void* after_attn);
 
-// Validation of one batch (no device access).  Returns a SLOT_KV_* status.
+// Validation of one batch (no device access, no allocation).  Returns a
+// SLOT_KV_* status.
 int check_batch(uint32_t n_slots, uint32_t slot_ctx, const uint32_t* positions,
                 const uint32_t* slots, uint32_t B);
+// Whether a slot appears twice among slots[0..n) (no allocation).
+bool has_duplicate(const uint32_t* slots, uint32_t n);
 
 // Work of one launch over rows [0, n) of positions / slots.
 struct LaunchWork {

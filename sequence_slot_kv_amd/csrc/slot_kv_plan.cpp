@@ -6,12 +6,38 @@
 // named twice in one batch is rejected (two rows would race on its rows).
 #include <algorithm>
 #include <atomic>
-#include <vector>
+#include <cstring>
 
 #include "slot_kv.h"
 #include "slot_kv_internal.h"
 
 namespace slotkv {
+
+bool has_duplicate(const uint32_t* slots, uint32_t n) {
+  if (n < 2) return false;
+  // One bit per slot, over windows of kWindow slots between the smallest and
+  // the largest slot named: a fixed stack bitmap, so the check allocates
+  // nothing (slot counts up to kWindow take a single pass).
+  constexpr uint32_t kWindow = 1u << 16;
+  uint64_t bits[kWindow / 64];
+  uint32_t lo = slots[0], hi = slots[0];
+  for (uint32_t i = 1; i < n; ++i) {
+    lo = std::min(lo, slots[i]);
+    hi = std::max(hi, slots[i]);
+  }
+  for (uint64_t base = lo; base <= hi; base += kWindow) {
+    std::memset(bits, 0, sizeof(bits));
+    for (uint32_t i = 0; i < n; ++i) {
+      const uint64_t off = slots[i] - base;
+      if (slots[i] < base || off >= kWindow) continue;
+      uint64_t& word = bits[off >> 6];
+      const uint64_t bit = uint64_t(1) << (off & 63);
+      if (word & bit) return true;
+      word |= bit;
+    }
+  }
+  return false;
+}
 
 int check_batch(uint32_t n_slots, uint32_t slot_ctx, const uint32_t* positions,
                 const uint32_t* slots, uint32_t B) {
@@ -19,15 +45,7 @@ int check_batch(uint32_t n_slots, uint32_t slot_ctx, const uint32_t* positions,
   if (!positions || !slots) return SLOT_KV_EINVAL;
   for (uint32_t b = 0; b < B; ++b)
     if (slots[b] >= n_slots || positions[b] >= slot_ctx) return SLOT_KV_ERANGE;
-  // duplicate detection: one bit per slot
-  std::vector<uint64_t> seen((static_cast<size_t>(n_slots) + 63) / 64, 0);
-  for (uint32_t b = 0; b < B; ++b) {
-    uint64_t bit = uint64_t(1) << (slots[b] & 63);
-    uint64_t& word = seen[slots[b] >> 6];
-    if (word & bit) return SLOT_KV_EDUP;
-    word |= bit;
-  }
-  return SLOT_KV_OK;
+  return has_duplicate(slots, B) ? SLOT_KV_EDUP : SLOT_KV_OK;
 }
 
 LaunchWork fill_rows(LaunchRows& rows, const uint32_t* positions, const uint32_t* slots,

@@ -33,11 +33,11 @@ def test_library_exports_every_declared_symbol():
 
 def test_strerror_names_every_status():
     seen = set()
-    for code in (0, -1, -2, -3, -4, -5, -6):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
         s = b.slot_kv_strerror(code)
         assert s and s != "unknown status"
         seen.add(s)
-    assert len(seen) == 7
+    assert len(seen) == 8
     assert b.slot_kv_strerror(-99) == "unknown status"
 
 
