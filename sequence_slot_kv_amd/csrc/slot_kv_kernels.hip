@@ -576,6 +576,32 @@ __global__ void __launch_bounds__(kWave * wg_waves<G>())
         for (int i = 0; i < NV4; ++i) acc[g][i] = f4{0.f, 0.f, 0.f, 0.f};
       }
     };
+    // Between the passes each stored score becomes its weight exp2(s - max),
+    // once per (key, head) and in place, the wave's lanes taking four entries
+    // at a time: pass 2 then only multiplies (its lanes would otherwise each
+    // take the exponential of every score of their key group).  An entry's
+    // head is fixed by its place in a stage's [key group][G][U] block, and a
+    // block's G*U entries divide 256, so each lane's four heads stay the same
+    // from one step of the loop to the next.
+    auto exp_pass = [&](uint32_t n_st_) {
+      constexpr uint32_t GU = G * U;
+      float mc[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t g_c = ((4 * lane + c) % GU) / U;
+        mc[c] = m[0];
+#pragma unroll
+        for (int g = 1; g < G; ++g) mc[c] = g_c == static_cast<uint32_t>(g) ? m[g] : mc[c];
+      }
+      const uint32_t n_ent = n_st_ * NG * GU;  // a multiple of 4: NG * GU >= 4
+      for (uint32_t e = 4 * lane; e < n_ent; e += 4 * kWave) {
+        f4 v = ld4(sc_w + e);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = fast_exp2(v[c] - mc[c]);  // masked keys: exp2(-inf) = 0
+        st4(sc_w + e, v);
+      }
+    };
+    static_assert(256 % (G * U) == 0 && (NG * G * U) % 4 == 0, "exp pass lane layout");
     auto accumulate = [&](const Stage<D, G>& sg, uint32_t st) {
       const float* src = sc_w + (st * NG + gi) * (G * U);
       float sc[G * U];
@@ -596,7 +622,7 @@ __global__ void __launch_bounds__(kWave * wg_waves<G>())
       for (int g = 0; g < G; ++g) {
 #pragma unroll
         for (int uu = 0; uu < U; ++uu) {
-          const float pu = fast_exp2(sc[g * U + uu] - m[g]);  // masked keys: exp2(-inf) = 0
+          const float pu = sc[g * U + uu];  // exp2(score - max), from the exp pass
           l[g] += pu;
 #pragma unroll
           for (int i = 0; i < NV4; ++i) acc[g][i] += pu * sg.x[uu][i];
@@ -623,6 +649,7 @@ __global__ void __launch_bounds__(kWave * wg_waves<G>())
       }
       finish_max();
       ask_next();
+      exp_pass(n_st);
       uint32_t st = 0;
       for (; st + 2 < n_st; st += 2) {  // pass 2 while two more stages follow
         load_stage<D, G>(p, u, gi, lo, B, n_st + st + 1);
