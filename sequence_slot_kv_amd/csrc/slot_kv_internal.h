@@ -73,11 +73,28 @@ SLOTKV_HD inline void locate_item(const LaunchRows& rows, uint32_t n_rows, uint3
 #endif
 constexpr int kWaveLanes = 64;
 
-// Waves per workgroup.  Eight waves share a unit's keys; G = 8 keeps four,
-// since its lanes hold twice the query and accumulator state and the larger
-// workgroups measured slower there.
-constexpr int decode_waves(int G) {
-  return SLOT_KV_WG_WAVES ? SLOT_KV_WG_WAVES : (G >= 8 ? 4 : 8);
+// Head shapes whose scores and weighted sums run on the matrix cores
+// (v_mfma_f32_16x16x4f32, the kv head's G query heads as the columns of a
+// 16-column tile); the others on the vector ALUs.  A bit per (head_dim,
+// group): bit 4 * log2(head_dim / 64) + log2(G).  G = 8 at head_dim 64 and
+// 128: there the vector form spends most of its time in the per-score
+// reductions, while the tile wastes half its columns; with smaller groups
+// the tile is mostly padding, and that arithmetic measured slower than the
+// vector form under sustained load.  (head_dim 256 would need more
+// registers than two waves per SIMD leave.)
+#ifndef SLOT_KV_MFMA_SHAPES
+#define SLOT_KV_MFMA_SHAPES 0x088u
+#endif
+constexpr bool decode_mfma(int D, int G) {
+  const int di = D == 64 ? 0 : (D == 128 ? 1 : 2);
+  const int gi = G == 1 ? 0 : (G == 2 ? 1 : (G == 4 ? 2 : 3));
+  return (SLOT_KV_MFMA_SHAPES >> (4 * di + gi)) & 1u;
+}
+// Waves per workgroup.  Eight waves share a unit's keys; in the vector-ALU
+// form G = 8 keeps four, since its lanes hold twice the query and
+// accumulator state and the larger workgroups measured slower there.
+constexpr int decode_waves(int D, int G) {
+  return SLOT_KV_WG_WAVES ? SLOT_KV_WG_WAVES : (G >= 8 && !decode_mfma(D, G) ? 4 : 8);
 }
 // Lanes per key row: enough that each lane holds about 32 floats of query
 // (G heads) and as many of accumulator, at most 16 (one DPP row).
@@ -96,15 +113,26 @@ constexpr int decode_unroll(int D, int G) {
   while (u > 1 && G * u > 16) u /= 2;
   return SLOT_KV_UNROLL ? SLOT_KV_UNROLL : u;
 }
-// Keys one wave streams per pipeline stage.
+// 16-key tiles per pipeline stage of the matrix-core form: a stage of
+// about 16 KB per wave (a wave issues a stage's loads one stage ahead, so
+// this sets the bytes it has in flight).
+#ifndef SLOT_KV_MFMA_TILES
+#define SLOT_KV_MFMA_TILES 0  // 0: by head_dim
+#endif
+constexpr int decode_mfma_tiles(int D) {
+  return SLOT_KV_MFMA_TILES ? SLOT_KV_MFMA_TILES : (D <= 64 ? 2 : 1);
+}
+// Keys one wave streams per pipeline stage: 16-key tiles on the matrix
+// cores, else (64 / lanes per key) key groups of `unroll` keys.
 constexpr int decode_step(int D, int G) {
-  return kWaveLanes / decode_lpk(D, G) * decode_unroll(D, G);
+  return decode_mfma(D, G) ? 16 * decode_mfma_tiles(D)
+                           : kWaveLanes / decode_lpk(D, G) * decode_unroll(D, G);
 }
 // Stages per pass that the LDS score buffer of one wave holds: a wave's
 // share of a full chunk of `chunk` keys, padded to even as the stage count
 // of every pass is.
 constexpr int decode_stage_bound(int D, int G, int chunk) {
-  const int kpw = chunk / decode_waves(G);
+  const int kpw = chunk / decode_waves(D, G);
   const int step = decode_step(D, G);
   return ((kpw + step - 1) / step + 1) & ~1;
 }

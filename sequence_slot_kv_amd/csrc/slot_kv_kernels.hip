@@ -31,6 +31,8 @@
 // row's result does not depend on the rest of the batch.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "slot_kv_internal.h"
 
 namespace slotkv {
@@ -129,14 +131,14 @@ __device__ __forceinline__ uint32_t mbox_wait(const uint32_t* slot) {
   return __builtin_amdgcn_readfirstlane(v);
 }
 
-template <int G>
+template <int D, int G>
 constexpr int wg_waves() {
-  return decode_waves(G);
+  return decode_waves(D, G);
 }
 
 template <int D, int G>
 struct alignas(16) Lds {
-  static constexpr int NW = wg_waves<G>();
+  static constexpr int NW = wg_waves<D, G>();
   float acc[NW][G][D];
   float m[NW][G];
   float l[NW][G];
@@ -156,8 +158,8 @@ constexpr int waves_per_eu() {
 constexpr uint32_t max_wave_stages(int D, int G, int chunk) {
   uint32_t most = 0;
   for (uint32_t n = 0; n <= static_cast<uint32_t>(chunk); ++n)
-    for (uint32_t w = 0; w < static_cast<uint32_t>(decode_waves(G)); ++w) {
-      const uint32_t st = wave_keys(n, decode_step(D, G), decode_waves(G), w).n_st;
+    for (uint32_t w = 0; w < static_cast<uint32_t>(decode_waves(D, G)); ++w) {
+      const uint32_t st = wave_keys(n, decode_step(D, G), decode_waves(D, G), w).n_st;
       most = st > most ? st : most;
     }
   return most;
@@ -165,17 +167,20 @@ constexpr uint32_t max_wave_stages(int D, int G, int chunk) {
 
 template <int D, int G>
 struct Shape {
-  static constexpr int NW = decode_waves(G);                 // waves per workgroup
+  static constexpr int NW = decode_waves(D, G);                 // waves per workgroup
   static constexpr int LPK = decode_lpk(D, G);
   static constexpr int U = decode_unroll(D, G);
   static constexpr int NV4 = D / (4 * LPK);                  // float4 per lane per head vector
   static constexpr int NG = kWave / LPK;                     // key groups per wave
   static constexpr int SL = 4 * LPK;                         // floats per slice
-  static constexpr int STEP = NG * U;                        // keys per wave per stage
+  static constexpr bool MFMA = decode_mfma(D, G);            // the matrix-core form
+  static constexpr int STEP = decode_step(D, G);             // keys per wave per stage
   // stages per pass the wave's LDS score buffer holds
   static constexpr int NST = decode_stage_bound(D, G, SLOT_KV_CHUNK);
-  static constexpr int SCORES = NST * NG * G * U;            // score slots per wave
-  static_assert(STEP == decode_step(D, G), "one stage size");
+  // score slots per wave: per stage [key group][G][U] (vector form) or
+  // [lane group][G][4] (matrix form)
+  static constexpr int SCORES = MFMA ? NST * STEP * G : NST * NG * G * U;
+  static_assert(MFMA ? STEP % 16 == 0 : STEP == NG * U, "one stage size");
   static_assert(NV4 >= 1 && D % (4 * LPK) == 0, "whole float4 slices per lane");
   static_assert(SLOT_KV_CHUNK % NW == 0, "a chunk splits evenly over the waves");
   static_assert(max_wave_stages(D, G, SLOT_KV_CHUNK) <= static_cast<uint32_t>(NST),
@@ -226,38 +231,6 @@ __device__ __forceinline__ UnitPlan plan_unit(const AttnArgs& a, const UnitId& i
   return u;
 }
 
-template <int D, int G>
-struct Stage {
-  f4 x[Shape<D, G>::U][Shape<D, G>::NV4];
-};
-
-// Stage qi of a unit (n_st >= 1): K stage qi for qi < n_st, else V stage
-// qi - n_st.  Every call issues the same U*NV4 loads whatever the stage: a
-// key past the wave's range re-reads the wave's last key row (pass 1 masks
-// its score to -inf, so pass 2 gives it weight 0).  The count of loads in
-// flight therefore never depends on the data, and the compiler can leave one
-// stage in flight while the other is consumed.
-template <int D, int G>
-__device__ __forceinline__ void load_stage(const AttnParams& p, const UnitPlan& u, uint32_t gi,
-                                           uint32_t lo, Stage<D, G>& sg, uint32_t qi) {
-  using S = Shape<D, G>;
-  const bool is_v = qi >= u.n_st;
-  const uint32_t st = is_v ? qi - u.n_st : qi;
-  const float* base = (is_v ? p.v_cache : p.k_cache) + static_cast<uint64_t>(u.slot) * p.slot_stride +
-                      u.j * D + lo;
-  const uint32_t first = u.k_begin + st * S::STEP + gi;
-  const uint32_t last = u.k_begin + u.len - 1;
-#pragma unroll
-  for (int uu = 0; uu < S::U; ++uu) {
-    const uint32_t row = min(first + S::NG * uu, last);
-    const float* r = base + static_cast<uint64_t>(row) * p.kv_dim;
-#pragma unroll
-    for (int i = 0; i < S::NV4; ++i) sg.x[uu][i] = ld4_stream(r + i * S::SL);
-  }
-  // keep the loads ahead of the work on the other buffer
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 // The next unit's query heads (and its new key) are normalised and rotated
 // while the current unit streams, and staged in LDS in two parity buffers.
 // Vector v < G is query head j*G + v; v == G is the new key, present only
@@ -272,7 +245,7 @@ struct alignas(16) PrepLds {
 };
 template <int D, int G>
 struct PrepRaw {
-  static constexpr int NW = wg_waves<G>();
+  static constexpr int NW = wg_waves<D, G>();
   static constexpr int EPL = D / kWave;
   static constexpr int SLOTS = (G + 1 + NW - 1) / NW;
   float x[SLOTS][EPL];
@@ -413,6 +386,409 @@ __device__ __forceinline__ void prep_finish(const AttnArgs& a, const UnitId& id,
   }
 }
 
+// ---------------------------------------------------------------- per-unit compute
+// A unit's work for one wave, in two forms with one interface: `load` issues
+// stage qi (K stage qi < n_st, else V stage qi - n_st) into a register
+// stage; `begin` takes the unit's query heads (and new key) from LDS;
+// `score` turns a K stage into scores (log2 units) in the wave's LDS score
+// buffer and a running max; `finish_max` makes the wave's max per head;
+// `weights` may turn the stored scores into exp2(score - max) in place;
+// `accumulate` adds a V stage weighted by them; `add_new_key` adds the row's
+// new key (the unit's wave that owns it); `store` leaves the wave's (acc,
+// max, sum) per head in LDS for the workgroup's merge.
+//
+// Every `load` issues the same loads whatever the stage: a key past the
+// wave's range re-reads the wave's last key row (pass 1 masks its score to
+// -inf, so pass 2 gives it weight 0).  The count of loads in flight therefore
+// never depends on the data, and the compiler can leave one stage in flight
+// while the other is consumed.
+
+// Vector-ALU form.  LPK lanes own one key row, each holding 4 floats of
+// every 4*LPK-float slice; a stage holds U keys per key group of LPK lanes
+// (key k_begin + s*STEP + gi + NG*u).  A score is the key group's DPP sum;
+// stored scores become weights in a pass of their own between the passes,
+// once per (key, head) rather than in every lane of a key group.
+template <int D, int G>
+struct ValuCore {
+  using S = Shape<D, G>;
+  static constexpr int LPK = S::LPK, U = S::U, NV4 = S::NV4, NG = S::NG, SL = S::SL;
+  struct Stage {
+    f4 x[U][NV4];
+  };
+  uint32_t lane, gi, lo;  // lo: the lane's float offset inside a slice
+  f4 q[G][NV4];
+  float mx[G];     // running max of this lane's key group, per head
+  float s_new[G];  // the new key's scores
+  float m[G];      // wave max per head: all key groups (and the new key) share it
+  float l[G];
+  f4 acc[G][NV4];
+
+  __device__ __forceinline__ void init(uint32_t lane_) {
+    lane = lane_;
+    gi = lane / LPK;
+    lo = 4 * (lane % LPK);
+  }
+  __device__ __forceinline__ void load(const AttnParams& p, const UnitPlan& u, Stage& sg,
+                                       uint32_t qi) const {
+    const bool is_v = qi >= u.n_st;
+    const uint32_t st = is_v ? qi - u.n_st : qi;
+    const float* base = (is_v ? p.v_cache : p.k_cache) +
+                        static_cast<uint64_t>(u.slot) * p.slot_stride + u.j * D + lo;
+    const uint32_t first = u.k_begin + st * S::STEP + gi;
+    const uint32_t last = u.k_begin + u.len - 1;
+#pragma unroll
+    for (int uu = 0; uu < U; ++uu) {
+      const uint32_t row = min(first + NG * uu, last);
+      const float* r = base + static_cast<uint64_t>(row) * p.kv_dim;
+#pragma unroll
+      for (int i = 0; i < NV4; ++i) sg.x[uu][i] = ld4_stream(r + i * SL);
+    }
+    // keep the loads ahead of the work on the other buffer
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __device__ __forceinline__ void begin(const PrepLds<D, G>& prep, uint32_t par, bool new_key) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int i = 0; i < NV4; ++i) q[g][i] = ld4(&prep.q[par][g][i * SL + lo]);
+#pragma unroll
+    for (int g = 0; g < G; ++g) mx[g] = -INFINITY;
+    if (new_key) {  // wave 0 of the row's last chunk scores the new key
+      f4 kn[NV4];
+#pragma unroll
+      for (int i = 0; i < NV4; ++i) kn[i] = ld4(&prep.kn[par][i * SL + lo]);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float sdot = dot4(q[g][0], kn[0]);
+#pragma unroll
+        for (int i = 1; i < NV4; ++i) sdot += dot4(q[g][i], kn[i]);
+        s_new[g] = group_sum<LPK>(sdot);
+        mx[g] = s_new[g];
+      }
+    }
+  }
+  static constexpr int KT = 0;  // no LDS K tile
+  __device__ __forceinline__ void score(const Stage& sg, uint32_t st, const UnitPlan& u,
+                                        float* sc_w, float*) {
+    const bool tail = st >= u.n_full;
+    float sc[G * U];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int uu = 0; uu < U; ++uu) {
+        float d = dot4(q[g][0], sg.x[uu][0]);
+#pragma unroll
+        for (int i = 1; i < NV4; ++i) d += dot4(q[g][i], sg.x[uu][i]);
+        d = group_sum<LPK>(d);
+        if (tail && st * S::STEP + gi + NG * uu >= u.len) d = -INFINITY;
+        sc[g * U + uu] = d;
+        mx[g] = max_nc(mx[g], d);
+      }
+    }
+    if (lane % LPK == 0) {
+      float* dst = sc_w + (st * NG + gi) * (G * U);
+      if constexpr ((G * U) % 4 == 0) {
+#pragma unroll
+        for (int e = 0; e < G * U; e += 4) st4(dst + e, f4{sc[e], sc[e + 1], sc[e + 2], sc[e + 3]});
+      } else {
+#pragma unroll
+        for (int e = 0; e < G * U; ++e) dst[e] = sc[e];
+      }
+    }
+  }
+  __device__ __forceinline__ void finish_max() {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float v = mx[g];
+#pragma unroll
+      for (int off = LPK; off < kWave; off <<= 1) v = max_nc(v, __shfl_xor(v, off));
+      m[g] = v;
+      l[g] = 0.f;  // pass 2's state starts here, so it holds no registers in pass 1
+#pragma unroll
+      for (int i = 0; i < NV4; ++i) acc[g][i] = f4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  // Each stored score becomes its weight exp2(s - max), the wave's lanes
+  // taking four entries at a time.  An entry's head is fixed by its place in a
+  // stage's [key group][G][U] block, and a block's G*U entries divide 256, so
+  // each lane's four heads stay the same from one step of the loop to the next.
+  __device__ __forceinline__ void weights(float* sc_w, uint32_t n_st) const {
+    constexpr uint32_t GU = G * U;
+    static_assert(256 % GU == 0 && (NG * GU) % 4 == 0, "weight pass lane layout");
+    float mc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t g_c = ((4 * lane + c) % GU) / U;
+      mc[c] = m[0];
+#pragma unroll
+      for (int g = 1; g < G; ++g) mc[c] = g_c == static_cast<uint32_t>(g) ? m[g] : mc[c];
+    }
+    const uint32_t n_ent = n_st * NG * GU;  // a multiple of 4
+    for (uint32_t e = 4 * lane; e < n_ent; e += 4 * kWave) {
+      f4 v = ld4(sc_w + e);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[c] = fast_exp2(v[c] - mc[c]);  // masked keys: exp2(-inf) = 0
+      st4(sc_w + e, v);
+    }
+  }
+  __device__ __forceinline__ void accumulate(const Stage& sg, uint32_t st, const float* sc_w) {
+    const float* src = sc_w + (st * NG + gi) * (G * U);
+    float sc[G * U];
+    if constexpr ((G * U) % 4 == 0) {
+#pragma unroll
+      for (int e = 0; e < G * U; e += 4) {
+        const f4 v = ld4(src + e);
+        sc[e] = v[0];
+        sc[e + 1] = v[1];
+        sc[e + 2] = v[2];
+        sc[e + 3] = v[3];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < G * U; ++e) sc[e] = src[e];
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int uu = 0; uu < U; ++uu) {
+        const float pu = sc[g * U + uu];  // exp2(score - max), from the weight pass
+        l[g] += pu;
+#pragma unroll
+        for (int i = 0; i < NV4; ++i) acc[g][i] += pu * sg.x[uu][i];
+      }
+    }
+  }
+  __device__ __forceinline__ void add_new_key(const PrepLds<D, G>& prep, uint32_t par) {
+    if (gi != 0) return;  // one key group adds it (the groups are summed next)
+    f4 vn[NV4];
+#pragma unroll
+    for (int i = 0; i < NV4; ++i) vn[i] = ld4(&prep.vn[par][i * SL + lo]);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float pn = fast_exp2(s_new[g] - m[g]);
+      l[g] += pn;
+#pragma unroll
+      for (int i = 0; i < NV4; ++i) acc[g][i] += pn * vn[i];
+    }
+  }
+  __device__ __forceinline__ void store(Lds<D, G>& sh, uint32_t w) {
+    // sum the wave's key groups (they share m)
+#pragma unroll
+    for (int off = LPK; off < kWave; off <<= 1) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        l[g] += __shfl_xor(l[g], off);
+#pragma unroll
+        for (int i = 0; i < NV4; ++i) {
+          f4 other;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) other[c] = __shfl_xor(acc[g][i][c], off);
+          acc[g][i] += other;
+        }
+      }
+    }
+    if (gi == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+#pragma unroll
+        for (int i = 0; i < NV4; ++i) st4(&sh.acc[w][g][i * SL + lo], acc[g][i]);
+      }
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        sh.m[w][g] = m[g];
+        sh.l[w][g] = l[g];
+      }
+    }
+  }
+};
+
+// Matrix-core form, on v_mfma_f32_16x16x4f32 with the kv head's G query
+// heads as the 16 columns of the tile (columns G..15 hold zero queries and
+// are dropped).  A stage is TPS tiles of 16 keys (tile t: keys 16t ..
+// 16t + 15 of the stage).  Lane l works on column c = l % 16 and lane group
+// g = l / 16:
+//   S^T = K Q^T, summed over head_dim in MFMA steps (v, e), v < D/16, e < 4:
+//     A = K[key c][d], B = Q[head c][d], d = 16v + 4g + e;
+//     result register r: S[key 4g + r][head c].
+//     Loading A straight from memory would make each load instruction read
+//     64 bytes from each of 16 key rows, which streams about 10% slower than
+//     the V pattern below; so K rows are loaded as V rows are (each lane group
+//     reading 256 contiguous bytes of one row) and pass through a per-wave LDS
+//     tile, 16 rows of D floats whose 16-byte segments are XOR-swizzled by row
+//     (segment s of row r at s ^ (r % 16)), so that both the writes and the A
+//     reads of sixteen lanes fall in distinct banks.
+//   O^T += V^T P^T, MFMA steps (m, u), m < 4, u < D/16:
+//     A = V[key 4g + m][d(c, u)], B = P[key 4g + m][head c] = the weight of
+//     score register m, so the scores never move between lanes;
+//     d(x, u) = 4x + 64(u/4) + u%4 (a V load of the sixteen lanes of a lane
+//     group reads 256 contiguous bytes of one row);
+//     result register r of tile u: O[head c][d(4g + r, u)].
+// A lane keeps the scores of its own column, so the weights are taken in
+// pass 2 (four per lane per stage) and the lane's maximum and sum need only
+// the two exchanges across its lane groups.
+template <int D, int G>
+struct MfmaCore {
+  using S = Shape<D, G>;
+  static constexpr int TPS = S::STEP / 16;  // tiles per stage
+  static constexpr int NK = D / 16;  // float4 loads per lane per tile (K, and V)
+  static constexpr int TD = D / 16;  // output tiles of 16 head_dim values
+  static constexpr int NV = TD / 4;  // V float4 per lane per key of its lane group
+  static_assert(TPS * 16 == S::STEP && NK == 4 * NV && NV >= 1, "16-key tiles, head_dim >= 64");
+  static constexpr int KT = 16 * D;  // floats of the wave's LDS K tile
+  struct Stage {
+    // tile t, K or V: x[t][m*NV + i] = row 16t + 4g + m, floats 4c + 64i ..
+    f4 x[TPS][NK];
+  };
+  // float offset of 16-byte segment s of row r in the LDS K tile
+  static __device__ __forceinline__ uint32_t kt_at(uint32_t r, uint32_t s) {
+    return r * D + 4 * (s ^ (r % 16));
+  }
+  uint32_t lane, g, c;
+  bool col;  // c < G: a real query head
+  float qv[D / 4];
+  float mx, s_new, m, l;  // this lane's head c
+  f4 o[TD];
+
+  __device__ __forceinline__ void init(uint32_t lane_) {
+    lane = lane_;
+    g = lane / 16;
+    c = lane % 16;
+    col = c < G;
+  }
+  __device__ __forceinline__ void load(const AttnParams& p, const UnitPlan& u, Stage& sg,
+                                       uint32_t qi) const {
+    const bool is_v = qi >= u.n_st;
+    const uint32_t st = is_v ? qi - u.n_st : qi;
+    const uint32_t last = u.k_begin + u.len - 1;
+    const float* base = (is_v ? p.v_cache : p.k_cache) +
+                        static_cast<uint64_t>(u.slot) * p.slot_stride + u.j * D;
+#pragma unroll
+    for (int t = 0; t < TPS; ++t) {
+      const uint32_t kb = u.k_begin + st * S::STEP + 16 * t;
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm) {
+        const float* r =
+            base + static_cast<uint64_t>(min(kb + 4 * g + mm, last)) * p.kv_dim + 4 * c;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) sg.x[t][mm * NV + i] = ld4_stream(r + 64 * i);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __device__ __forceinline__ void begin(const PrepLds<D, G>& prep, uint32_t par, bool new_key) {
+    const float* qh = &prep.q[par][col ? c : 0][4 * g];
+#pragma unroll
+    for (int v = 0; v < NK; ++v) {
+      const f4 x = ld4(qh + 16 * v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qv[4 * v + e] = col ? x[e] : 0.f;
+    }
+    mx = -INFINITY;
+    if (new_key) {  // wave 0 of the row's last chunk scores the new key
+      float sdot = 0.f;
+#pragma unroll
+      for (int v = 0; v < NK; ++v) {
+        const f4 k = ld4(&prep.kn[par][16 * v + 4 * g]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sdot += qv[4 * v + e] * k[e];
+      }
+      sdot += __shfl_xor(sdot, 16);
+      sdot += __shfl_xor(sdot, 32);
+      s_new = sdot;
+      mx = sdot;
+    }
+  }
+  __device__ __forceinline__ void score(const Stage& sg, uint32_t st, const UnitPlan& u,
+                                        float* sc_w, float* kt) {
+#pragma unroll
+    for (int t = 0; t < TPS; ++t) {
+      // the tile's K rows into the LDS tile, then back as the A operand
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm)
+#pragma unroll
+        for (int i = 0; i < NV; ++i) st4(kt + kt_at(4 * g + mm, c + 16 * i), sg.x[t][mm * NV + i]);
+      f4 s = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < NK; ++v) {
+        const f4 a = ld4(kt + kt_at(c, 4 * v + g));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], qv[4 * v + e], s, 0, 0, 0);
+      }
+      if (st >= u.n_full) {  // the wave's last partial stage, or a padding one
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (st * S::STEP + 16 * t + 4 * g + r >= u.len) s[r] = -INFINITY;
+      }
+      mx = max_nc(mx, max_nc(max_nc(s[0], s[1]), max_nc(s[2], s[3])));
+      if (col) st4(sc_w + (((st * TPS + t) * 4 + g) * G + c) * 4, s);
+    }
+  }
+  __device__ __forceinline__ void finish_max() {
+    float v = mx;
+    v = max_nc(v, __shfl_xor(v, 16));
+    v = max_nc(v, __shfl_xor(v, 32));
+    m = v;
+    l = 0.f;
+#pragma unroll
+    for (int t = 0; t < TD; ++t) o[t] = f4{0.f, 0.f, 0.f, 0.f};
+  }
+  __device__ __forceinline__ void weights(float*, uint32_t) const {}  // taken in accumulate
+  __device__ __forceinline__ void accumulate(const Stage& sg, uint32_t st, const float* sc_w) {
+#pragma unroll
+    for (int t = 0; t < TPS; ++t) {
+      const f4 sv = ld4(sc_w + (((st * TPS + t) * 4 + g) * G + (col ? c : 0)) * 4);
+      float pr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pr[r] = col ? fast_exp2(sv[r] - m) : 0.f;  // masked keys: exp2(-inf) = 0
+        l += pr[r];
+      }
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm)
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            o[4 * i + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(sg.x[t][mm * NV + i][e], pr[mm],
+                                                                 o[4 * i + e], 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void add_new_key(const PrepLds<D, G>& prep, uint32_t par) {
+    if (!col) return;
+    const float pn = fast_exp2(s_new - m);
+    if (g == 0) l += pn;  // once per head (the lane groups are summed next)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const f4 vn = ld4(&prep.vn[par][16 * g + 4 * r + 64 * i]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[4 * i + e][r] += pn * vn[e];
+      }
+  }
+  __device__ __forceinline__ void store(Lds<D, G>& sh, uint32_t w) {
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (col) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+          st4(&sh.acc[w][c][16 * g + 4 * r + 64 * i],
+              f4{o[4 * i][r], o[4 * i + 1][r], o[4 * i + 2][r], o[4 * i + 3][r]});
+      if (g == 0) {
+        sh.m[w][c] = m;
+        sh.l[w][c] = l;
+      }
+    }
+  }
+};
+
+template <int D, int G>
+using DecodeCore = typename std::conditional<Shape<D, G>::MFMA, MfmaCore<D, G>, ValuCore<D, G>>::type;
+
 template <int D, int G>
 __device__ __forceinline__ void merge_row(const AttnParams& p, uint32_t b, uint32_t j,
                                           uint32_t n_chunks, uint32_t tid, uint32_t n_threads);
@@ -430,13 +806,14 @@ __device__ __forceinline__ void merge_row(const AttnParams& p, uint32_t b, uint3
 // leaves one unnormalised partial per chunk, merged by the row's last
 // workgroup.
 template <int D, int G>
-__global__ void __launch_bounds__(kWave * wg_waves<G>())
+__global__ void __launch_bounds__((kWave * wg_waves<D, G>()))
     __attribute__((amdgpu_waves_per_eu(waves_per_eu<D, G>()))) decode_attn_kernel(const AttnArgs a) {
   using S = Shape<D, G>;
+  using Core = DecodeCore<D, G>;
   constexpr int NW = S::NW, kThreads = kWave * NW;
-  constexpr int LPK = S::LPK, U = S::U, NV4 = S::NV4, NG = S::NG, SL = S::SL, STEP = S::STEP;
   __shared__ Lds<D, G> sh;
   __shared__ __attribute__((aligned(16))) float sc_lds[NW][S::SCORES];
+  __shared__ __attribute__((aligned(16))) float kt_lds[NW][Core::KT > 0 ? Core::KT : 1];
   __shared__ uint32_t mbox[2];  // next unit, by unit parity; kNoUnit until posted
   __shared__ PrepLds<D, G> prep;
   if (a.magic != kArgsMagic) return;  // argument block not delivered whole
@@ -444,9 +821,9 @@ __global__ void __launch_bounds__(kWave * wg_waves<G>())
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid % kWave;
   const uint32_t w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
-  const uint32_t gi = lane / LPK;
-  const uint32_t lo = 4 * (lane % LPK);  // lane's float offset inside a slice
   const uint32_t n_blocks = gridDim.x;
+  Core cc;
+  cc.init(lane);
 
   if (tid == 0) {
     mbox[0] = kNoUnit;
@@ -454,8 +831,8 @@ __global__ void __launch_bounds__(kWave * wg_waves<G>())
   }
   const UnitId first = locate_unit(a, blockIdx.x);  // blocks <= n_units
   UnitPlan u = plan_unit<D, G>(a, first, w);
-  Stage<D, G> A, B;
-  if (u.n_st > 0) load_stage<D, G>(p, u, gi, lo, A, 0);  // A always holds the next stage
+  typename Core::Stage A, B;
+  if (u.n_st > 0) cc.load(p, u, A, 0);  // A always holds the next stage
   const PrepConst<D> pconst = prep_const<D>(p, lane);
   PrepRaw<D, G> praw;
   prep_issue<D, G>(a, first, w, lane, praw);
@@ -502,214 +879,56 @@ __global__ void __launch_bounds__(kWave * wg_waves<G>())
     };
 
     // ---- prologue: queries and new key from LDS ------------------------------
-    f4 q[G][NV4];
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int i = 0; i < NV4; ++i) q[g][i] = ld4(&prep.q[par][g][i * SL + lo]);
-    float mx[G];  // running max of this lane's key group, per head
-    float s_new[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) mx[g] = -INFINITY;
-    if (u.new_key) {  // wave 0 of the row's last chunk scores the new key
-      f4 kn[NV4];
-#pragma unroll
-      for (int i = 0; i < NV4; ++i) kn[i] = ld4(&prep.kn[par][i * SL + lo]);
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float sdot = dot4(q[g][0], kn[0]);
-#pragma unroll
-        for (int i = 1; i < NV4; ++i) sdot += dot4(q[g][i], kn[i]);
-        s_new[g] = group_sum<LPK>(sdot);
-        mx[g] = s_new[g];
-      }
-    }
+    cc.begin(prep, par, u.new_key);
 
     // ---- two passes over this wave's history keys ------------------------
     // Pass 1 streams the K rows, keeps each key's scores (log2 units) in LDS
     // and the running max per head; pass 2 streams the V rows and
     // accumulates exp2(score - max) * v against the wave's final max, so no
     // accumulator is ever rescaled.  Both passes form one double-buffered
-    // sequence of 2 * n_st stages; stage s of a pass holds key
-    // k_begin + s*STEP + gi + NG*u for u < U.
-    float* sc_w = &sc_lds[w][0];  // [stage][key group][G][U]
-    auto score = [&](const Stage<D, G>& sg, uint32_t st) {
-      const bool tail = st >= u.n_full;
-      float sc[G * U];
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-#pragma unroll
-        for (int uu = 0; uu < U; ++uu) {
-          float d = dot4(q[g][0], sg.x[uu][0]);
-#pragma unroll
-          for (int i = 1; i < NV4; ++i) d += dot4(q[g][i], sg.x[uu][i]);
-          d = group_sum<LPK>(d);
-          if (tail && st * STEP + gi + NG * uu >= u.len) d = -INFINITY;
-          sc[g * U + uu] = d;
-          mx[g] = max_nc(mx[g], d);
-        }
-      }
-      if (lane % LPK == 0) {
-        float* dst = sc_w + (st * NG + gi) * (G * U);
-        if constexpr ((G * U) % 4 == 0) {
-#pragma unroll
-          for (int e = 0; e < G * U; e += 4)
-            st4(dst + e, f4{sc[e], sc[e + 1], sc[e + 2], sc[e + 3]});
-        } else {
-#pragma unroll
-          for (int e = 0; e < G * U; ++e) dst[e] = sc[e];
-        }
-      }
-    };
-    float m[G];  // wave max per head: all key groups (and the new key) share it
-    float l[G];
-    f4 acc[G][NV4];
-    auto finish_max = [&]() {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float v = mx[g];
-#pragma unroll
-        for (int off = LPK; off < kWave; off <<= 1) v = max_nc(v, __shfl_xor(v, off));
-        m[g] = v;
-        l[g] = 0.f;  // pass 2's state starts here, so it holds no registers in pass 1
-#pragma unroll
-        for (int i = 0; i < NV4; ++i) acc[g][i] = f4{0.f, 0.f, 0.f, 0.f};
-      }
-    };
-    // Between the passes each stored score becomes its weight exp2(s - max),
-    // once per (key, head) and in place, the wave's lanes taking four entries
-    // at a time: pass 2 then only multiplies (its lanes would otherwise each
-    // take the exponential of every score of their key group).  An entry's
-    // head is fixed by its place in a stage's [key group][G][U] block, and a
-    // block's G*U entries divide 256, so each lane's four heads stay the same
-    // from one step of the loop to the next.
-    auto exp_pass = [&](uint32_t n_st_) {
-      constexpr uint32_t GU = G * U;
-      float mc[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t g_c = ((4 * lane + c) % GU) / U;
-        mc[c] = m[0];
-#pragma unroll
-        for (int g = 1; g < G; ++g) mc[c] = g_c == static_cast<uint32_t>(g) ? m[g] : mc[c];
-      }
-      const uint32_t n_ent = n_st_ * NG * GU;  // a multiple of 4: NG * GU >= 4
-      for (uint32_t e = 4 * lane; e < n_ent; e += 4 * kWave) {
-        f4 v = ld4(sc_w + e);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) v[c] = fast_exp2(v[c] - mc[c]);  // masked keys: exp2(-inf) = 0
-        st4(sc_w + e, v);
-      }
-    };
-    static_assert(256 % (G * U) == 0 && (NG * G * U) % 4 == 0, "exp pass lane layout");
-    auto accumulate = [&](const Stage<D, G>& sg, uint32_t st) {
-      const float* src = sc_w + (st * NG + gi) * (G * U);
-      float sc[G * U];
-      if constexpr ((G * U) % 4 == 0) {
-#pragma unroll
-        for (int e = 0; e < G * U; e += 4) {
-          const f4 v = ld4(src + e);
-          sc[e] = v[0];
-          sc[e + 1] = v[1];
-          sc[e + 2] = v[2];
-          sc[e + 3] = v[3];
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < G * U; ++e) sc[e] = src[e];
-      }
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-#pragma unroll
-        for (int uu = 0; uu < U; ++uu) {
-          const float pu = sc[g * U + uu];  // exp2(score - max), from the exp pass
-          l[g] += pu;
-#pragma unroll
-          for (int i = 0; i < NV4; ++i) acc[g][i] += pu * sg.x[uu][i];
-        }
-      }
-    };
-    // Stage loads run one ahead of use in two buffers: K stages, then V
-    // stages; stage index qi < n_st is K stage qi, qi >= n_st is V stage
-    // qi - n_st.  n_st is even, so each pass starts in A.  The last V stage
-    // is consumed with nothing behind it; the next unit's first K stage goes
-    // out once this unit's results are stored.
+    // sequence of 2 * n_st stages.  Stage loads run one ahead of use in two
+    // buffers: K stages, then V stages; stage index qi < n_st is K stage qi,
+    // qi >= n_st is V stage qi - n_st.  n_st is even, so each pass starts in
+    // A.  The last V stage is consumed with nothing behind it; the next unit's
+    // first K stage goes out once this unit's results are stored.
+    float* sc_w = &sc_lds[w][0];
+    float* kt_w = &kt_lds[w][0];
     const uint32_t n_st = u.n_st;
     if (n_st > 0) {  // wave-uniform
       // pass 1
-      load_stage<D, G>(p, u, gi, lo, B, 1);
-      score(A, 0);
-      load_stage<D, G>(p, u, gi, lo, A, 2);  // V stage 0 when n_st == 2
-      score(B, 1);
+      cc.load(p, u, B, 1);
+      cc.score(A, 0, u, sc_w, kt_w);
+      cc.load(p, u, A, 2);  // V stage 0 when n_st == 2
+      cc.score(B, 1, u, sc_w, kt_w);
       for (uint32_t st = 2; st < n_st; st += 2) {
-        load_stage<D, G>(p, u, gi, lo, B, st + 1);
-        score(A, st);
-        load_stage<D, G>(p, u, gi, lo, A, st + 2);  // the last trip loads V stage 0
-        score(B, st + 1);
+        cc.load(p, u, B, st + 1);
+        cc.score(A, st, u, sc_w, kt_w);
+        cc.load(p, u, A, st + 2);  // the last trip loads V stage 0
+        cc.score(B, st + 1, u, sc_w, kt_w);
       }
-      finish_max();
+      cc.finish_max();
       ask_next();
-      exp_pass(n_st);
+      cc.weights(sc_w, n_st);
       uint32_t st = 0;
       for (; st + 2 < n_st; st += 2) {  // pass 2 while two more stages follow
-        load_stage<D, G>(p, u, gi, lo, B, n_st + st + 1);
-        accumulate(A, st);
-        load_stage<D, G>(p, u, gi, lo, A, n_st + st + 2);
-        accumulate(B, st + 1);
+        cc.load(p, u, B, n_st + st + 1);
+        cc.accumulate(A, st, sc_w);
+        cc.load(p, u, A, n_st + st + 2);
+        cc.accumulate(B, st + 1, sc_w);
       }
-      load_stage<D, G>(p, u, gi, lo, B, n_st + st + 1);  // the last stage
-      accumulate(A, st);
+      cc.load(p, u, B, n_st + st + 1);  // the last stage
+      cc.accumulate(A, st, sc_w);
       take_next();
-      accumulate(B, st + 1);
+      cc.accumulate(B, st + 1, sc_w);
     } else {
       ask_next();
       take_next();
-      finish_max();
+      cc.finish_max();
     }
-    if (u.new_key && gi == 0) {
-      f4 vn[NV4];
-#pragma unroll
-      for (int i = 0; i < NV4; ++i) vn[i] = ld4(&prep.vn[par][i * SL + lo]);
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float pn = fast_exp2(s_new[g] - m[g]);
-        l[g] += pn;
-#pragma unroll
-        for (int i = 0; i < NV4; ++i) acc[g][i] += pn * vn[i];
-      }
-    }
+    if (u.new_key) cc.add_new_key(prep, par);
 
-    // ---- sum the wave's key groups (they share m) ------------------------
-#pragma unroll
-    for (int off = LPK; off < kWave; off <<= 1) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        l[g] += __shfl_xor(l[g], off);
-#pragma unroll
-        for (int i = 0; i < NV4; ++i) {
-          f4 other;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) other[c] = __shfl_xor(acc[g][i][c], off);
-          acc[g][i] += other;
-        }
-      }
-    }
-
-    // ---- merge the NW waves through LDS -----------------------------------
-    if (gi == 0) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-#pragma unroll
-        for (int i = 0; i < NV4; ++i) st4(&sh.acc[w][g][i * SL + lo], acc[g][i]);
-      }
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        sh.m[w][g] = m[g];
-        sh.l[w][g] = l[g];
-      }
-    }
+    // ---- the wave's (acc, max, sum) per head into LDS; merge the NW waves ----
+    cc.store(sh, w);
     // Publication of the previous unit's partial.  Its stores are agent-scope
     // atomic stores, written through to the level all XCDs share, and were
     // issued a whole unit ago; every wave waits for them to be acknowledged
@@ -768,7 +987,7 @@ __global__ void __launch_bounds__(kWave * wg_waves<G>())
     auto prefetch_next = [&]() {
       if (has_next) {
         const UnitPlan nu = plan_unit<D, G>(a, un, w);
-        if (nu.n_st > 0) load_stage<D, G>(p, nu, gi, lo, A, 0);
+        if (nu.n_st > 0) cc.load(p, nu, A, 0);
       }
     };
     prefetch_next();
@@ -841,7 +1060,7 @@ __device__ __forceinline__ void merge_row(const AttnParams& p, uint32_t b, uint3
 
 template <int D, int G>
 hipError_t launch_shape(const AttnArgs& a, uint32_t blocks, hipStream_t s, hipEvent_t mark) {
-  hipLaunchKernelGGL((decode_attn_kernel<D, G>), dim3(blocks), dim3(kWave * wg_waves<G>()), 0, s, a);
+  hipLaunchKernelGGL((decode_attn_kernel<D, G>), dim3(blocks), dim3(kWave * wg_waves<D, G>()), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && mark) e = hipEventRecord(mark, s);
   return e;
@@ -855,7 +1074,7 @@ uint32_t resident_shape() {
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_attn_kernel<D, G>,
-                                                     kWave * wg_waves<G>(), 0) != hipSuccess)
+                                                     kWave * wg_waves<D, G>(), 0) != hipSuccess)
       return 0;
     cached = static_cast<uint32_t>(per_cu > 0 ? per_cu : 1) * static_cast<uint32_t>(cus);
   }

@@ -34,7 +34,7 @@ int main() {
   for (int chunk = 256; chunk <= 2048; chunk += 64)
     for (int D : Ds)
       for (int G : Gs) {
-        const uint32_t nw = decode_waves(G), step = decode_step(D, G);
+        const uint32_t nw = decode_waves(D, G), step = decode_step(D, G);
         const uint32_t bound = decode_stage_bound(D, G, chunk);
         if (chunk % nw) continue;  // the kernel requires an even split (asserted there)
         for (uint32_t n = 0; n <= uint32_t(chunk); ++n) {
@@ -74,10 +74,11 @@ int main() {
 
 # build settings of the shape constants: the defaults, then the knobs the
 # kernel exposes (waves per workgroup, lanes per key row, keys per group and
-# stage)
+# stage, which shapes run on the matrix cores)
 SETTINGS = [[], ["-DSLOT_KV_WG_WAVES=2"], ["-DSLOT_KV_WG_WAVES=4"], ["-DSLOT_KV_WG_WAVES=16"],
             ["-DSLOT_KV_LPK=8"], ["-DSLOT_KV_LPK=4"], ["-DSLOT_KV_UNROLL=2"],
-            ["-DSLOT_KV_UNROLL=1"]]
+            ["-DSLOT_KV_UNROLL=1"], ["-DSLOT_KV_MFMA_SHAPES=0"],
+            ["-DSLOT_KV_MFMA_SHAPES=0", "-DSLOT_KV_WG_WAVES=4"], ["-DSLOT_KV_MFMA_SHAPES=0xfff"]]
 
 
 @pytest.mark.parametrize("flags", SETTINGS, ids=lambda f: " ".join(f) or "default")
@@ -93,9 +94,9 @@ def test_wave_split_tiles_chunk_within_score_buffer(flags, tmp_path):
 
 
 def test_bound_is_tight_where_it_was_once_too_small():
-    # A 768-key chunk at head_dim 64, G = 1 splits into 24 stages of 32 keys
-    # over 8 waves: 3 each, padded to 4.  The unpadded bound (3) was once too
-    # small; the bound must be 4 there.
+    # In the vector-ALU form, a 768-key chunk at head_dim 64, G = 1 splits
+    # into 24 stages of 32 keys over 8 waves: 3 each, padded to 4.  The
+    # unpadded bound (3) was once too small; the bound must be 4 there.
     drv = r"""
 #include <cstdio>
 #include "slot_kv_internal.h"
@@ -108,8 +109,8 @@ int main() {
     with tempfile.TemporaryDirectory() as d:
         src, exe = os.path.join(d, "t.cpp"), os.path.join(d, "t")
         open(src, "w").write(drv)
-        subprocess.run(["g++", "-std=c++17", "-I", INCLUDE, "-I", CSRC, src, "-o", exe],
-                       check=True, capture_output=True)
+        subprocess.run(["g++", "-std=c++17", "-DSLOT_KV_MFMA_SHAPES=0", "-I", INCLUDE, "-I", CSRC,
+                        src, "-o", exe], check=True, capture_output=True)
         step, bound, n_st = map(int, subprocess.run([exe], capture_output=True, text=True,
                                                     check=True).stdout.split())
     assert (step, bound, n_st) == (32, 4, 4)
