@@ -378,7 +378,17 @@ struct SplitLds {
   f4 acc[kAttnWaves - 1][D / 16][kWave];
   float m[kAttnWaves - 1][kWave];
   float l[kAttnWaves - 1][kWave];
+  // per wave: a K block on its way to the A layout (head_dim up to 128)
+  float kt[kAttnWaves][D <= 128 ? 16 * D : 4];
 };
+
+// Float offset of 16-byte segment s of row r in a wave's LDS K block: the
+// segments are XOR-swizzled by row, so that the sixteen lanes of a lane
+// group, writing one row each or reading sixteen rows, hit distinct banks.
+template <int D>
+__device__ __forceinline__ uint32_t kt_at(uint32_t r, uint32_t s) {
+  return r * D + 4 * (s ^ (r % 16));
+}
 
 template <int D, int G>
 __global__ void __launch_bounds__(kWave * kAttnWaves)
@@ -436,27 +446,42 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_eu<D>()))) split_attn_kernel(
   const uint64_t slot_base = a.s.slot[sq] * p.slot_stride;
   const float* kbase = p.k_cache + slot_base + j * D;
   const float* vbase = p.v_cache + slot_base + j * D;
-  // Block b of the chunk: K row k0 + 16b + c, V rows k0 + 16b + 4g + m.
+  // Block b of the chunk: keys k0 + 16b .. k0 + 16b + 15.  Lane (g, c) loads
+  // V rows k0 + 16b + 4g + m, floats 4c + 64x .. 4c + 64x + 3, so that the
+  // sixteen lanes of a lane group read 256 contiguous bytes of one row.  K
+  // rows are loaded the same way and go through the wave's LDS block into
+  // the A layout (loading the operand in that layout would read 64 bytes of
+  // each of sixteen rows per instruction, which streams measurably slower);
+  // at head_dim 256 the registers leave no room for that, and K row
+  // k0 + 16b + c is loaded in the A layout (floats 16v + 4g .. for v < D/16,
+  // held as kr[v / NV][v % NV]).
   // Loads are issued unconditionally, so that the number in flight is known
   // where a block is consumed: rows past the chunk (a partial last block, or
   // the block after the last) re-read its last key, which the mask drops.
   // (an inactive wave issues no load: its loop runs no block, and its
   // prologue loads are skipped below)
-  auto load_k = [&](f4 (&kr)[NK], uint32_t b) {
-    const uint32_t kb = k0 + 16 * b;
-    const float* kp = kbase + static_cast<size_t>(min(kb + c, k1 - 1)) * p.kv_dim + 4 * g;
-#pragma unroll
-    for (int v = 0; v < NK; ++v) kr[v] = *reinterpret_cast<const f4*>(kp + 16 * v);
-  };
-  auto load_v = [&](f4 (&vr)[4][NV], uint32_t b) {
+  auto load_rows = [&](const float* base, f4 (&r)[4][NV], uint32_t b) {
     const uint32_t kb = k0 + 16 * b;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const float* vp = vbase + static_cast<size_t>(min(kb + 4 * g + m, k1 - 1)) * p.kv_dim + TD * c;
+      const float* rp = base + static_cast<size_t>(min(kb + 4 * g + m, k1 - 1)) * p.kv_dim + 4 * c;
 #pragma unroll
-      for (int x = 0; x < NV; ++x) vr[m][x] = *reinterpret_cast<const f4*>(vp + 4 * x);
+      for (int x = 0; x < NV; ++x) r[m][x] = *reinterpret_cast<const f4*>(rp + 64 * x);
     }
   };
+  constexpr bool kKTile = D <= 128;
+  auto load_k = [&](f4 (&kr)[4][NV], uint32_t b) {
+    if constexpr (kKTile) {
+      load_rows(kbase, kr, b);
+    } else {
+      const uint32_t kb = k0 + 16 * b;
+      const float* kp = kbase + static_cast<size_t>(min(kb + c, k1 - 1)) * p.kv_dim + 4 * g;
+#pragma unroll
+      for (int v = 0; v < NK; ++v) kr[v / NV][v % NV] = *reinterpret_cast<const f4*>(kp + 16 * v);
+    }
+  };
+  auto load_v = [&](f4 (&vr)[4][NV], uint32_t b) { load_rows(vbase, vr, b); };
+  float* kt = sh.kt[w];
 
   float m_run = -INFINITY, l_run = 0.f;
   f4 o[TD];
@@ -465,14 +490,26 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_eu<D>()))) split_attn_kernel(
   // scores of block b (from its K rows), then its softmax weights
   f4 pr;
   float corr;
-  auto scores = [&](const f4 (&kr)[NK], uint32_t b) {
+  auto scores = [&](const f4 (&kr)[4][NV], uint32_t b) {
     const uint32_t kb = k0 + 16 * b;
+    // the block's K rows into the LDS block (row 4g + m, segment c + 16x),
+    // then back as the A operand: lane (g, c) takes row c, d = 16v + 4g + e
+    if constexpr (kKTile) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int x = 0; x < NV; ++x)
+          *reinterpret_cast<f4*>(kt + kt_at<D>(4 * g + m, c + 16 * x)) = kr[m][x];
+    }
     f4 s = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int v = 0; v < NK; ++v)
+    for (int v = 0; v < NK; ++v) {
+      const f4 ka_v = kKTile ? *reinterpret_cast<const f4*>(kt + kt_at<D>(c, 4 * v + g))
+                             : kr[v / NV][v % NV];
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        s = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[v][e], qv[4 * v + e], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_16x16x4f32(ka_v[e], qv[4 * v + e], s, 0, 0, 0);
+    }
     // key kb + 4g + r counts iff it is in the chunk and not after the row
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -508,7 +545,7 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_eu<D>()))) split_attn_kernel(
   // rows are reloaded (for the block two ahead) as soon as its scores are
   // taken and its V rows as soon as they are accumulated, so about three
   // half-blocks are in flight while a block is multiplied.
-  f4 ka[NK], va[4][NV], kb_[NK], vb[4][NV];
+  f4 ka[4][NV], va[4][NV], kb_[4][NV], vb[4][NV];
   if (active) {
     load_k(ka, 0);
     load_v(va, 0);
@@ -567,12 +604,13 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_eu<D>()))) split_attn_kernel(
 #pragma unroll
     for (int u = 0; u < TD; ++u) o[u] += sh.acc[v][u][lane] * sv;
   }
-  float* acc = p.part + (static_cast<size_t>(item) * 16 + c) * D + DQ * g;
+  // register r of output tile u holds d = 16g + 4r + 64(u/4) + u%4 of row c
+  float* acc = p.part + (static_cast<size_t>(item) * 16 + c) * D + 16 * g;
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int u = 0; u < TD; u += 4)
-      *reinterpret_cast<f4*>(acc + TD * r + u) = f4{o[u][r], o[u + 1][r], o[u + 2][r], o[u + 3][r]};
+      *reinterpret_cast<f4*>(acc + 4 * r + 16 * u) = f4{o[u][r], o[u + 1][r], o[u + 2][r], o[u + 3][r]};
   if (g == 0) {
     float* ml = p.part + static_cast<size_t>(p.n_items) * 16 * D + (static_cast<size_t>(item) * 16 + c) * 2;
     ml[0] = mx;
