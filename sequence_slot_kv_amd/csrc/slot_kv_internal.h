@@ -90,11 +90,10 @@ constexpr bool decode_mfma(int D, int G) {
   const int gi = G == 1 ? 0 : (G == 2 ? 1 : (G == 4 ? 2 : 3));
   return (SLOT_KV_MFMA_SHAPES >> (4 * di + gi)) & 1u;
 }
-// Waves per workgroup.  Eight waves share a unit's keys; in the vector-ALU
-// form G = 8 keeps four, since its lanes hold twice the query and
-// accumulator state and the larger workgroups measured slower there.
+// Waves per workgroup.  Eight waves share a unit's keys; G = 8 keeps four
+// (two workgroups per CU), which measured faster there in both forms.
 constexpr int decode_waves(int D, int G) {
-  return SLOT_KV_WG_WAVES ? SLOT_KV_WG_WAVES : (G >= 8 && !decode_mfma(D, G) ? 4 : 8);
+  return SLOT_KV_WG_WAVES ? SLOT_KV_WG_WAVES : (G >= 8 ? 4 : 8);
 }
 // Lanes per key row: enough that each lane holds about 32 floats of query
 // (G heads) and as many of accumulator, at most 16 (one DPP row).

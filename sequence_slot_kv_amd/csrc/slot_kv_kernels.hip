@@ -139,7 +139,12 @@ constexpr int wg_waves() {
 template <int D, int G>
 struct alignas(16) Lds {
   static constexpr int NW = wg_waves<D, G>();
-  float acc[NW][G][D];
+  // Wave w's (acc, max, sum) per head for the workgroup's merge.  In the
+  // matrix-core form acc[w] is 16 rows long and is also the wave's K tile
+  // during pass 1: the wave stores its accumulators there only after its
+  // pass 2, and the next unit's pass 1 starts after the merge.
+  static constexpr int ROWS = decode_mfma(D, G) ? 16 : G;
+  float acc[NW][ROWS][D];
   float m[NW][G];
   float l[NW][G];
   uint32_t last;
@@ -467,7 +472,6 @@ struct ValuCore {
       }
     }
   }
-  static constexpr int KT = 0;  // no LDS K tile
   __device__ __forceinline__ void score(const Stage& sg, uint32_t st, const UnitPlan& u,
                                         float* sc_w, float*) {
     const bool tail = st >= u.n_full;
@@ -636,7 +640,7 @@ struct MfmaCore {
   static constexpr int TD = D / 16;  // output tiles of 16 head_dim values
   static constexpr int NV = TD / 4;  // V float4 per lane per key of its lane group
   static_assert(TPS * 16 == S::STEP && NK == 4 * NV && NV >= 1, "16-key tiles, head_dim >= 64");
-  static constexpr int KT = 16 * D;  // floats of the wave's LDS K tile
+  static_assert(Lds<D, G>::ROWS == 16, "the K tile shares the wave's accumulator slot");
   struct Stage {
     // tile t, K or V: x[t][m*NV + i] = row 16t + 4g + m, floats 4c + 64i ..
     f4 x[TPS][NK];
@@ -813,7 +817,6 @@ __global__ void __launch_bounds__((kWave * wg_waves<D, G>()))
   constexpr int NW = S::NW, kThreads = kWave * NW;
   __shared__ Lds<D, G> sh;
   __shared__ __attribute__((aligned(16))) float sc_lds[NW][S::SCORES];
-  __shared__ __attribute__((aligned(16))) float kt_lds[NW][Core::KT > 0 ? Core::KT : 1];
   __shared__ uint32_t mbox[2];  // next unit, by unit parity; kNoUnit until posted
   __shared__ PrepLds<D, G> prep;
   if (a.magic != kArgsMagic) return;  // argument block not delivered whole
@@ -892,7 +895,7 @@ __global__ void __launch_bounds__((kWave * wg_waves<D, G>()))
     // A.  The last V stage is consumed with nothing behind it; the next unit's
     // first K stage goes out once this unit's results are stored.
     float* sc_w = &sc_lds[w][0];
-    float* kt_w = &kt_lds[w][0];
+    float* kt_w = &sh.acc[w][0][0];  // the K tile of the matrix-core form
     const uint32_t n_st = u.n_st;
     if (n_st > 0) {  // wave-uniform
       // pass 1
