@@ -12,6 +12,7 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -24,25 +25,54 @@ ARCH = "gfx950"
 SOURCES = ["slot_kv_api.hip", "slot_kv_kernels.hip", "slot_kv_prefill.hip", "slot_kv_state.hip",
            "slot_kv_plan.cpp"]
 
-COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"--offload-arch={ARCH}",
-          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          # every atomic in the kernels is issued by a single lane; the
-          # wave-aggregating rewrite would read each result at once
-          "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
-          "-I", INCLUDE, "-I", CSRC]
+def common(csrc: str = CSRC) -> list:
+    """hipcc flags of every source (headers from ``csrc``)."""
+    return ["-O3", "-std=c++17", "-fPIC", "-Wall", f"--offload-arch={ARCH}",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # every atomic in the kernels is issued by a single lane; the
+            # wave-aggregating rewrite would read each result at once
+            "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
+            "-I", INCLUDE, "-I", csrc]
 
 
-def build(extra=None, out: str = LIB, verbose: bool = False) -> str:
-    """Compile every source into ``out`` (a fresh build each call)."""
+COMMON = common()
+
+# Flags of single sources.  The prefill kernels keep their MFMA accumulators
+# in ordinary VGPRs: in the AGPR form every rescale of an output accumulator
+# copies it out and back, and the split register file lowers the tiled
+# attention's occupancy from four waves per SIMD to three.
+PER_SOURCE = {"slot_kv_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
+def build(extra=None, out: str = LIB, verbose: bool = False, csrc: str = CSRC) -> str:
+    """Compile every source of ``csrc`` (in parallel) and link ``out``; a
+    fresh build each call."""
     extra = list(extra or [])
     tmp = out + ".tmp"
-    cmd = [HIPCC, *COMMON, *extra, "-shared", "-o", tmp,
-           *[os.path.join(CSRC, s) for s in SOURCES]]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stdout}\n{r.stderr}")
+    with tempfile.TemporaryDirectory() as tmpd:
+        jobs, objs = [], []
+        for src in SOURCES:
+            obj = os.path.join(tmpd, src + ".o")
+            cmd = [HIPCC, *common(csrc), *PER_SOURCE.get(src, []), *extra, "-c", "-o", obj,
+                   os.path.join(csrc, src)]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            jobs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                               stderr=subprocess.PIPE, text=True)))
+            objs.append(obj)
+        failed = []
+        for cmd, proc in jobs:
+            so, se = proc.communicate()
+            if proc.returncode != 0:
+                failed.append(f"{cmd[-1]} ({proc.returncode}):\n{so}\n{se}")
+        if failed:
+            raise RuntimeError("hipcc failed: " + "\n".join(failed))
+        cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-o", tmp, *objs]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed ({r.returncode}):\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, out)
     return out
 

@@ -50,6 +50,7 @@ struct SsmLayer {
 
 struct slot_kv {
   int device = -1;
+  uint32_t n_cu = 0;  // compute units of the device
   uint32_t n_slots = 0, slot_ctx = 0;
   std::vector<LayerState> layers;
   std::vector<SsmLayer> ssm;                  // per-slot SSM state, one entry per ssm layer
@@ -260,8 +261,12 @@ int slot_state_alloc(slot_kv* h, uint32_t n_slots, uint32_t slot_ctx, const uint
   free_scratch(h);
   h->n_slots = h->slot_ctx = 0;
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return SLOT_KV_EDEVICE;
+  int cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return SLOT_KV_EDEVICE;
   h->device = dev;
+  h->n_cu = static_cast<uint32_t>(std::max(cus, 1));
   scratch_setup(dev);  // the allocation-free decode's scratch on this device
   // Everything is allocated into h's vectors as it goes, so a failure part
   // way frees exactly what was made.
@@ -640,10 +645,11 @@ struct PrefillLaunch {
 void tiled_counts(const std::vector<SeqRows>& seqs, size_t s0, uint32_t n, uint32_t G,
                   uint32_t ck, uint64_t* groups, uint64_t* items_per_head) {
   *groups = *items_per_head = 0;
+  const uint64_t rpg = slotkv::kPrefillRowsPerGroup;
   for (size_t i = s0; i < s0 + n; ++i) {
     const uint64_t tiles = (uint64_t(seqs[i].len) * G + 15) / 16;
     const uint64_t n_ck = ck ? (uint64_t(seqs[i].pos0) + seqs[i].len + ck - 1) / ck : 1;
-    *groups += (tiles * 16 + slotkv::kPrefillRowsPerGroup - 1) / slotkv::kPrefillRowsPerGroup * n_ck;
+    *groups += (tiles * 16 + rpg - 1) / rpg * n_ck;
     *items_per_head += tiles * n_ck;
   }
 }
@@ -691,6 +697,7 @@ uint32_t plan_split(const std::vector<SeqRows>& seqs, size_t s0, uint32_t n, uin
     if (ck >= max_keys) return 0;
   }
 }
+
 
 int run_prefill(slot_kv* h, uint32_t layer, const float* q, const float* k_new,
                 const float* v_new, float* out, const std::vector<SeqRows>& seqs, void* stream) {
@@ -782,6 +789,7 @@ int run_prefill(slot_kv* h, uint32_t layer, const float* q, const float* k_new,
     p.n_items = items;
     p.split_keys = ck;
     p.n_groups = 0;
+    p.band = 0;
     if (!split) {  // tiled workgroups, heaviest sequence first
       std::vector<uint64_t> work(n);
       for (uint32_t i = 0; i < n; ++i) {
@@ -801,6 +809,9 @@ int run_prefill(slot_kv* h, uint32_t layer, const float* q, const float* k_new,
       }
       a.s.grp_off[n] = groups;
       p.n_groups = groups;
+      // Launch bands of one workgroup per CU: the kv heads of a group rank
+      // are launched together, so a band is n_cu / n_kv_heads ranks.
+      p.band = std::max<uint32_t>(1, h->n_cu / L.n_kv_heads);
     }
     p.n_seq = n;
     p.n_rows = rows;

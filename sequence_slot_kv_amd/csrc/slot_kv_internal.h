@@ -90,10 +90,11 @@ constexpr bool decode_mfma(int D, int G) {
   const int gi = G == 1 ? 0 : (G == 2 ? 1 : (G == 4 ? 2 : 3));
   return (SLOT_KV_MFMA_SHAPES >> (4 * di + gi)) & 1u;
 }
-// Waves per workgroup.  Eight waves share a unit's keys; G = 8 keeps four
-// (two workgroups per CU), which measured faster there in both forms.
+// Waves per workgroup.  Eight waves share a unit's keys in the vector-ALU
+// form; G = 8 and the matrix-core form keep four (two workgroups per CU),
+// which measured faster there.
 constexpr int decode_waves(int D, int G) {
-  return SLOT_KV_WG_WAVES ? SLOT_KV_WG_WAVES : (G >= 8 ? 4 : 8);
+  return SLOT_KV_WG_WAVES ? SLOT_KV_WG_WAVES : (G >= 8 || decode_mfma(D, G) ? 4 : 8);
 }
 // Lanes per key row: enough that each lane holds about 32 floats of query
 // (G heads) and as many of accumulator, at most 16 (one DPP row).
@@ -243,6 +244,7 @@ struct PrefillParams {
   float qk_scale_log2;     // scale * log2(e)
   uint32_t flags;          // SLOT_KV_FLAG_*
   uint32_t prep_vpw;       // head vectors per wave of the prep kernel
+  uint32_t band;           // tiled: groups per launch band, every other band reversed (0: none)
 };
 
 struct PrefillSeqs {
@@ -265,7 +267,6 @@ static_assert(sizeof(PrefillArgs) < 4000, "kernel arguments must stay below 4 Ki
 
 // Query rows per attention workgroup of a prefill (4 waves x 16 rows).
 constexpr uint32_t kPrefillRowsPerGroup = 64;
-
 // Key-chunked attention.  The keys of a (sequence, kv head) are cut into
 // chunks of split_keys keys, and each (chunk, 16-row tile) pair leaves a
 // partial result (an item), ordered within a sequence
@@ -314,7 +315,10 @@ SLOTKV_HD inline uint32_t split_item_of_block(const PrefillSeqs& seqs, uint32_t 
 constexpr uint32_t kSplitMinKeys = 256;       // smallest split-K chunk
 constexpr uint32_t kMaxSplitItems = 1u << 14; // per launch (bounds the partials)
 constexpr uint32_t kChunkBelowGroups = 512;
-constexpr uint32_t kChunkTargetGroups = 1024;
+#ifndef SLOT_KV_CHUNK_TARGET
+#define SLOT_KV_CHUNK_TARGET 1024
+#endif
+constexpr uint32_t kChunkTargetGroups = SLOT_KV_CHUNK_TARGET;
 
 // Launches of a prefill / verify: norm + RoPE + KV write, then the
 // attention (tiled, or split-K and merge when `split`).  `before_attn` /

@@ -32,6 +32,7 @@ constexpr int kPrepWaves = 4;
 constexpr int kAttnWaves = 4;
 static_assert(kAttnWaves * 16 == kPrefillRowsPerGroup, "rows per attention workgroup");
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyLog2 = 8.f;  // tiled attention: max growth absorbed without a rescale
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -159,15 +160,19 @@ __global__ void __launch_bounds__(kWave * kPrepWaves) prefill_prep_kernel(const 
 // l works on row c = l % 16 and lane group g = l / 16:
 //   S^T block:  A = K[key c][d], B = Q[row c][d] with d = (D/4)*g + i for
 //               MFMA i < D/4; result lane l, register r: key 4g + r, row c;
-//   O^T tile u: MFMA m < 4 sums key 4g + m (A = V[key][d], d = (D/16)*c + u;
+//   O^T tile u: MFMA m < 4 sums key 4g + m (A = V[key][d], d = 4c + 64(u/4)
+//               + u%4, so that the sixteen lanes of a lane group read 256
+//               contiguous bytes of a staged row, free of bank conflicts;
 //               B = the score register m); result lane l, register r:
-//               d = (D/16)*(4g + r) + u, row c.
-// So a lane's whole accumulator belongs to its own row, and its output
-// values are d = (D/4)*g .. (D/4)*g + D/4 - 1.  Workgroups are launched
+//               d = 16g + 4r + 64(u/4) + u%4, row c.
+// So a lane's whole accumulator belongs to its own row.  Workgroup ranks run
 // heaviest first: sequences by decreasing work, and inside a sequence its
-// last tokens first, so that the short ones fill in at the end.
+// last tokens first.  The ranks are launched in bands of one workgroup per
+// CU, every other band reversed: the CUs take their first workgroups about
+// one from each band, so that each CU's resident set sums to about the same
+// work (in plain heaviest-first order the first CU would hold the heaviest
+// of every band), and the shortest ones fill in at the end.
 constexpr int kLdsPad = 4;  // floats of padding per staged row: rows start 4 banks apart
-
 template <int D>
 struct PrefillLds {
   float k[2][16][D + kLdsPad];
@@ -187,10 +192,17 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) prefill_attn_kernel(const 
   const uint32_t lane = tid % kWave;
   const uint32_t w = tid / kWave;
   const uint32_t g = lane / 16, c = lane % 16;
-  // workgroup -> (kv head, sequence, tile group, key chunk), heaviest first
+  // workgroup -> (kv head, sequence, tile group, key chunk)
   const uint32_t CK = CHUNKED ? p.split_keys : 0;  // 0: one chunk of all keys
   const uint32_t j = blockIdx.x % p.n_kv_heads;
-  const uint32_t flat = blockIdx.x / p.n_kv_heads;  // < n_groups
+  // the group's rank in the heaviest-first order; every other band of
+  // p.band ranks is taken in reverse, so that the workgroups a CU receives
+  // at once (about one from each band) add up to about the same work
+  uint32_t flat = blockIdx.x / p.n_kv_heads;  // < n_groups
+  if (p.band) {
+    const uint32_t b0 = flat - flat % p.band;
+    if ((flat / p.band) & 1) flat = b0 + min(p.band, p.n_groups - b0) - 1 - (flat - b0);
+  }
   uint32_t lo = 0, hi = p.n_seq;
   while (hi - lo > 1) {
     const uint32_t mid = (lo + hi) / 2;
@@ -202,20 +214,19 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) prefill_attn_kernel(const 
   const uint32_t local = a.s.grp_off[lo + 1] - 1 - flat;  // the sequence's last group first
   const uint32_t grp = local / n_ck, chunk = local - grp * n_ck;
   const uint32_t n_tiles = (T * G + 15) / 16;
-  const uint32_t tile = grp * kAttnWaves + w;  // may be past the last tile: then it only stages
-  const uint32_t R = tile * 16 + c;
-  const uint32_t t = R / G, h = j * G + R % G;
-  const bool row_ok = t < T;
-  const uint32_t tq = row_ok ? t : T - 1;  // rows past the last token compute on it, unused
-  const uint32_t row_pos = pos0 + tq;
-  // keys of this wave's tile, and of the workgroup (its last existing tile)
-  const uint32_t wave_keys = pos0 + min((tile * 16 + 15) / G, T - 1) + 1;
-  const uint32_t last_tile = min(grp * kAttnWaves + kAttnWaves - 1, n_tiles - 1);
-  const uint32_t n_keys = pos0 + min((last_tile * 16 + 15) / G, T - 1) + 1;
+  // keys up to and including the last token of a tile's rows
+  auto tile_keys = [&](uint32_t tl) { return pos0 + min((tl * 16 + 15) / G, T - 1) + 1; };
+  // the wave's tile (one past the last tile only helps stage)
+  const uint32_t tile = grp * kAttnWaves + w;
+  const uint32_t n_keys = tile_keys(min(grp * kAttnWaves + kAttnWaves - 1, n_tiles - 1));
   // the workgroup's keys [k_lo, k_hi): its chunk of the keys of its last tile
   const uint32_t k_lo = CK ? chunk * CK : 0;
   if (k_lo >= n_keys) return;  // workgroup-uniform, before any barrier
   const uint32_t k_hi = CK ? min(k_lo + CK, n_keys) : n_keys;
+  const uint32_t R = tile * 16 + c;
+  const uint32_t t = R / G, h = j * G + R % G;
+  const uint32_t tq = min(t, T - 1);  // rows past the last token compute on it, unused
+  const uint32_t row_pos = pos0 + tq;
 
   float qv[DQ];
   {
@@ -235,79 +246,127 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) prefill_attn_kernel(const 
   // Staging: float4 f = tid + 256*s of a block is row f / (D/4), column
   // 4 * (f % (D/4)).  Keys past the workgroup's range re-read its last key.
   f4 stk[NF4], stv[NF4];
-  auto fetch = [&](uint32_t kb) {
+  auto fetch = [&](f4* st, const float* base, uint32_t kb) {
 #pragma unroll
     for (int s = 0; s < NF4; ++s) {
       const uint32_t f = tid + kWave * kAttnWaves * s;
       const uint32_t row = f / (D / 4), col = 4 * (f % (D / 4));
-      const size_t at = static_cast<size_t>(min(kb + row, k_hi - 1)) * p.kv_dim + col;
-      stk[s] = *reinterpret_cast<const f4*>(kbase + at);
-      stv[s] = *reinterpret_cast<const f4*>(vbase + at);
+      st[s] = *reinterpret_cast<const f4*>(base + static_cast<size_t>(min(kb + row, k_hi - 1)) *
+                                                      p.kv_dim + col);
     }
   };
-  auto stage = [&](uint32_t buf) {
+  auto stage = [&](float (*buf)[D + kLdsPad], const f4* st) {
 #pragma unroll
     for (int s = 0; s < NF4; ++s) {
       const uint32_t f = tid + kWave * kAttnWaves * s;
-      const uint32_t row = f / (D / 4), col = 4 * (f % (D / 4));
-      *reinterpret_cast<f4*>(&sh.k[buf][row][col]) = stk[s];
-      *reinterpret_cast<f4*>(&sh.v[buf][row][col]) = stv[s];
+      *reinterpret_cast<f4*>(&buf[f / (D / 4)][4 * (f % (D / 4))]) = st[s];
     }
+  };
+  // S^T of a staged key block
+  auto scores = [&](uint32_t buf) {
+    f4 sc = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < DQ; i += 4) {
+      const f4 ka = *reinterpret_cast<const f4*>(&sh.k[buf][c][DQ * g + i]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        sc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[e], qv[i + e], sc, 0, 0, 0);
+    }
+    return sc;
   };
 
   float m_run = -INFINITY, l_run = 0.f;
   f4 o[TD];
 #pragma unroll
   for (int u = 0; u < TD; ++u) o[u] = f4{0.f, 0.f, 0.f, 0.f};
-
-  const uint32_t n_blk = (k_hi - k_lo + 15) / 16;
-  fetch(k_lo);
-  stage(0);
-  __syncthreads();
-  for (uint32_t blk = 0; blk < n_blk; ++blk) {  // workgroup-uniform
-    const uint32_t buf = blk & 1;
-    const uint32_t kb = k_lo + blk * 16;
-    if (blk + 1 < n_blk) fetch(kb + 16);
-    if (kb < wave_keys) {  // wave-uniform: blocks past the tile are all masked
-      f4 s = f4{0.f, 0.f, 0.f, 0.f};
+  // the block's weights: causal mask, running reference, exponentials
+  auto weights = [&](f4 sc, uint32_t kb) {
+    // key kb + 4g + r counts iff it is <= the row's position and inside the
+    // workgroup's keys (keys >= n_keys are past every row)
 #pragma unroll
-      for (int i = 0; i < DQ; i += 4) {
-        const f4 ka = *reinterpret_cast<const f4*>(&sh.k[buf][c][DQ * g + i]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          s = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[e], qv[i + e], s, 0, 0, 0);
-      }
-      // causal mask: key kb + 4g + r counts iff it is <= the row's position
-      // and inside the workgroup's keys (keys >= n_keys are past every row)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (kb + 4 * g + r > row_pos || (CHUNKED && kb + 4 * g + r >= k_hi)) s[r] = -INFINITY;
-      float mb = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-      mb = fmaxf(mb, __shfl_xor(mb, 16));
-      mb = fmaxf(mb, __shfl_xor(mb, 32));
-      const float m_new = fmaxf(m_run, mb);
-      // finite from key 0 on; a later chunk may hold no key of a row yet
-      const float m_use = (CHUNKED && m_new == -INFINITY) ? 0.f : m_new;
-      const float corr = fast_exp2(m_run - m_use);
-      f4 pr;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(s[r] - m_use);
-      l_run = l_run * corr + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+    for (int r = 0; r < 4; ++r)
+      if (kb + 4 * g + r > row_pos || (CHUNKED && kb + 4 * g + r >= k_hi)) sc[r] = -INFINITY;
+    float mb = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mb = fmaxf(mb, __shfl_xor(mb, 16));
+    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    // m_run is the reference the exponentials are taken against; it moves
+    // (rescaling the sum and accumulator) only when a block's max passes it
+    // by more than kLazyLog2, so most blocks skip the rescale and every
+    // weight stays below 2^kLazyLog2
+    const bool up = mb > m_run + kLazyLog2;
+    if (__any(up)) {  // wave-uniform
+      const float m_new = up ? mb : m_run;
+      const float corr = up ? fast_exp2(m_run - m_new) : 1.f;  // 0 from -inf
+      l_run *= corr;
 #pragma unroll
       for (int u = 0; u < TD; ++u) o[u] *= corr;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-#pragma unroll
-        for (int u = 0; u < TD; u += 4) {
-          const f4 va = *reinterpret_cast<const f4*>(&sh.v[buf][4 * g + m][TD * c + u]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            o[u + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(va[e], pr[m], o[u + e], 0, 0, 0);
-        }
-      }
       m_run = m_new;
     }
-    if (blk + 1 < n_blk) stage(buf ^ 1u);
+    // finite from key 0 on; a later chunk may hold no key of a row yet
+    const float m_use = (CHUNKED && m_run == -INFINITY) ? 0.f : m_run;
+    f4 pr;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sc[r] - m_use);
+    l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    return pr;
+  };
+  // O^T += V^T P^T
+  auto accumulate = [&](uint32_t buf, f4 pr) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+#pragma unroll
+      for (int u = 0; u < TD; u += 4) {
+        const f4 va = *reinterpret_cast<const f4*>(&sh.v[buf][4 * g + m][4 * c + 16 * u]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[u + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(va[e], pr[m], o[u + e], 0, 0, 0);
+      }
+    }
+  };
+
+  // Software pipeline over the key blocks b: the pass of block b takes the
+  // weights of b (from the scores the previous pass left), the scores of
+  // b + 1 and the accumulation of b, so that the matrix cores have
+  // independent work while the weights are formed.  K runs one block ahead
+  // of V: during pass b, K(b+1) and V(b) are read from LDS while K(b+2) and
+  // V(b+1) are fetched into registers, then written into the buffers that
+  // K(b) and V(b-1) held (read in the previous pass, before its barrier).
+  const uint32_t n_blk = (k_hi - k_lo + 15) / 16;
+  // the wave's blocks: those below its tile's last key (none past the last tile)
+  const uint32_t wave_keys = tile_keys(tile);
+  const uint32_t w_blk =
+      tile < n_tiles && wave_keys > k_lo ? min(n_blk, (wave_keys - k_lo + 15) / 16) : 0;
+  fetch(stk, kbase, k_lo);
+  fetch(stv, vbase, k_lo);
+  stage(sh.k[0], stk);
+  stage(sh.v[0], stv);
+  if (n_blk > 1) {
+    fetch(stk, kbase, k_lo + 16);
+    stage(sh.k[1], stk);
+  }
+  // The query registers are read in every pass: their loads land here, so
+  // that no wait inside the loop (where a fetch may or may not have been
+  // issued) has to wait for the loop's fetches as well.
+#pragma unroll
+  for (int i = 0; i < DQ; ++i) asm volatile("" ::"v"(qv[i]));
+  __syncthreads();
+  f4 s_cur = f4{0.f, 0.f, 0.f, 0.f};
+  if (w_blk > 0) s_cur = scores(0);
+  __syncthreads();  // K buffer 0 is written again in pass 0
+  for (uint32_t b = 0; b < n_blk; ++b) {  // workgroup-uniform
+    const uint32_t kb = k_lo + b * 16;
+    const bool next_k = b + 2 < n_blk, next_v = b + 1 < n_blk;
+    if (next_k) fetch(stk, kbase, kb + 32);
+    if (next_v) fetch(stv, vbase, kb + 16);
+    if (b + 1 < w_blk) {  // wave-uniform
+      const f4 s_next = scores((b + 1) & 1);
+      accumulate(b & 1, weights(s_cur, kb));
+      s_cur = s_next;
+    } else if (b < w_blk) {
+      accumulate(b & 1, weights(s_cur, kb));
+    }
+    if (next_k) stage(sh.k[b & 1], stk);
+    if (next_v) stage(sh.v[(b + 1) & 1], stv);
     __syncthreads();
   }
 
@@ -318,12 +377,12 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) prefill_attn_kernel(const 
   if (CHUNKED) {  // one chunk of several: leave the partial for the merge
     if (k_lo >= wave_keys) return;  // no key of this tile here: the merge skips it
     const uint32_t item = a.s.item_off[sq] + (chunk * p.n_kv_heads + j) * n_tiles + tile;
-    float* acc = p.part + (static_cast<size_t>(item) * 16 + c) * D + DQ * g;
+    float* acc = p.part + (static_cast<size_t>(item) * 16 + c) * D + 16 * g;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int u = 0; u < TD; u += 4)
-        *reinterpret_cast<f4*>(acc + TD * r + u) = f4{o[u][r], o[u + 1][r], o[u + 2][r], o[u + 3][r]};
+        *reinterpret_cast<f4*>(acc + 4 * r + 16 * u) = f4{o[u][r], o[u + 1][r], o[u + 2][r], o[u + 3][r]};
     if (g == 0) {
       float* ml = p.part + static_cast<size_t>(p.n_items) * 16 * D + (static_cast<size_t>(item) * 16 + c) * 2;
       ml[0] = m_run;
@@ -340,14 +399,14 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) prefill_attn_kernel(const 
       L = L * sa + fast_exp2(sk - mn);
     }
   }
-  if (!row_ok) return;
+  if (t >= T) return;
   const float rs = sa / L;
-  float* dst = p.out + (static_cast<size_t>(row0 + t) * p.n_heads + h) * D + DQ * g;
+  float* dst = p.out + (static_cast<size_t>(row0 + t) * p.n_heads + h) * D + 16 * g;
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int u = 0; u < TD; u += 4)
-      *reinterpret_cast<f4*>(dst + TD * r + u) =
+      *reinterpret_cast<f4*>(dst + 4 * r + 16 * u) =
           f4{o[u][r], o[u + 1][r], o[u + 2][r], o[u + 3][r]} * rs;
 }
 
