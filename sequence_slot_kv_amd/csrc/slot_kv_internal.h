@@ -281,7 +281,10 @@ constexpr uint32_t kSplitMaxRows = 64;
 // Split-K workgroups take four consecutive chunks of one (sequence, kv head,
 // tile), ordered item_off[i] + (j * n_tiles + tile) * groups + group, and
 // leave one partial each.
-constexpr uint32_t kSplitChunksPerGroup = 4;
+#ifndef SLOT_KV_SPLIT_GROUP
+#define SLOT_KV_SPLIT_GROUP 4
+#endif
+constexpr uint32_t kSplitChunksPerGroup = SLOT_KV_SPLIT_GROUP;
 SLOTKV_HD inline uint32_t split_groups(uint32_t keys, uint32_t split_keys) {
   const uint32_t chunks = (keys + split_keys - 1) / split_keys;
   return (chunks + kSplitChunksPerGroup - 1) / kSplitChunksPerGroup;
@@ -312,7 +315,10 @@ SLOTKV_HD inline uint32_t split_item_of_block(const PrefillSeqs& seqs, uint32_t 
   }
   return seqs.item_off[lo] + (f - seqs.grp_off[lo]) * ng + ng - 1;
 }
-constexpr uint32_t kSplitMinKeys = 256;       // smallest split-K chunk
+#ifndef SLOT_KV_SPLIT_MIN_KEYS
+#define SLOT_KV_SPLIT_MIN_KEYS 256
+#endif
+constexpr uint32_t kSplitMinKeys = SLOT_KV_SPLIT_MIN_KEYS;  // smallest split-K chunk
 constexpr uint32_t kMaxSplitItems = 1u << 14; // per launch (bounds the partials)
 constexpr uint32_t kChunkBelowGroups = 512;
 #ifndef SLOT_KV_CHUNK_TARGET

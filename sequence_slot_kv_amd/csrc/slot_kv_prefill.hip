@@ -432,13 +432,14 @@ constexpr int split_waves_per_eu() { return D <= 128 ? 2 : 1; }
 // LDS of a split-K workgroup: waves 1..3 hand their results to wave 0,
 // element-major ([float][lane]) so that the 16-byte stores of a wave fall on
 // consecutive banks.
+constexpr int kSplitWaves = kSplitChunksPerGroup;  // waves per split-K workgroup
 template <int D>
 struct SplitLds {
-  f4 acc[kAttnWaves - 1][D / 16][kWave];
-  float m[kAttnWaves - 1][kWave];
-  float l[kAttnWaves - 1][kWave];
+  f4 acc[kSplitWaves > 1 ? kSplitWaves - 1 : 1][D / 16][kWave];
+  float m[kSplitWaves > 1 ? kSplitWaves - 1 : 1][kWave];
+  float l[kSplitWaves > 1 ? kSplitWaves - 1 : 1][kWave];
   // per wave: a K block on its way to the A layout (head_dim up to 128)
-  float kt[kAttnWaves][D <= 128 ? 16 * D : 4];
+  float kt[kSplitWaves][D <= 128 ? 16 * D : 4];
 };
 
 // Float offset of 16-byte segment s of row r in a wave's LDS K block: the
@@ -450,7 +451,7 @@ __device__ __forceinline__ uint32_t kt_at(uint32_t r, uint32_t s) {
 }
 
 template <int D, int G>
-__global__ void __launch_bounds__(kWave * kAttnWaves)
+__global__ void __launch_bounds__(kWave * kSplitWaves)
 __attribute__((amdgpu_waves_per_eu(split_waves_per_eu<D>()))) split_attn_kernel(const PrefillArgs a) {
   constexpr int NK = D / 16;   // K float4 per lane per block
   constexpr int TD = D / 16;   // output tiles of 16 head_dim values
@@ -483,7 +484,7 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_eu<D>()))) split_attn_kernel(
   const uint32_t tile = ut % n_tiles;
   const uint32_t j = ut / n_tiles;
   const uint32_t tile_keys = pos0 + min((tile * 16 + 15) / G, T - 1) + 1;
-  const uint32_t k0 = (grp * kAttnWaves + w) * p.split_keys;
+  const uint32_t k0 = (grp * kSplitWaves + w) * p.split_keys;
   const bool active = k0 < tile_keys;  // wave-uniform: else nothing of this tile here
   const uint32_t k1 = active ? min(k0 + p.split_keys, tile_keys) : k0 + 1;
   const uint32_t n_blk = active ? (k1 - k0 + 15) / 16 : 0;
@@ -525,7 +526,8 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_eu<D>()))) split_attn_kernel(
     for (int m = 0; m < 4; ++m) {
       const float* rp = base + static_cast<size_t>(min(kb + 4 * g + m, k1 - 1)) * p.kv_dim + 4 * c;
 #pragma unroll
-      for (int x = 0; x < NV; ++x) r[m][x] = *reinterpret_cast<const f4*>(rp + 64 * x);
+      for (int x = 0; x < NV; ++x)
+        r[m][x] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(rp + 64 * x));
     }
   };
   constexpr bool kKTile = D <= 128;
@@ -536,7 +538,8 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_eu<D>()))) split_attn_kernel(
       const uint32_t kb = k0 + 16 * b;
       const float* kp = kbase + static_cast<size_t>(min(kb + c, k1 - 1)) * p.kv_dim + 4 * g;
 #pragma unroll
-      for (int v = 0; v < NK; ++v) kr[v / NV][v % NV] = *reinterpret_cast<const f4*>(kp + 16 * v);
+      for (int v = 0; v < NK; ++v)
+        kr[v / NV][v % NV] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(kp + 16 * v));
     }
   };
   auto load_v = [&](f4 (&vr)[4][NV], uint32_t b) { load_rows(vbase, vr, b); };
@@ -611,6 +614,11 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_eu<D>()))) split_attn_kernel(
     load_k(kb_, 1);
     load_v(vb, 1);
   }
+  // The query registers are read in every block: their loads land here.
+  // Left to the loop, the wait for them would sit where the loads in flight
+  // are those of the next blocks, and would wait for those as well.
+#pragma unroll
+  for (int i = 0; i < DQ; ++i) asm volatile("" ::"v"(qv[i]));
   uint32_t b = 0;
   for (; b + 2 <= n_blk; b += 2) {
     __builtin_amdgcn_sched_barrier(0);
@@ -640,24 +648,26 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_eu<D>()))) split_attn_kernel(
   // waves 1..3 hand (acc, m, l) to wave 0, which rescales all four to their
   // common maximum (an empty chunk, m = -inf, weighs 0) and adds them in
   // wave order
-  if (w > 0) {
+  if constexpr (kSplitWaves > 1) {
+    if (w > 0) {
 #pragma unroll
-    for (int u = 0; u < TD; ++u) sh.acc[w - 1][u][lane] = o[u];
-    sh.m[w - 1][lane] = m_run;
-    sh.l[w - 1][lane] = L;
+      for (int u = 0; u < TD; ++u) sh.acc[w - 1][u][lane] = o[u];
+      sh.m[w - 1][lane] = m_run;
+      sh.l[w - 1][lane] = L;
+    }
+    __syncthreads();
+    if (w > 0) return;
   }
-  __syncthreads();
-  if (w > 0) return;
   float mx = m_run;
 #pragma unroll
-  for (int v = 0; v < kAttnWaves - 1; ++v) mx = fmaxf(mx, sh.m[v][lane]);
+  for (int v = 0; v < kSplitWaves - 1; ++v) mx = fmaxf(mx, sh.m[v][lane]);
   const float base = mx == -INFINITY ? 0.f : mx;  // every chunk empty: all stays zero
   const float s0 = fast_exp2(m_run - base);
   L *= s0;
 #pragma unroll
   for (int u = 0; u < TD; ++u) o[u] *= s0;
 #pragma unroll
-  for (int v = 0; v < kAttnWaves - 1; ++v) {
+  for (int v = 0; v < kSplitWaves - 1; ++v) {
     const float sv = fast_exp2(sh.m[v][lane] - base);
     L += sh.l[v][lane] * sv;
 #pragma unroll
@@ -700,7 +710,7 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) split_merge_kernel(const P
   // split-K partials are per group of kAttnWaves chunks (j-major items);
   // chunked tiled ones per chunk (chunk-major items)
   const bool grouped = p.n_groups == 0;
-  const uint32_t span = grouped ? p.split_keys * kAttnWaves : p.split_keys;
+  const uint32_t span = grouped ? p.split_keys * kSplitWaves : p.split_keys;
   const uint32_t nck = (tile_keys + span - 1) / span;
   const uint32_t first = grouped ? a.s.item_off[sq] + (j * n_tiles + tile) * split_groups(pos0 + T, p.split_keys)
                                  : a.s.item_off[sq] + j * n_tiles + tile;
@@ -759,7 +769,7 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) split_merge_kernel(const P
 
 template <int D, int G>
 hipError_t launch_split(const PrefillArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((split_attn_kernel<D, G>), dim3(a.p.n_items), dim3(kWave * kAttnWaves), 0, s, a);
+  hipLaunchKernelGGL((split_attn_kernel<D, G>), dim3(a.p.n_items), dim3(kWave * kSplitWaves), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint32_t waves = a.p.n_rows * a.p.n_heads;
