@@ -71,6 +71,7 @@ CSRC = os.path.join(ROOT, "sequence_slot_kv_amd", "csrc")
 KERNEL_SRC = os.path.join(CSRC, "slot_kv_kernels.hip")
 PREFILL_SRC = os.path.join(CSRC, "slot_kv_prefill.hip")
 STATE_SRC = os.path.join(CSRC, "slot_kv_state.hip")
+DEVICE_H = os.path.join(CSRC, "slot_kv_device.h")
 # launch-shaping constants (chunk size, waves per workgroup, row tables) that
 # every kernel is built with
 INTERNAL_H = os.path.join(CSRC, "slot_kv_internal.h")
@@ -83,10 +84,10 @@ def log(*a):
 
 
 def kernel_hash(src: str = KERNEL_SRC) -> str:
-    """Hash of a kernel's source file and of the internal header it is built
-    with: a profiler record stays valid only while both are unchanged."""
+    """Hash of a kernel's source file and of the internal headers it is built
+    with: a profiler record stays valid only while all are unchanged."""
     h = hashlib.sha256()
-    for path in (src, INTERNAL_H):
+    for path in (src, INTERNAL_H, DEVICE_H):
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
