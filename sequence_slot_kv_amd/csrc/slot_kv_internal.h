@@ -267,6 +267,7 @@ static_assert(sizeof(PrefillArgs) < 4000, "kernel arguments must stay below 4 Ki
 
 // Query rows per attention workgroup of a prefill (4 waves x 16 rows).
 constexpr uint32_t kPrefillRowsPerGroup = 64;
+
 // Key-chunked attention.  The keys of a (sequence, kv head) are cut into
 // chunks of split_keys keys, and each (chunk, 16-row tile) pair leaves a
 // partial result (an item), ordered within a sequence
@@ -278,9 +279,10 @@ constexpr uint32_t kPrefillRowsPerGroup = 64;
 // workgroups, which are cut into key chunks only when they are too few to
 // fill the chip (fewer than kChunkBelowGroups per launch).
 constexpr uint32_t kSplitMaxRows = 64;
-// Split-K workgroups take four consecutive chunks of one (sequence, kv head,
-// tile), ordered item_off[i] + (j * n_tiles + tile) * groups + group, and
-// leave one partial each.
+// Split-K workgroups take kSplitChunksPerGroup consecutive chunks (a build
+// setting, 4 by default: one per wave) of one (sequence, kv head, tile),
+// ordered item_off[i] + (j * n_tiles + tile) * groups + group, and leave one
+// partial each.
 #ifndef SLOT_KV_SPLIT_GROUP
 #define SLOT_KV_SPLIT_GROUP 4
 #endif

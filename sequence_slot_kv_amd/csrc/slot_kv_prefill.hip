@@ -707,7 +707,7 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) split_merge_kernel(const P
   const uint32_t j = h / G, R = t * G + h % G, tile = R / 16, c = R % 16;
   const uint32_t n_tiles = (T * G + 15) / 16;
   const uint32_t tile_keys = pos0 + min((tile * 16 + 15) / G, T - 1) + 1;
-  // split-K partials are per group of kAttnWaves chunks (j-major items);
+  // split-K partials are per group of kSplitWaves chunks (j-major items);
   // chunked tiled ones per chunk (chunk-major items)
   const bool grouped = p.n_groups == 0;
   const uint32_t span = grouped ? p.split_keys * kSplitWaves : p.split_keys;
