@@ -173,6 +173,18 @@ __global__ void __launch_bounds__(kWave * kPrepWaves) prefill_prep_kernel(const 
 // work (in plain heaviest-first order the first CU would hold the heaviest
 // of every band), and the shortest ones fill in at the end.
 constexpr int kLdsPad = 4;  // floats of padding per staged row: rows start 4 banks apart
+
+// Key-chunked tiled launches: the keys [0, n_keys) of a tile group are cut
+// into the sequence's n_ck chunks evenly, in whole 16-key blocks, so that
+// the group's workgroups carry equal work (a fixed chunk of split_keys
+// would leave the last one short).  The merge derives the same length.
+#ifndef SLOT_KV_EVEN_CHUNKS
+#define SLOT_KV_EVEN_CHUNKS 1
+#endif
+__device__ __forceinline__ uint32_t group_chunk_keys(uint32_t n_keys, uint32_t n_ck,
+                                                     uint32_t split_keys) {
+  return SLOT_KV_EVEN_CHUNKS ? ((n_keys + n_ck - 1) / n_ck + 15) / 16 * 16 : split_keys;
+}
 template <int D>
 struct PrefillLds {
   float k[2][16][D + kLdsPad];
@@ -220,9 +232,10 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) prefill_attn_kernel(const 
   const uint32_t tile = grp * kAttnWaves + w;
   const uint32_t n_keys = tile_keys(min(grp * kAttnWaves + kAttnWaves - 1, n_tiles - 1));
   // the workgroup's keys [k_lo, k_hi): its chunk of the keys of its last tile
-  const uint32_t k_lo = CK ? chunk * CK : 0;
-  if (k_lo >= n_keys) return;  // workgroup-uniform, before any barrier
-  const uint32_t k_hi = CK ? min(k_lo + CK, n_keys) : n_keys;
+  const uint32_t ckg = CK ? group_chunk_keys(n_keys, n_ck, CK) : 0;
+  const uint32_t k_lo = chunk * ckg;
+  if (CK && k_lo >= n_keys) return;  // workgroup-uniform, before any barrier
+  const uint32_t k_hi = CK ? min(k_lo + ckg, n_keys) : n_keys;
   const uint32_t R = tile * 16 + c;
   const uint32_t t = R / G, h = j * G + R % G;
   const uint32_t tq = min(t, T - 1);  // rows past the last token compute on it, unused
@@ -708,9 +721,17 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) split_merge_kernel(const P
   const uint32_t n_tiles = (T * G + 15) / 16;
   const uint32_t tile_keys = pos0 + min((tile * 16 + 15) / G, T - 1) + 1;
   // split-K partials are per group of kSplitWaves chunks (j-major items);
-  // chunked tiled ones per chunk (chunk-major items)
+  // chunked tiled ones per chunk (chunk-major items), each chunk of the
+  // tile group's keys cut evenly
   const bool grouped = p.n_groups == 0;
-  const uint32_t span = grouped ? p.split_keys * kSplitWaves : p.split_keys;
+  uint32_t span = p.split_keys * kSplitWaves;
+  if (!grouped) {
+    const uint32_t grp = tile / kAttnWaves;
+    const uint32_t last = min(grp * kAttnWaves + kAttnWaves - 1, n_tiles - 1);
+    const uint32_t n_keys = pos0 + min((last * 16 + 15) / G, T - 1) + 1;
+    const uint32_t n_ck = (pos0 + T + p.split_keys - 1) / p.split_keys;
+    span = group_chunk_keys(n_keys, n_ck, p.split_keys);
+  }
   const uint32_t nck = (tile_keys + span - 1) / span;
   const uint32_t first = grouped ? a.s.item_off[sq] + (j * n_tiles + tile) * split_groups(pos0 + T, p.split_keys)
                                  : a.s.item_off[sq] + j * n_tiles + tile;
