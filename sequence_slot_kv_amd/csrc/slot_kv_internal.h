@@ -268,6 +268,30 @@ static_assert(sizeof(PrefillArgs) < 4000, "kernel arguments must stay below 4 Ki
 // Query rows per attention workgroup of a prefill (4 waves x 16 rows).
 constexpr uint32_t kPrefillRowsPerGroup = 64;
 
+// Tiled launches: the heaviest-first rank of the workgroup at launch index
+// `flat` (< n_groups, per kv head).  Every other band of `band` ranks is
+// taken in reverse, so that the workgroups a CU receives at once (about one
+// from each band) add up to about the same work; band 0 leaves the order as
+// it is.  A permutation of [0, n_groups).
+SLOTKV_HD inline uint32_t tiled_rank(uint32_t flat, uint32_t band, uint32_t n_groups) {
+  if (band == 0 || (flat / band) % 2 == 0) return flat;
+  const uint32_t b0 = flat - flat % band;
+  const uint32_t len = n_groups - b0 < band ? n_groups - b0 : band;
+  return b0 + len - 1 - (flat - b0);
+}
+
+// Key-chunked tiled launches: a sequence's keys give n_ck chunks of
+// split_keys, and each tile group cuts its own keys [0, n_keys) into n_ck
+// even chunks of whole 16-key blocks, so that the group's workgroups carry
+// equal work.  Chunk c covers [c * len, min((c + 1) * len, n_keys)); a
+// chunk past n_keys is empty.
+#ifndef SLOT_KV_EVEN_CHUNKS
+#define SLOT_KV_EVEN_CHUNKS 1
+#endif
+SLOTKV_HD inline uint32_t group_chunk_keys(uint32_t n_keys, uint32_t n_ck, uint32_t split_keys) {
+  return SLOT_KV_EVEN_CHUNKS ? ((n_keys + n_ck - 1) / n_ck + 15) / 16 * 16 : split_keys;
+}
+
 // Key-chunked attention.  The keys of a (sequence, kv head) are cut into
 // chunks of split_keys keys, and each (chunk, 16-row tile) pair leaves a
 // partial result (an item), ordered within a sequence

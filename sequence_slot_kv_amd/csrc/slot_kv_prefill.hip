@@ -173,18 +173,6 @@ __global__ void __launch_bounds__(kWave * kPrepWaves) prefill_prep_kernel(const 
 // work (in plain heaviest-first order the first CU would hold the heaviest
 // of every band), and the shortest ones fill in at the end.
 constexpr int kLdsPad = 4;  // floats of padding per staged row: rows start 4 banks apart
-
-// Key-chunked tiled launches: the keys [0, n_keys) of a tile group are cut
-// into the sequence's n_ck chunks evenly, in whole 16-key blocks, so that
-// the group's workgroups carry equal work (a fixed chunk of split_keys
-// would leave the last one short).  The merge derives the same length.
-#ifndef SLOT_KV_EVEN_CHUNKS
-#define SLOT_KV_EVEN_CHUNKS 1
-#endif
-__device__ __forceinline__ uint32_t group_chunk_keys(uint32_t n_keys, uint32_t n_ck,
-                                                     uint32_t split_keys) {
-  return SLOT_KV_EVEN_CHUNKS ? ((n_keys + n_ck - 1) / n_ck + 15) / 16 * 16 : split_keys;
-}
 template <int D>
 struct PrefillLds {
   float k[2][16][D + kLdsPad];
@@ -207,14 +195,8 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) prefill_attn_kernel(const 
   // workgroup -> (kv head, sequence, tile group, key chunk)
   const uint32_t CK = CHUNKED ? p.split_keys : 0;  // 0: one chunk of all keys
   const uint32_t j = blockIdx.x % p.n_kv_heads;
-  // the group's rank in the heaviest-first order; every other band of
-  // p.band ranks is taken in reverse, so that the workgroups a CU receives
-  // at once (about one from each band) add up to about the same work
-  uint32_t flat = blockIdx.x / p.n_kv_heads;  // < n_groups
-  if (p.band) {
-    const uint32_t b0 = flat - flat % p.band;
-    if ((flat / p.band) & 1) flat = b0 + min(p.band, p.n_groups - b0) - 1 - (flat - b0);
-  }
+  // the group's rank in the heaviest-first order, in launch bands
+  const uint32_t flat = tiled_rank(blockIdx.x / p.n_kv_heads, p.band, p.n_groups);
   uint32_t lo = 0, hi = p.n_seq;
   while (hi - lo > 1) {
     const uint32_t mid = (lo + hi) / 2;

@@ -173,3 +173,89 @@ def test_split_item_mapping(split_map):
         assert len(is_last) == items and sum(is_last) == last
         flags = [is_last[i] for i in order]
         assert flags == sorted(flags), "whole-span groups first, last groups after"
+
+
+# Tiled prefill / verify launches: the launch-band order of tile groups and
+# the even cut of a tile group's keys into chunks (both used on the device
+# through the same header).
+TILED_DRIVER = r"""
+#include <cstdio>
+#include "slot_kv_internal.h"
+using namespace slotkv;
+int main() {
+  char what;
+  unsigned a, b, c;
+  while (std::scanf(" %c %u %u %u", &what, &a, &b, &c) == 4) {
+    if (what == 'r') {  // band n_groups (third unused): the order
+      for (unsigned f = 0; f < b; ++f) std::printf("%u ", tiled_rank(f, a, b));
+    } else {            // n_keys n_ck split_keys: the chunk length
+      std::printf("%u", group_chunk_keys(a, b, c));
+    }
+    std::printf("\n");
+  }
+  return 0;
+}
+"""
+
+
+@pytest.fixture(scope="module")
+def tiled(tmp_path_factory):
+    d = tmp_path_factory.mktemp("tiled")
+    src = d / "tiled.cpp"
+    src.write_text(TILED_DRIVER)
+    exe = d / "tiled"
+    subprocess.run(["g++", "-O1", "-std=c++17", "-I", INCLUDE, "-I", CSRC, str(src), "-o", str(exe)],
+                   check=True, capture_output=True)
+
+    def run(queries):
+        inp = "".join(f"{q[0]} {q[1]} {q[2]} {q[3]}\n" for q in queries)
+        r = subprocess.run([str(exe)], input=inp, capture_output=True, text=True, check=True)
+        return [list(map(int, ln.split())) for ln in r.stdout.strip("\n").split("\n")]
+    return run
+
+
+def test_tiled_rank_bands(tiled):
+    cases = [(0, 37), (1, 9), (32, 32), (32, 100), (32, 64), (32, 65), (256, 1000), (7, 3)]
+    outs = tiled([("r", band, n, 0) for band, n in cases])
+    for (band, n), order in zip(cases, outs):
+        assert sorted(order) == list(range(n)), "a permutation"
+        if band == 0:
+            assert order == list(range(n))
+            continue
+        for b0 in range(0, n, band):
+            seg = list(range(b0, min(b0 + band, n)))
+            want = seg[::-1] if (b0 // band) % 2 else seg
+            assert order[b0:b0 + band] == want
+
+
+def test_group_chunk_cut(tiled):
+    """Each tile group's n_ck chunks tile its keys in whole 16-key blocks,
+    every chunk the merge reads for any tile of the group is one the
+    attention kernel wrote, and no chunk exceeds the sequence's own chunk."""
+    rng = np.random.default_rng(5)
+    cases = []
+    for sk in (256, 1024):
+        for _ in range(150):
+            seq_keys = int(rng.integers(1, 20000))
+            n_keys = int(rng.integers(1, seq_keys + 1))  # a tile group's keys
+            cases.append((n_keys, (seq_keys + sk - 1) // sk, sk))
+    cases += [(1, 1, 256), (16, 1, 256), (17, 2, 256), (256, 1, 256), (257, 2, 256),
+              (3584, 4, 1024), (3073, 4, 1024)]
+    outs = tiled([("c", *c) for c in cases])
+    for (n_keys, n_ck, sk), (ln,) in zip(cases, outs):
+        assert ln % 16 == 0 and ln > 0
+        assert ln <= ((sk + 15) // 16) * 16 or n_ck * sk < n_keys
+        # the kernel's chunks: [c*ln, min((c+1)*ln, n_keys)) for c < n_ck, empty past n_keys
+        covered = 0
+        for c in range(n_ck):
+            lo, hi = c * ln, min((c + 1) * ln, n_keys)
+            if lo >= n_keys:
+                continue
+            assert lo == covered
+            covered = hi
+        assert covered == n_keys, "every key in exactly one chunk"
+        # the merge of a tile with t_keys <= n_keys reads ceil(t_keys / ln) chunks,
+        # each one the kernel wrote (start below n_keys, index below n_ck)
+        for t_keys in {1, n_keys, max(1, n_keys // 2), max(1, n_keys - 15)}:
+            nck = (t_keys + ln - 1) // ln
+            assert nck <= n_ck and (nck - 1) * ln < n_keys
