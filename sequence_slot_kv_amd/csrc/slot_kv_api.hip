@@ -777,14 +777,7 @@ int run_prefill(slot_kv* h, uint32_t layer, const float* q, const float* k_new,
                  (split ? slotkv::split_groups(keys, ck) : (keys + ck - 1) / ck) * L.n_kv_heads;
     }
     a.s.item_off[n] = items;
-    if (split) {  // each (sequence, kv head, tile) has one last group
-      uint32_t last = 0;
-      for (uint32_t i = 0; i < n; ++i) {
-        a.s.grp_off[i] = last;
-        last += (a.s.len[i] * G + 15) / 16 * L.n_kv_heads;
-      }
-      a.s.grp_off[n] = last;
-    }
+    if (split) slotkv::order_split_groups(a.s, n, G, L.n_kv_heads, ck);
     p.part = ck ? h->part + size_t(pl.rows) * qd : nullptr;
     p.n_items = items;
     p.split_keys = ck;
@@ -793,7 +786,7 @@ int run_prefill(slot_kv* h, uint32_t layer, const float* q, const float* k_new,
     if (!split) {  // tiled workgroups, heaviest sequence first
       std::vector<uint64_t> work(n);
       for (uint32_t i = 0; i < n; ++i) {
-        a.s.by_work[i] = i;
+        a.s.by_work[i] = static_cast<uint8_t>(i);
         work[i] = static_cast<uint64_t>(a.s.len[i]) * (2ull * a.s.pos0[i] + a.s.len[i]);
       }
       std::stable_sort(a.s.by_work, a.s.by_work + n,

@@ -252,11 +252,14 @@ struct PrefillSeqs {
   uint32_t pos0[kMaxSeqPerLaunch];
   uint32_t len[kMaxSeqPerLaunch];
   uint32_t row_off[kMaxSeqPerLaunch + 1];  // first row of each sequence (and the total)
-  uint32_t by_work[kMaxSeqPerLaunch];      // tiled: the sequences, most attention work first
   uint32_t grp_off[kMaxSeqPerLaunch + 1];  // tiled: first workgroup of by_work[k] (per kv head);
                                            // split-K: the last-group items of sequences before i
   uint32_t item_off[kMaxSeqPerLaunch + 1]; // key-chunked: first partial item of each sequence
+  uint32_t last_off[kMaxSeqPerLaunch + 1]; // split-K: the last-group items of by_work[0..k)
+  uint8_t by_work[kMaxSeqPerLaunch];       // tiled: the sequences, most attention work first;
+                                           // split-K: longest last group first
 };
+static_assert(kMaxSeqPerLaunch <= 256, "by_work holds sequence indices in bytes");
 
 struct PrefillArgs {
   PrefillParams p;
@@ -318,29 +321,69 @@ SLOTKV_HD inline uint32_t split_groups(uint32_t keys, uint32_t split_keys) {
 
 // Split-K launches: the partial item that workgroup `block` (< n_items)
 // computes.  Items stay sequence-major, (kv head, tile) then group, but the
-// workgroups take every group of whole chunk spans first and each tile's last
-// group after them; seqs.grp_off[i] counts the last groups of the sequences
-// before i.
+// workgroups take every group of whole chunk spans first, in sequence order,
+// and each tile's last group after them, the sequences of longer last groups
+// first (seqs.by_work), so that the end of the grid holds the shortest work;
+// seqs.grp_off[i] counts the last groups of the sequences before i, and
+// seqs.last_off[k] those of by_work[0..k).
 SLOTKV_HD inline uint32_t split_item_of_block(const PrefillSeqs& seqs, uint32_t n_seq,
                                               uint32_t n_items, uint32_t split_keys,
                                               uint32_t block) {
   const uint32_t n_whole = n_items - seqs.grp_off[n_seq];
-  const bool whole = block < n_whole;
-  const uint32_t f = whole ? block : block - n_whole;
-  // the sequence: the last i whose first such item is <= f
-  uint32_t lo = 0, hi = n_seq;
-  while (hi - lo > 1) {
-    const uint32_t mid = (lo + hi) / 2;
-    const uint32_t first = whole ? seqs.item_off[mid] - seqs.grp_off[mid] : seqs.grp_off[mid];
-    if (first <= f) lo = mid; else hi = mid;
-  }
-  const uint32_t ng = split_groups(seqs.pos0[lo] + seqs.len[lo], split_keys);
-  if (whole) {
-    const uint32_t r = f - (seqs.item_off[lo] - seqs.grp_off[lo]);
+  if (block < n_whole) {
+    // the sequence: the last i whose first whole-span item is <= block
+    uint32_t lo = 0, hi = n_seq;
+    while (hi - lo > 1) {
+      const uint32_t mid = (lo + hi) / 2;
+      if (seqs.item_off[mid] - seqs.grp_off[mid] <= block) lo = mid; else hi = mid;
+    }
+    const uint32_t ng = split_groups(seqs.pos0[lo] + seqs.len[lo], split_keys);
+    const uint32_t r = block - (seqs.item_off[lo] - seqs.grp_off[lo]);
     return seqs.item_off[lo] + r / (ng - 1) * ng + r % (ng - 1);
   }
-  return seqs.item_off[lo] + (f - seqs.grp_off[lo]) * ng + ng - 1;
+  // the rank k in by_work: the last k with last_off[k] <= f
+  const uint32_t f = block - n_whole;
+  uint32_t k = 0, hi = n_seq;
+  while (hi - k > 1) {
+    const uint32_t mid = (k + hi) / 2;
+    if (seqs.last_off[mid] <= f) k = mid; else hi = mid;
+  }
+  const uint32_t i = seqs.by_work[k];
+  const uint32_t ng = split_groups(seqs.pos0[i] + seqs.len[i], split_keys);
+  return seqs.item_off[i] + (f - seqs.last_off[k]) * ng + ng - 1;
 }
+// Split-K launches, host side: fills seqs.grp_off, seqs.by_work and
+// seqs.last_off for split_item_of_block from the sequences' pos0 and len
+// (item_off is filled by the caller).  A sequence's last group holds its keys
+// past the whole spans of kSplitChunksPerGroup * split_keys.
+inline void order_split_groups(PrefillSeqs& seqs, uint32_t n_seq, uint32_t G,
+                               uint32_t n_kv_heads, uint32_t split_keys) {
+  uint32_t last_keys[kMaxSeqPerLaunch];
+  uint32_t last = 0;
+  for (uint32_t i = 0; i < n_seq; ++i) {
+    seqs.grp_off[i] = last;
+    last += (seqs.len[i] * G + 15) / 16 * n_kv_heads;
+    const uint32_t keys = seqs.pos0[i] + seqs.len[i];
+    last_keys[i] = keys - (split_groups(keys, split_keys) - 1) * split_keys * kSplitChunksPerGroup;
+    seqs.by_work[i] = static_cast<uint8_t>(i);
+  }
+  seqs.grp_off[n_seq] = last;
+  // stable insertion sort, longest last group first (n_seq <= kMaxSeqPerLaunch)
+  for (uint32_t k = 1; k < n_seq; ++k) {
+    const uint8_t v = seqs.by_work[k];
+    uint32_t m = k;
+    for (; m > 0 && last_keys[seqs.by_work[m - 1]] < last_keys[v]; --m)
+      seqs.by_work[m] = seqs.by_work[m - 1];
+    seqs.by_work[m] = v;
+  }
+  last = 0;
+  for (uint32_t k = 0; k < n_seq; ++k) {
+    seqs.last_off[k] = last;
+    last += (seqs.len[seqs.by_work[k]] * G + 15) / 16 * n_kv_heads;
+  }
+  seqs.last_off[n_seq] = last;
+}
+
 #ifndef SLOT_KV_SPLIT_MIN_KEYS
 #define SLOT_KV_SPLIT_MIN_KEYS 256
 #endif

@@ -117,18 +117,16 @@ int main() {
   unsigned n, G, hkv, sk;
   if (std::scanf("%u %u %u %u", &n, &G, &hkv, &sk) != 4 || n > kMaxSeqPerLaunch) return 2;
   static PrefillSeqs s;
-  uint32_t items = 0, last = 0;
+  uint32_t items = 0;
   for (unsigned i = 0; i < n; ++i) {
     if (std::scanf("%u %u", &s.pos0[i], &s.len[i]) != 2) return 2;
     const uint32_t tiles = (s.len[i] * G + 15) / 16;
     s.item_off[i] = items;
-    s.grp_off[i] = last;
     items += tiles * split_groups(s.pos0[i] + s.len[i], sk) * hkv;
-    last += tiles * hkv;
   }
   s.item_off[n] = items;
-  s.grp_off[n] = last;
-  std::printf("%u %u\n", items, last);
+  order_split_groups(s, n, G, hkv, sk);
+  std::printf("%u %u\n", items, s.grp_off[n]);
   for (uint32_t b = 0; b < items; ++b) std::printf("%u\n", split_item_of_block(s, n, items, sk, b));
   return 0;
 }
@@ -164,15 +162,25 @@ def test_split_item_mapping(split_map):
                 for _ in range(int(rng.integers(1, 129)))]
         items, last, order = split_map(seqs, G, hkv, sk)
         assert sorted(order) == list(range(items)), "a bijection onto the items"
-        # which items are a tile's last group
-        is_last = []
-        for p0, t in seqs:
+        # which items are a tile's last group, and the keys of each group
+        is_last, gkeys, seq_of = [], [], []
+        for s, (p0, t) in enumerate(seqs):
             ng = _groups(p0 + t, sk)
             for _ in range((t * G + 15) // 16 * hkv):
                 is_last += [g == ng - 1 for g in range(ng)]
+                gkeys += [min(p0 + t - g * 4 * sk, 4 * sk) for g in range(ng)]
+                seq_of += [s] * ng
         assert len(is_last) == items and sum(is_last) == last
         flags = [is_last[i] for i in order]
         assert flags == sorted(flags), "whole-span groups first, last groups after"
+        whole = [i for i in order if not is_last[i]]
+        assert whole == sorted(whole), "whole-span groups in item order"
+        tail = [i for i in order if is_last[i]]
+        keys = [gkeys[i] for i in tail]
+        assert keys == sorted(keys, reverse=True), "longest last group first"
+        # ties keep sequence order, and a sequence's last groups stay in item order
+        ranked = [(-gkeys[i], seq_of[i], i) for i in tail]
+        assert ranked == sorted(ranked)
 
 
 # Tiled prefill / verify launches: the launch-band order of tile groups and
