@@ -406,19 +406,20 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) prefill_attn_kernel(const 
 }
 
 // Split-K attention for sequences with few query rows per kv head (a verify
-// of k rows, a short prefill).  Every wave is one work item: a 16-row tile of
-// one sequence and kv head j against one chunk of split_keys keys, loaded
-// straight from the cache into registers (no other wave needs them), with the
-// next 16-key block in flight while the current one is multiplied.  The
-// MFMA forms are those of prefill_attn_kernel, except that the head_dim
+// of k rows, a short prefill).  Every wave takes a 16-row tile of one
+// sequence and kv head j against a range of keys (its share of the
+// workgroup's group, below), loaded straight from the cache into registers
+// (no other wave needs them), with the next 16-key block in flight while the
+// current one is multiplied.  The MFMA forms are those of prefill_attn_kernel,
+// except that the head_dim
 // order of the score product is permuted so that each K load instruction
 // reads 64 contiguous bytes per row: lane (c, g) multiplies
 // d = 16v + 4g + e at MFMA (v, e), for K row c and for its query row c.
-// The four waves of a workgroup take four consecutive chunks of the same
-// (sequence, kv head, tile) and combine their results through LDS, so that
-// one unnormalised partial per workgroup (per row: running max m in log2
-// units, sum l, and acc[D]) goes to memory; split_merge_kernel combines the
-// partials of a row.
+// The four waves of a workgroup take a group of four chunks of the same
+// (sequence, kv head, tile), its keys cut evenly between them in 16-key
+// blocks, and combine their results through LDS, so that one unnormalised
+// partial per workgroup (per row: running max m in log2 units, sum l, and
+// acc[D]) goes to memory; split_merge_kernel combines the partials of a row.
 // Two waves per SIMD where the registers allow it without spilling (head_dim
 // up to 128); head_dim 256 takes the whole register file.
 template <int D>
@@ -458,8 +459,9 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_eu<D>()))) split_attn_kernel(
   const uint32_t lane = threadIdx.x % kWave;
   const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const uint32_t g = lane / 16, c = lane % 16;
-  // workgroup -> (sequence, kv head j, tile, chunk group); wave w takes chunk
-  // 4 * group + w.  All of it is uniform: scalar registers, uniform loops.
+  // workgroup -> (sequence, kv head j, tile, chunk group); wave w takes the
+  // w-th share of the group's keys.  All of it is uniform: scalar registers,
+  // uniform loops.
   // Workgroups run the groups of whole chunk spans first and every tile's
   // last (shorter) group after them, so the end of the grid holds short work.
   if (blockIdx.x >= p.n_items) return;  // workgroup-uniform, before any barrier
@@ -479,9 +481,14 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_eu<D>()))) split_attn_kernel(
   const uint32_t tile = ut % n_tiles;
   const uint32_t j = ut / n_tiles;
   const uint32_t tile_keys = pos0 + min((tile * 16 + 15) / G, T - 1) + 1;
-  const uint32_t k0 = (grp * kSplitWaves + w) * p.split_keys;
-  const bool active = k0 < tile_keys;  // wave-uniform: else nothing of this tile here
-  const uint32_t k1 = active ? min(k0 + p.split_keys, tile_keys) : k0 + 1;
+  // the group's keys [g_lo, g_hi) of this tile, cut evenly over the waves
+  // in whole 16-key blocks (a short last group keeps every wave streaming)
+  const uint32_t g_lo = grp * kSplitWaves * p.split_keys;
+  const uint32_t g_hi = max(g_lo, min(g_lo + kSplitWaves * p.split_keys, tile_keys));
+  const uint32_t per = ((g_hi - g_lo + 15) / 16 + kSplitWaves - 1) / kSplitWaves * 16;
+  const uint32_t k0 = g_lo + w * per;
+  const bool active = k0 < g_hi;  // wave-uniform: else nothing of this tile here
+  const uint32_t k1 = active ? min(k0 + per, g_hi) : k0 + 1;
   const uint32_t n_blk = active ? (k1 - k0 + 15) / 16 : 0;
   const uint32_t R = tile * 16 + c;
   const uint32_t t = R / G, h = j * G + R % G;
