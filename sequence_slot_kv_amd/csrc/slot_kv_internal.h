@@ -35,6 +35,20 @@ static_assert(offsetof(LaunchRows, tail_row) % 4 == 0, "tail_row is read through
 #define SLOTKV_HD
 #endif
 
+// The last index i in [0, n) with key(i) <= x, for key non-decreasing over
+// [0, n) and key(0) <= x (n >= 1), by halving.  (Probing 15 indices per round
+// instead, two rounds for 256 entries, measured slower in every kernel: the
+// extra scalar loads cost more than the shorter chain saves.)
+template <class Key>
+SLOTKV_HD inline uint32_t last_le(uint32_t n, uint32_t x, Key key) {
+  uint32_t lo = 0, hi = n;
+  while (hi - lo > 1) {
+    const uint32_t mid = (lo + hi) / 2;
+    if (key(mid) <= x) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
 // Byte k of a row table, through its aligned word (on the device the read
 // stays a scalar load).
 SLOTKV_HD inline uint32_t row_byte(const uint8_t* table, uint32_t k) {
@@ -48,13 +62,9 @@ SLOTKV_HD inline void locate_item(const LaunchRows& rows, uint32_t n_rows, uint3
                                   uint32_t* chunk_index) {
   if (item < n_full) {
     // full chunk: the last row whose first full chunk is <= item
-    uint32_t blo = 0, bhi = n_rows;
-    while (bhi - blo > 1) {
-      const uint32_t mid = (blo + bhi) / 2;
-      if (rows.full_prefix[mid] <= item) blo = mid; else bhi = mid;
-    }
-    *row = blo;
-    *chunk_index = item - rows.full_prefix[blo];
+    const uint32_t b = last_le(n_rows, item, [&](uint32_t i) { return rows.full_prefix[i]; });
+    *row = b;
+    *chunk_index = item - rows.full_prefix[b];
   } else {
     *row = row_byte(rows.tail_row, item - n_full);
     *chunk_index = rows.pos[*row] / chunk;  // the partial last chunk
@@ -320,37 +330,34 @@ SLOTKV_HD inline uint32_t split_groups(uint32_t keys, uint32_t split_keys) {
 }
 
 // Split-K launches: the partial item that workgroup `block` (< n_items)
-// computes.  Items stay sequence-major, (kv head, tile) then group, but the
+// computes, and its sequence.  Items stay sequence-major, (kv head, tile) then group, but the
 // workgroups take every group of whole chunk spans first, in sequence order,
 // and each tile's last group after them, the sequences of longer last groups
 // first (seqs.by_work), so that the end of the grid holds the shortest work;
 // seqs.grp_off[i] counts the last groups of the sequences before i, and
 // seqs.last_off[k] those of by_work[0..k).
-SLOTKV_HD inline uint32_t split_item_of_block(const PrefillSeqs& seqs, uint32_t n_seq,
-                                              uint32_t n_items, uint32_t split_keys,
-                                              uint32_t block) {
+struct SplitItem {
+  uint32_t item, seq;
+};
+SLOTKV_HD inline SplitItem split_item_of_block(const PrefillSeqs& seqs, uint32_t n_seq,
+                                               uint32_t n_items, uint32_t split_keys,
+                                               uint32_t block) {
   const uint32_t n_whole = n_items - seqs.grp_off[n_seq];
   if (block < n_whole) {
     // the sequence: the last i whose first whole-span item is <= block
-    uint32_t lo = 0, hi = n_seq;
-    while (hi - lo > 1) {
-      const uint32_t mid = (lo + hi) / 2;
-      if (seqs.item_off[mid] - seqs.grp_off[mid] <= block) lo = mid; else hi = mid;
-    }
+    const uint32_t lo = last_le(n_seq, block, [&](uint32_t i) {
+      return seqs.item_off[i] - seqs.grp_off[i];
+    });
     const uint32_t ng = split_groups(seqs.pos0[lo] + seqs.len[lo], split_keys);
     const uint32_t r = block - (seqs.item_off[lo] - seqs.grp_off[lo]);
-    return seqs.item_off[lo] + r / (ng - 1) * ng + r % (ng - 1);
+    return {seqs.item_off[lo] + r / (ng - 1) * ng + r % (ng - 1), lo};
   }
   // the rank k in by_work: the last k with last_off[k] <= f
   const uint32_t f = block - n_whole;
-  uint32_t k = 0, hi = n_seq;
-  while (hi - k > 1) {
-    const uint32_t mid = (k + hi) / 2;
-    if (seqs.last_off[mid] <= f) k = mid; else hi = mid;
-  }
+  const uint32_t k = last_le(n_seq, f, [&](uint32_t r) { return seqs.last_off[r]; });
   const uint32_t i = seqs.by_work[k];
   const uint32_t ng = split_groups(seqs.pos0[i] + seqs.len[i], split_keys);
-  return seqs.item_off[i] + (f - seqs.last_off[k]) * ng + ng - 1;
+  return {seqs.item_off[i] + (f - seqs.last_off[k]) * ng + ng - 1, i};
 }
 // Split-K launches, host side: fills seqs.grp_off, seqs.by_work and
 // seqs.last_off for split_item_of_block from the sequences' pos0 and len

@@ -44,12 +44,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // The sequence holding launch row `row`: the last i with row_off[i] <= row.
 __device__ __forceinline__ uint32_t seq_of_row(const PrefillArgs& a, uint32_t row) {
-  uint32_t lo = 0, hi = a.p.n_seq;
-  while (hi - lo > 1) {
-    const uint32_t mid = (lo + hi) / 2;
-    if (a.s.row_off[mid] <= row) lo = mid; else hi = mid;
-  }
-  return lo;
+  return last_le(a.p.n_seq, row, [&](uint32_t i) { return a.s.row_off[i]; });
 }
 
 // A workgroup takes 4 * prep_vpw head vectors of a token row (the row's
@@ -197,11 +192,7 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) prefill_attn_kernel(const 
   const uint32_t j = blockIdx.x % p.n_kv_heads;
   // the group's rank in the heaviest-first order, in launch bands
   const uint32_t flat = tiled_rank(blockIdx.x / p.n_kv_heads, p.band, p.n_groups);
-  uint32_t lo = 0, hi = p.n_seq;
-  while (hi - lo > 1) {
-    const uint32_t mid = (lo + hi) / 2;
-    if (a.s.grp_off[mid] <= flat) lo = mid; else hi = mid;
-  }
+  const uint32_t lo = last_le(p.n_seq, flat, [&](uint32_t k) { return a.s.grp_off[k]; });
   const uint32_t sq = a.s.by_work[lo];
   const uint32_t T = a.s.len[sq], pos0 = a.s.pos0[sq], row0 = a.s.row_off[sq];
   const uint32_t n_ck = CK ? (pos0 + T + CK - 1) / CK : 1;
@@ -465,13 +456,8 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_eu<D>()))) split_attn_kernel(
   // Workgroups run the groups of whole chunk spans first and every tile's
   // last (shorter) group after them, so the end of the grid holds short work.
   if (blockIdx.x >= p.n_items) return;  // workgroup-uniform, before any barrier
-  const uint32_t item = split_item_of_block(a.s, p.n_seq, p.n_items, p.split_keys, blockIdx.x);
-  uint32_t lo = 0, hi = p.n_seq;  // the sequence: last i with item_off[i] <= item
-  while (hi - lo > 1) {
-    const uint32_t mid = (lo + hi) / 2;
-    if (a.s.item_off[mid] <= item) lo = mid; else hi = mid;
-  }
-  const uint32_t sq = lo;
+  const SplitItem si = split_item_of_block(a.s, p.n_seq, p.n_items, p.split_keys, blockIdx.x);
+  const uint32_t item = si.item, sq = si.seq;
   const uint32_t T = a.s.len[sq], pos0 = a.s.pos0[sq], row0 = a.s.row_off[sq];
   const uint32_t n_tiles = (T * G + 15) / 16;
   const uint32_t n_grp = split_groups(pos0 + T, p.split_keys);

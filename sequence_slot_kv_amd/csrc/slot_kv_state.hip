@@ -32,11 +32,7 @@ __global__ __launch_bounds__(kResetThreads) void state_reset_kernel(ResetArgs a)
   const uint32_t t = blockIdx.x / a.n;
   const uint32_t i = blockIdx.x - t * a.n;
   // the segment holding tile t: the last k with segs[k].tile0 <= t
-  uint32_t lo = 0, hi = a.n_seg;
-  while (hi - lo > 1) {
-    const uint32_t mid = (lo + hi) / 2;
-    if (a.segs[mid].tile0 <= t) lo = mid; else hi = mid;
-  }
+  const uint32_t lo = last_le(a.n_seg, t, [&](uint32_t k) { return a.segs[k].tile0; });
   const StateSeg seg = a.segs[lo];
   // byte addresses of the slot's region [r0, r1) and of the tile's first unit
   const uint64_t r0 = reinterpret_cast<uintptr_t>(seg.base) + uint64_t(a.slots[i]) * seg.len * 4;

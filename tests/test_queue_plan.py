@@ -127,7 +127,12 @@ int main() {
   s.item_off[n] = items;
   order_split_groups(s, n, G, hkv, sk);
   std::printf("%u %u\n", items, s.grp_off[n]);
-  for (uint32_t b = 0; b < items; ++b) std::printf("%u\n", split_item_of_block(s, n, items, sk, b));
+  for (uint32_t b = 0; b < items; ++b) {
+    const SplitItem si = split_item_of_block(s, n, items, sk, b);
+    // the sequence returned is the one whose items hold the item
+    if (si.seq >= n || si.item < s.item_off[si.seq] || si.item >= s.item_off[si.seq + 1]) return 3;
+    std::printf("%u\n", si.item);
+  }
   return 0;
 }
 """
@@ -267,3 +272,45 @@ def test_group_chunk_cut(tiled):
         for t_keys in {1, n_keys, max(1, n_keys // 2), max(1, n_keys - 15)}:
             nck = (t_keys + ln - 1) // ln
             assert nck <= n_ck and (nck - 1) * ln < n_keys
+
+
+# The kernels' table lookups (row of a queue item, sequence of a launch row or
+# workgroup, segment of a reset tile) all go through last_le: the last index
+# whose non-decreasing key is <= x.
+SEARCH_DRIVER = r"""
+#include <cstdio>
+#include <vector>
+#include "slot_kv_internal.h"
+int main() {
+  unsigned n, x;
+  while (std::scanf("%u %u", &n, &x) == 2) {
+    std::vector<uint32_t> v(n);
+    for (unsigned i = 0; i < n; ++i) if (std::scanf("%u", &v[i]) != 1) return 2;
+    std::printf("%u\n", slotkv::last_le(n, x, [&](uint32_t i) { return v[i]; }));
+  }
+  return 0;
+}
+"""
+
+
+def test_last_le_matches_brute_force(tmp_path):
+    src = tmp_path / "search.cpp"
+    src.write_text(SEARCH_DRIVER)
+    exe = tmp_path / "search"
+    subprocess.run(["g++", "-O1", "-std=c++17", "-fsanitize=address,undefined", "-I", INCLUDE,
+                    "-I", CSRC, str(src), "-o", str(exe)], check=True, capture_output=True)
+    rng = np.random.default_rng(17)
+    cases = []
+    for n in list(range(1, 40)) + [63, 64, 65, 127, 128, 129, 255, 256, 257, 300]:
+        for _ in range(6):
+            # non-decreasing keys from 0 with plateaus (empty sequences, zero-length rows)
+            steps = rng.integers(0, 4, n) * (rng.random(n) < 0.7)
+            keys = np.concatenate([[0], np.cumsum(steps[1:])]).astype(np.int64)
+            for x in {0, int(keys[-1]), int(keys[-1]) + 5, int(rng.integers(0, keys[-1] + 2)),
+                      int(keys[n // 2])}:
+                cases.append((keys, x))
+    inp = "".join(f"{len(k)} {x} " + " ".join(map(str, k.tolist())) + "\n" for k, x in cases)
+    r = subprocess.run([str(exe)], input=inp, capture_output=True, text=True, check=True)
+    got = list(map(int, r.stdout.split()))
+    want = [int(np.nonzero(k <= x)[0].max()) for k, x in cases]
+    assert got == want
