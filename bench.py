@@ -52,6 +52,7 @@ from __future__ import annotations
 
 import argparse
 import concurrent.futures as cf
+import gc
 import hashlib
 import json
 import os
@@ -79,6 +80,16 @@ INTERNAL_H = os.path.join(CSRC, "slot_kv_internal.h")
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_counters.json")
 TRACE_RECORD = os.path.join(ROOT, "profiles", "kernel_trace.json")
 
+
+
+def gc_off():
+    """Warm-up and timed passes run with Python's cyclic collector off, after
+    one full collection: a collection of the interpreter's objects (tens of
+    milliseconds with torch loaded) landing in the timed region would stall
+    the launch loop, and when it lands depends on everything allocated
+    before.  The caller turns it back on after its last timed pass."""
+    gc.collect()
+    gc.disable()
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -256,20 +267,6 @@ def decode_bench(args, w, b):
     torch.cuda.synchronize()
     log("[bench] history filled")
 
-    hist, cpu_rows_, sampled = None, None, False
-    if not args.no_cpu_baseline:  # snapshot the timed rows' history before any step runs
-        cpu_rows_, sampled = cpu_rows(w)
-        hist = {}
-        for bi in cpu_rows_:
-            p = int(w.positions[bi])
-            for l, P in enumerate(w.layers):
-                if p == 0:
-                    z = np.zeros((0, P.kv_dim), np.float32)
-                    hist[(bi, l)] = (z, z)
-                else:
-                    k, v = kv.read_rows(l, int(w.slots[bi]), 0, p)
-                    hist[(bi, l)] = (k.cpu().numpy(), v.cpu().numpy())
-
     ins = [tuple(torch.from_numpy(a).cuda() for a in (li.q, li.k_new, li.v_new)) for li in w.inputs]
     outs = [torch.empty_like(x[0]) for x in ins]
     positions, slots = w.positions, w.slots
@@ -280,6 +277,7 @@ def decode_bench(args, w, b):
             q, kn, vn = ins[l]
             kv.decode_attn(l, q, kn, vn, positions, slots, out=outs[l], stream=stream)
 
+    gc_off()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -343,8 +341,24 @@ def decode_bench(args, w, b):
         f"{pair_ms / n_launch * 1e3:.1f} us; {cold_launch_ms * 1e3:.1f} us/launch with caches "
         f"flushed; rocprofv3 record {prof_us}")
 
+    gc.enable()
     cpu = None
-    if hist is not None:
+    if not args.no_cpu_baseline:
+        # the oracle's rows and their history, copied to the host only now:
+        # a step writes row pos of each row's slot and never rows 0..pos-1,
+        # and host work of this size before the timed region has slowed the
+        # launch loop that follows it
+        cpu_rows_, sampled = cpu_rows(w)
+        hist = {}
+        for bi in cpu_rows_:
+            p = int(w.positions[bi])
+            for l, P in enumerate(w.layers):
+                if p == 0:
+                    z = np.zeros((0, P.kv_dim), np.float32)
+                    hist[(bi, l)] = (z, z)
+                else:
+                    k, v = kv.read_rows(l, int(w.slots[bi]), 0, p)
+                    hist[(bi, l)] = (k.cpu().numpy(), v.cpu().numpy())
         log("[bench] timing the CPU oracle")
         cpu = cpu_baseline(w, cpu_rows_, sampled, hist)
 
@@ -389,6 +403,7 @@ def prefill_bench(args, w, b):
     kv.alloc(w.n_slots, w.slot_ctx, [L.kv_dim])
     kv.set_layer(0, L)
     hist_k = hist_v = np.zeros((0, L.kv_dim), np.float32)
+    hist_dev = None  # copied to the host after the timed passes
     if w.pos0:
         g = torch.Generator(device="cuda")
         g.manual_seed(77 + w.seed)
@@ -396,13 +411,14 @@ def prefill_bench(args, w, b):
         hv = torch.randn((w.pos0, L.kv_dim), generator=g, device="cuda")
         kv.write_rows(0, w.slot, 0, hk, hv)
         if not args.no_cpu_baseline:
-            hist_k, hist_v = hk.cpu().numpy(), hv.cpu().numpy()
+            hist_dev = (hk, hv)
     q, kn, vn = (torch.from_numpy(x).cuda() for x in (li.q, li.k_new, li.v_new))
     out = torch.empty_like(q)
 
     def step():
         kv.prefill_attn(0, q, kn, vn, w.slot, w.pos0, out=out)
 
+    gc_off()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -423,7 +439,10 @@ def prefill_bench(args, w, b):
     tflops = w.attn_flops() / (attn_us * 1e-6) / 1e12
     log(f"[bench] {ms_per_step * 1e3:.1f} us/step, attention kernel {attn_us:.1f} us, "
         f"{tflops:.1f} TFLOP/s")
+    if hist_dev is not None:
+        hist_k, hist_v = (x.cpu().numpy() for x in hist_dev)
 
+    gc.enable()
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -474,19 +493,20 @@ def verify_bench(args, w, b):
     kv.set_layer(0, L)
     g = torch.Generator(device="cuda")
     g.manual_seed(99)
-    hist = {}
+    hist = {}  # per slot, on the device until the timed passes are over
     for s, p0 in zip(w.slots.tolist(), w.pos0.tolist()):
         hk = torch.randn((p0, L.kv_dim), generator=g, device="cuda")
         hv = torch.randn((p0, L.kv_dim), generator=g, device="cuda")
         kv.write_rows(0, s, 0, hk, hv)
         if not args.no_cpu_baseline:
-            hist[s] = (hk.cpu().numpy(), hv.cpu().numpy())
+            hist[s] = (hk, hv)
     q, kn, vn = (torch.from_numpy(x).cuda() for x in (li.q, li.k_new, li.v_new))
     out = torch.empty_like(q)
 
     def step():
         kv.verify_attn(0, q, kn, vn, w.slots, w.pos0, w.ks, out=out)
 
+    gc_off()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -507,6 +527,8 @@ def verify_bench(args, w, b):
     achieved = w.kv_bytes() / (attn_us * 1e-6) / 1e9
     log(f"[bench] {ms_per_step * 1e3:.1f} us/step, attention kernel {attn_us:.1f} us, "
         f"{achieved:.0f} GB/s")
+    hist = {s: (hk.cpu().numpy(), hv.cpu().numpy()) for s, (hk, hv) in hist.items()}
+    gc.enable()
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -567,6 +589,7 @@ def state_bench(args, w, b):
     def step():
         kv.reset_batch(w.slots)
 
+    gc_off()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -588,6 +611,7 @@ def state_bench(args, w, b):
     log(f"[bench] {ms_per_step * 1e3:.1f} us/step, reset kernel {k_us:.1f} us, "
         f"{achieved:.0f} GB/s")
     kv.close()
+    gc.enable()
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
