@@ -324,6 +324,23 @@ constexpr uint32_t kSplitMaxRows = 64;
 #define SLOT_KV_SPLIT_GROUP 4
 #endif
 constexpr uint32_t kSplitChunksPerGroup = SLOT_KV_SPLIT_GROUP;
+// Split-K launches: wave w's share [k0, k1) of a group's keys [g_lo, g_hi)
+// (g_hi >= g_lo), cut evenly over the kSplitChunksPerGroup waves in whole
+// 16-key blocks, and its block count; a wave past the keys gets k1 = k0 + 1
+// and no block.
+struct WaveShare {
+  uint32_t k0, k1, n_blk;
+};
+SLOTKV_HD inline WaveShare split_wave_share(uint32_t g_lo, uint32_t g_hi, uint32_t w) {
+  const uint32_t per =
+      ((g_hi - g_lo + 15) / 16 + kSplitChunksPerGroup - 1) / kSplitChunksPerGroup * 16;
+  WaveShare s;
+  s.k0 = g_lo + w * per;
+  const bool active = s.k0 < g_hi;
+  s.k1 = active ? (s.k0 + per < g_hi ? s.k0 + per : g_hi) : s.k0 + 1;
+  s.n_blk = active ? (s.k1 - s.k0 + 15) / 16 : 0;
+  return s;
+}
 SLOTKV_HD inline uint32_t split_groups(uint32_t keys, uint32_t split_keys) {
   const uint32_t chunks = (keys + split_keys - 1) / split_keys;
   return (chunks + kSplitChunksPerGroup - 1) / kSplitChunksPerGroup;

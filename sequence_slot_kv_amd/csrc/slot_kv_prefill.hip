@@ -471,11 +471,9 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_eu<D>()))) split_attn_kernel(
   // in whole 16-key blocks (a short last group keeps every wave streaming)
   const uint32_t g_lo = grp * kSplitWaves * p.split_keys;
   const uint32_t g_hi = max(g_lo, min(g_lo + kSplitWaves * p.split_keys, tile_keys));
-  const uint32_t per = ((g_hi - g_lo + 15) / 16 + kSplitWaves - 1) / kSplitWaves * 16;
-  const uint32_t k0 = g_lo + w * per;
-  const bool active = k0 < g_hi;  // wave-uniform: else nothing of this tile here
-  const uint32_t k1 = active ? min(k0 + per, g_hi) : k0 + 1;
-  const uint32_t n_blk = active ? (k1 - k0 + 15) / 16 : 0;
+  const WaveShare ws = split_wave_share(g_lo, g_hi, w);
+  const uint32_t k0 = ws.k0, k1 = ws.k1, n_blk = ws.n_blk;
+  const bool active = n_blk > 0;  // wave-uniform: else nothing of this tile here
   const uint32_t R = tile * 16 + c;
   const uint32_t t = R / G, h = j * G + R % G;
   const uint32_t tq = t < T ? t : T - 1;  // rows past the last token compute on it, unused

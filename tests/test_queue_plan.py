@@ -314,3 +314,59 @@ def test_last_le_matches_brute_force(tmp_path):
     got = list(map(int, r.stdout.split()))
     want = [int(np.nonzero(k <= x)[0].max()) for k, x in cases]
     assert got == want
+
+
+SHARE_DRIVER = r"""
+#include <cstdio>
+#include "slot_kv_internal.h"
+int main() {
+  unsigned lo, hi;
+  while (std::scanf("%u %u", &lo, &hi) == 2) {
+    for (uint32_t w = 0; w < slotkv::kSplitChunksPerGroup; ++w) {
+      const slotkv::WaveShare s = slotkv::split_wave_share(lo, hi, w);
+      std::printf("%u %u %u ", s.k0, s.k1, s.n_blk);
+    }
+    std::printf("\n");
+  }
+  return 0;
+}
+"""
+
+
+def test_split_wave_shares_tile_the_group(tmp_path):
+    """The split-K waves of a workgroup cut its group's keys [lo, hi) evenly:
+    the active waves' ranges tile [lo, hi) in order, each of whole 16-key
+    blocks but the last, every active wave but the last takes the same
+    number of blocks (the last at most that many), and a wave past the keys
+    has none (it issues no load)."""
+    src = tmp_path / "share.cpp"
+    src.write_text(SHARE_DRIVER)
+    exe = tmp_path / "share"
+    subprocess.run(["g++", "-O1", "-std=c++17", "-I", INCLUDE, "-I", CSRC, str(src), "-o", str(exe)],
+                   check=True, capture_output=True)
+    rng = np.random.default_rng(23)
+    groups = [(0, n) for n in range(0, 1100)]
+    groups += [(int(lo) * 1024, int(lo) * 1024 + int(rng.integers(0, 1025))) for lo in rng.integers(0, 40, 400)]
+    inp = "".join(f"{lo} {hi}\n" for lo, hi in groups)
+    r = subprocess.run([str(exe)], input=inp, capture_output=True, text=True, check=True)
+    for (lo, hi), line in zip(groups, r.stdout.strip("\n").split("\n")):
+        v = list(map(int, line.split()))
+        shares = [tuple(v[i:i + 3]) for i in range(0, len(v), 3)]
+        pos, blocks = lo, []
+        for k0, k1, nb in shares:
+            if nb == 0:
+                assert k1 == k0 + 1 and k0 >= hi, (lo, hi, shares)
+                continue
+            assert k0 == pos and k1 > k0 and nb == (k1 - k0 + 15) // 16
+            assert (k0 - lo) % 16 == 0
+            if k1 != hi:
+                assert (k1 - k0) % 16 == 0, (lo, hi, shares)
+            pos = k1
+            blocks.append(nb)
+        assert pos == max(lo, hi), (lo, hi, shares)
+        if blocks:
+            assert len(set(blocks[:-1])) <= 1 and blocks[-1] <= blocks[0], (lo, hi, shares)
+            # even: no more waves idle than a cut of ceil(blocks / waves) each leaves
+            total = -(-(hi - lo) // 16)
+            per = -(-total // len(shares))
+            assert blocks[0] == per and len(blocks) == -(-total // per)
