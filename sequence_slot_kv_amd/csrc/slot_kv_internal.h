@@ -21,13 +21,19 @@ constexpr uint32_t kMaxRowsPerLaunch = 256;
 
 // The launch's work items are the (row, chunk) pairs: first every full chunk
 // (row-major), then each row's shorter last chunk, longest first.
+// The first kFirstItems full-chunk items also have their row listed, so that
+// a workgroup finds its first unit (and any unit among them) with one load
+// instead of a halving search.
+constexpr uint32_t kFirstItems = 256;
 struct LaunchRows {
   uint32_t pos[kMaxRowsPerLaunch];    // position written and attended up to (inclusive)
   uint32_t slot[kMaxRowsPerLaunch];   // slot index
   uint32_t full_prefix[kMaxRowsPerLaunch + 1];  // full chunks of the rows before b
   uint8_t tail_row[kMaxRowsPerLaunch];          // rows owning a partial chunk, longest first
+  uint8_t first_row[kFirstItems];               // row of full-chunk item i < kFirstItems
 };
 static_assert(offsetof(LaunchRows, tail_row) % 4 == 0, "tail_row is read through 32-bit words");
+static_assert(offsetof(LaunchRows, first_row) % 4 == 0, "first_row is read through 32-bit words");
 
 #if defined(__HIPCC__)
 #define SLOTKV_HD __host__ __device__
@@ -62,7 +68,9 @@ SLOTKV_HD inline void locate_item(const LaunchRows& rows, uint32_t n_rows, uint3
                                   uint32_t* chunk_index) {
   if (item < n_full) {
     // full chunk: the last row whose first full chunk is <= item
-    const uint32_t b = last_le(n_rows, item, [&](uint32_t i) { return rows.full_prefix[i]; });
+    const uint32_t b = item < kFirstItems
+                           ? row_byte(rows.first_row, item)
+                           : last_le(n_rows, item, [&](uint32_t i) { return rows.full_prefix[i]; });
     *row = b;
     *chunk_index = item - rows.full_prefix[b];
   } else {

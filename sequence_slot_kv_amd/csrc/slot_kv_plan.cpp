@@ -58,6 +58,8 @@ LaunchWork fill_rows(LaunchRows& rows, const uint32_t* positions, const uint32_t
     rows.pos[b] = positions[b];
     rows.slot[b] = slots[b];
     rows.full_prefix[b] = work.n_full;
+    for (uint32_t i = work.n_full; i < std::min(work.n_full + keys / chunk, kFirstItems); ++i)
+      rows.first_row[i] = static_cast<uint8_t>(b);
     work.n_full += keys / chunk;
     if (keys % chunk) tails[n_tails++] = b;
     work.max_chunks = std::max(work.max_chunks, (keys + chunk - 1) / chunk);
