@@ -179,7 +179,7 @@ struct UnitPlan {
   bool new_key;                         // this wave also owns the row's new key
 };
 
-// Row, kv head and chunk of a unit (the binary search is done once per unit).
+// Row, kv head and chunk of a unit (the row lookup is done once per unit).
 struct UnitId {
   uint32_t b, j, chunk;
 };
