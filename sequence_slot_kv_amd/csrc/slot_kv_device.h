@@ -21,15 +21,20 @@ __device__ __forceinline__ float load_agent(const float* p) {
 
 // Increment of an epoch-tagged queue or counter word (see kEpochShift): with
 // `raise`, the word is first lifted to this launch's epoch, which restarts
-// its count at zero if an older launch left it; returns the count before the
-// increment.  Both atomics come from one lane in program order, so they
-// reach the word in that order.
-__device__ __forceinline__ uint32_t epoch_increment(uint64_t* word, uint64_t epoch_tag,
+// its count at zero if an older launch left it; returns the word as it was
+// before the increment, whose count epoch_count() gives.  Both atomics come
+// from one lane in program order, so they reach the word in that order.  The
+// caller takes the count where it needs it: the wait for the atomic's return
+// is placed at the first use of the result, and returns are counted in order
+// with the loads, so a use right here would also wait for every load the
+// wave has in flight.
+__device__ __forceinline__ uint64_t epoch_increment(uint64_t* word, uint64_t epoch_tag,
                                                     bool raise) {
   if (raise) (void)__hip_atomic_fetch_max(word, epoch_tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint64_t old = __hip_atomic_fetch_add(word, uint64_t(1), __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-  return static_cast<uint32_t>(old & kCountMask);
+  return __hip_atomic_fetch_add(word, uint64_t(1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t epoch_count(uint64_t word) {
+  return static_cast<uint32_t>(word & kCountMask);
 }
 
 }  // namespace slotkv

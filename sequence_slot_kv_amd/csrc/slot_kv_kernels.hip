@@ -833,7 +833,7 @@ __global__ void __launch_bounds__((kWave * wg_waves<D, G>()))
     // V stages, and a workgroup holds a unit it has not begun only for the
     // end of the current one, so that few units sit reserved when the queue
     // runs dry.
-    uint32_t ticket = 0;
+    uint64_t ticket = 0;  // the queue word before the ask (lane 0 of wave 0)
     // (The workgroup's first ask lifts the queue word to this launch's epoch;
     // its later asks find it there.)
     auto ask_next = [&]() {
@@ -848,7 +848,7 @@ __global__ void __launch_bounds__((kWave * wg_waves<D, G>()))
     // makes before it waits for any other wave.  The raw next queries go out.
     auto take_next = [&]() {
       if (w == 0) {
-        nxt = __builtin_amdgcn_readfirstlane(ticket) + n_blocks;
+        nxt = __builtin_amdgcn_readfirstlane(epoch_count(ticket)) + n_blocks;
         if (lane == 0) __hip_atomic_store(&mbox[par], nxt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       } else {
         nxt = mbox_wait(&mbox[par]);
@@ -927,7 +927,7 @@ __global__ void __launch_bounds__((kWave * wg_waves<D, G>()))
       __builtin_amdgcn_s_waitcnt(0);
     }
     __syncthreads();
-    uint32_t done_prev = 0;
+    uint64_t done_prev = 0;  // the previous partial's counter word before its increment
     if (pending && tid == 0)
       done_prev = epoch_increment(&p.counters[pend_b * p.n_kv_heads + pend_j], p.epoch_tag, true);
     const uint32_t h0 = u.j * G;
@@ -976,7 +976,10 @@ __global__ void __launch_bounds__((kWave * wg_waves<D, G>()))
     if (pending) {  // workgroup-uniform
       // the last workgroup of the previous partial's (row, kv head) merges
       // the row's chunks in order
-      if (tid == 0) sh.last = (done_prev == pend_n - 1) ? 1u : 0u;
+      // (read through readfirstlane here, so that the wait for the atomic's
+      // return stays at this use instead of right after the atomic)
+      const uint32_t done_lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(done_prev));
+      if (tid == 0) sh.last = (epoch_count(done_lo) == pend_n - 1) ? 1u : 0u;
       __syncthreads();
       if (sh.last) merge_row<D, G>(p, pend_b, pend_j, pend_n, tid, kThreads);
     }
@@ -995,9 +998,9 @@ __global__ void __launch_bounds__((kWave * wg_waves<D, G>()))
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
-      const uint32_t done =
+      const uint64_t done =
           epoch_increment(&p.counters[pend_b * p.n_kv_heads + pend_j], p.epoch_tag, true);
-      sh.last = (done == pend_n - 1) ? 1u : 0u;
+      sh.last = (epoch_count(done) == pend_n - 1) ? 1u : 0u;
     }
     __syncthreads();
     if (sh.last) merge_row<D, G>(p, pend_b, pend_j, pend_n, tid, kThreads);
