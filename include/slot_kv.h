@@ -228,8 +228,9 @@ int slot_decode_attn_noalloc(slot_kv *h, uint32_t layer, const float *q,
  *   stream hipStream_t (NULL = the null stream)
  * Requires history rows 0..pos0-1 of the slot to hold the sequence's keys and
  * values.  The handle keeps a scratch buffer (grown on demand, freed with
- * the handle) for the rotated queries, T*n_heads*head_dim floats, and, when
- * the keys are cut into chunks, the chunks' partial results: at most 16,384
+ * the handle) for a per-row table of the query heads' norm, rotation and
+ * scale factors, 2*T*head_dim floats, and, when the keys are cut into
+ * chunks, the chunks' partial results: at most 16,384
  * items of 16*(head_dim+2) floats per launch.  Calls with at most 64 query
  * rows per kv head (T * n_heads / n_kv_heads <= 64) run the split-K kernel;
  * longer ones the tiled kernel, cut into key chunks when it would have

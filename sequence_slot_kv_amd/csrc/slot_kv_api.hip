@@ -711,8 +711,8 @@ int run_prefill(slot_kv* h, uint32_t layer, const float* q, const float* k_new,
   // workgroups share each K/V block between four tiles.
   bool split = true;
   for (const SeqRows& r : seqs) split = split && uint64_t(r.len) * G <= slotkv::kSplitMaxRows;
-  // plan every launch, then size the scratch (rotated queries, then the
-  // split-K partials) for the largest one, before any enqueue
+  // plan every launch, then size the scratch (the rows' query table, then
+  // the key-chunked partials) for the largest one, before any enqueue
   std::vector<PrefillLaunch> plan;
   size_t scratch = 0;
   for (size_t s0 = 0; s0 < seqs.size(); s0 += M) {
@@ -729,8 +729,7 @@ int run_prefill(slot_kv* h, uint32_t layer, const float* q, const float* k_new,
     if (!split)
       pl.split_keys = plan_tiled_chunks(seqs, pl.s0, pl.n, G, L.n_kv_heads, &pl.n_items);
     if (!pl.split_keys) pl.n_items = 0;
-    scratch = std::max(scratch, size_t(pl.rows) * L.n_heads * D +
-                                    size_t(pl.n_items) * 16 * (D + 2));
+    scratch = std::max(scratch, size_t(pl.rows) * 2 * D + size_t(pl.n_items) * 16 * (D + 2));
   }
   int rc = ensure_partials(h, scratch);
   if (rc) return rc;
@@ -740,7 +739,7 @@ int run_prefill(slot_kv* h, uint32_t layer, const float* q, const float* k_new,
   slotkv::PrefillParams& p = a.p;
   p.k_cache = L.k;
   p.v_cache = L.v;
-  p.qs = h->part;
+  p.rope = h->part;
   p.q_norm_w = L.params;
   p.k_norm_w = L.params + D;
   p.inv_freq = L.params + 2 * D;
@@ -778,7 +777,7 @@ int run_prefill(slot_kv* h, uint32_t layer, const float* q, const float* k_new,
     }
     a.s.item_off[n] = items;
     if (split) slotkv::order_split_groups(a.s, n, G, L.n_kv_heads, ck);
-    p.part = ck ? h->part + size_t(pl.rows) * qd : nullptr;
+    p.part = ck ? h->part + size_t(pl.rows) * 2 * D : nullptr;
     p.n_items = items;
     p.split_keys = ck;
     p.n_groups = 0;
@@ -808,10 +807,10 @@ int run_prefill(slot_kv* h, uint32_t layer, const float* q, const float* k_new,
     }
     p.n_seq = n;
     p.n_rows = rows;
-    // prep: one vector per wave while that keeps the workgroups few (up to
-    // about 2048, 8 per CU); more per wave for long calls
+    // prep: one key head per wave while that keeps the workgroups few (up
+    // to about 2048, 8 per CU); more per wave for long calls
     {
-      const uint32_t n_vec4 = (L.n_heads + L.n_kv_heads + 3) / 4;
+      const uint32_t n_vec4 = (L.n_kv_heads + 3) / 4;
       p.prep_vpw = std::max<uint32_t>(1, std::min<uint32_t>(n_vec4, rows * n_vec4 / 2048));
     }
     p.q = q + first_row * qd;

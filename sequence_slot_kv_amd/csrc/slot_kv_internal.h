@@ -240,7 +240,8 @@ struct PrefillParams {
   const float* q;          // [n_rows][n_heads*D]
   const float* k_new;      // [n_rows][kv_dim]
   const float* v_new;      // [n_rows][kv_dim]
-  float* qs;               // [n_rows][n_heads][D] rotated queries times scale*log2(e) (scratch)
+  float* rope;             // [n_rows][D][2] (scratch): per query element d the factors A, B
+                           // of its norm weight, rotation and scale (prep kernel)
   float* part;             // split-K partials (scratch): acc [n_items][16][D], then
                            // (max, sum) [n_items][16][2]
   float* out;              // [n_rows][n_heads*D]

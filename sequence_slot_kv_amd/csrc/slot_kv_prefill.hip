@@ -6,12 +6,14 @@
 // verify of ks[i] consecutive rows for each of n_seqs sequences).
 //
 // Launches on the caller's stream:
-//   prep  one wave per head vector of every token row: RMSNorm and RoPE; a
-//         query head goes to a scratch buffer (times scale*log2(e)), a key
-//         head and its value row go into the slot.
+//   prep  one wave per key head of every token row: RMSNorm and RoPE, and
+//         the key head and its value row go into the slot; per row, a table
+//         of the query heads' norm-weight, rotation and scale factors.
 //   attn  causal attention of every row over its slot's positions
-//         0 .. pos0+t, now all in the cache.  Many query rows meet each key
-//         block, so this is a dense contraction and runs on the matrix cores:
+//         0 .. pos0+t, now all in the cache; each wave first normalises and
+//         rotates its raw query rows with the table.  Many query rows meet
+//         each key block, so this is a dense contraction and runs on the
+//         matrix cores:
 //         v_mfma_f32_16x16x4f32 in its transposed form
 //             S^T = K * Q^T   (16 keys x 16 query rows, summed over head_dim)
 //             O^T += V^T * P^T (16 head_dim values x 16 rows, summed over keys)
@@ -47,26 +49,27 @@ __device__ __forceinline__ uint32_t seq_of_row(const PrefillArgs& a, uint32_t ro
   return last_le(a.p.n_seq, row, [&](uint32_t i) { return a.s.row_off[i]; });
 }
 
-// A workgroup takes 4 * prep_vpw head vectors of a token row (the row's
-// n_heads query heads, then its n_kv_heads key heads), wave w the vectors
+// A workgroup takes 4 * prep_vpw key heads of a token row, wave w the heads
 // w, w + 4, ...; prep_vpw is 1 for calls of a few hundred rows, so that they
-// spread over the whole chip, and larger for long ones.  The workgroup first puts
-// the cos / sin of the row's D/2 angles in LDS.  Lane l holds elements
-// l*EPL .. l*EPL+EPL-1 of the vector; the RoPE partner d +- D/2 of an
-// element sits in lane l ^ 32 with the same angle, and with interleaved
-// pairs the partner d ^ 1 is the neighbouring element of the lane (lane
-// l ^ 1 when a lane holds one) and the angle that of d / 2.
+// spread over the whole chip, and larger for long ones.  The workgroup first
+// puts the cos / sin of the row's D/2 angles in LDS, and the row's first
+// workgroup also writes the row's entry of the query table, from which the
+// attention kernels normalise and rotate the row's query heads.  Lane l
+// holds elements l*EPL .. l*EPL+EPL-1 of the vector; the RoPE partner
+// d +- D/2 of an element sits in lane l ^ 32 with the same angle, and with
+// interleaved pairs the partner d ^ 1 is the neighbouring element of the
+// lane (lane l ^ 1 when a lane holds one) and the angle that of d / 2.
 template <int D>
 __global__ void __launch_bounds__(kWave * kPrepWaves) prefill_prep_kernel(const PrefillArgs a) {
   constexpr int EPL = D / kWave;
   __shared__ float cs[D / 2], sn[D / 2];
   if (a.magic != kArgsMagic) return;  // argument block not delivered whole
   const PrefillParams& p = a.p;
-  const uint32_t n_vec = p.n_heads + p.n_kv_heads;
   const uint32_t per_wg = kPrepWaves * p.prep_vpw;
-  const uint32_t per_row = (n_vec + per_wg - 1) / per_wg;
+  const uint32_t per_row = (p.n_kv_heads + per_wg - 1) / per_wg;
   const uint32_t row = blockIdx.x / per_row;  // < n_rows
-  const uint32_t v0 = (blockIdx.x - row * per_row) * per_wg + threadIdx.x / kWave;
+  const uint32_t part = blockIdx.x - row * per_row;
+  const uint32_t v0 = part * per_wg + threadIdx.x / kWave;
   const uint32_t i = seq_of_row(a, row);
   const uint32_t t = row - a.s.row_off[i];
   const uint32_t pos = a.s.pos0[i] + t;
@@ -79,16 +82,23 @@ __global__ void __launch_bounds__(kWave * kPrepWaves) prefill_prep_kernel(const 
     cs[e] = c_;
   }
   __syncthreads();
-  const uint32_t lane = threadIdx.x % kWave;
-  const uint64_t at_row = a.s.slot[i] * p.slot_stride + static_cast<uint64_t>(pos) * p.kv_dim;
   const float one = (p.flags & SLOT_KV_FLAG_NORM_ONE_PLUS_W) ? 1.f : 0.f;
   const bool inter = p.flags & SLOT_KV_FLAG_ROPE_INTERLEAVED;  // uniform
-  for (uint32_t v = v0; v < min(v0 + per_wg, n_vec); v += kPrepWaves) {  // wave-uniform
-    const bool is_q = v < p.n_heads;  // wave-uniform
-    const uint32_t kvh = v - p.n_heads;
-    const float* src = is_q ? p.q + (static_cast<size_t>(row) * p.n_heads + v) * D
-                            : p.k_new + static_cast<size_t>(row) * p.kv_dim + kvh * D;
-    const float* w = is_q ? p.q_norm_w : p.k_norm_w;
+  if (part == 0) {  // workgroup-uniform: the row's query rotation table
+    float2* tab = reinterpret_cast<float2*>(p.rope) + static_cast<size_t>(row) * D;
+    for (uint32_t d = threadIdx.x; d < D; d += kWave * kPrepWaves) {
+      const uint32_t k = inter ? d / 2 : d % (D / 2);            // the angle of d
+      const uint32_t pd = inter ? d ^ 1u : (d + D / 2) % D;       // its partner
+      const bool first = inter ? (d & 1u) == 0 : d < D / 2;
+      const float wa = p.qk_scale_log2 * (one + p.q_norm_w[d]);
+      const float wb = p.qk_scale_log2 * (one + p.q_norm_w[pd]);
+      tab[d] = make_float2(wa * cs[k], first ? -wb * sn[k] : wb * sn[k]);
+    }
+  }
+  const uint32_t lane = threadIdx.x % kWave;
+  const uint64_t at_row = a.s.slot[i] * p.slot_stride + static_cast<uint64_t>(pos) * p.kv_dim;
+  for (uint32_t kvh = v0; kvh < min(v0 + per_wg, p.n_kv_heads); kvh += kPrepWaves) {  // wave-uniform
+    const float* src = p.k_new + static_cast<size_t>(row) * p.kv_dim + kvh * D;
     float x[EPL];
     float ss = 0.f;
 #pragma unroll
@@ -100,7 +110,7 @@ __global__ void __launch_bounds__(kWave * kPrepWaves) prefill_prep_kernel(const 
     const float rn = 1.0f / sqrtf(ss * (1.0f / D) + p.eps);
     float xn[EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) xn[e] = x[e] * rn * (one + w[lane * EPL + e]);
+    for (int e = 0; e < EPL; ++e) xn[e] = x[e] * rn * (one + p.k_norm_w[lane * EPL + e]);
     float y[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
@@ -119,29 +129,132 @@ __global__ void __launch_bounds__(kWave * kPrepWaves) prefill_prep_kernel(const 
       }
       y[e] = first ? xn[e] * cs[k] - partner * sn[k] : xn[e] * cs[k] + partner * sn[k];
     }
-    if (is_q) {
-      float* dst = p.qs + (static_cast<size_t>(row) * p.n_heads + v) * D + lane * EPL;
+    const uint64_t at = at_row + kvh * D + lane * EPL;
+    const float* vsrc = p.v_new + static_cast<size_t>(row) * p.kv_dim + kvh * D + lane * EPL;
+    float vw[EPL];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) dst[e] = y[e] * p.qk_scale_log2;
+    for (int e = 0; e < EPL; ++e) vw[e] = vsrc[e];
+    if (p.flags & SLOT_KV_FLAG_V_NORM) {  // uniform: weightless RMSNorm of the value
+      float sv = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) sv += vw[e] * vw[e];
+      const float rv = 1.0f / sqrtf(wave_sum(sv) * (1.0f / D) + p.eps);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) vw[e] *= rv;
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      p.k_cache[at + e] = y[e];
+      p.v_cache[at + e] = vw[e];
+    }
+  }
+}
+
+// The query heads of a row are normalised and rotated by the attention waves
+// that use them.  With xn = x * r * (one + w) the normalised query (r the
+// reciprocal RMS of the head vector x) and p(d) the RoPE partner of element d
+// at the angle a(d), the rotated, scaled element is
+//   q[d] = s * (xn[d] cos a(d) -+ xn[p(d)] sin a(d))
+//        = r * (x[d] * A[d] + x[p(d)] * B[d]),
+//   A[d] = s (one + w[d]) cos a(d),  B[d] = -+ s (one + w[p(d)]) sin a(d),
+// minus for the first element of a pair, s = scale * log2(e) (so that the
+// scores come out in log2 units).  A and B depend on the row's position and
+// the weights only: the prep kernel writes them per row ([row][d] (A, B)), and
+// a lane then needs the raw query, its elements' (A, B) and the partners.
+// The sum of squares of a query row is spread over lanes l, l ^ 16, l ^ 32 and
+// l ^ 48 in both layouts below.
+__device__ __forceinline__ float row_rms(const PrefillParams& p, float ss, int D) {
+  ss += __shfl_xor(ss, 16);
+  ss += __shfl_xor(ss, 32);
+  return 1.0f / sqrtf(ss * (1.0f / static_cast<float>(D)) + p.eps);
+}
+
+// Tiled layout: lane group g holds d = (D/4)*g + i, i < D/4.  With
+// rotate-half pairs the partner d +- D/2 is element i of lane l ^ 32; with
+// interleaved pairs the partner d ^ 1 is element i ^ 1 of the lane.
+template <int D>
+__device__ __forceinline__ void tiled_query(const PrefillParams& p, uint32_t row, uint32_t h,
+                                            uint32_t g, float (&qv)[D / 4]) {
+  constexpr int DQ = D / 4;
+  const float* src = p.q + (static_cast<size_t>(row) * p.n_heads + h) * D + DQ * g;
+  const f4* tab = reinterpret_cast<const f4*>(p.rope + (static_cast<size_t>(row) * D + DQ * g) * 2);
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < DQ; i += 4) {
+    const f4 v = *reinterpret_cast<const f4*>(src + i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qv[i + e] = v[e];
+      ss += v[e] * v[e];
+    }
+  }
+  const bool inter = p.flags & SLOT_KV_FLAG_ROPE_INTERLEAVED;  // uniform
+  const float rn = row_rms(p, ss, D);
+  // the table in two halves (the registers of a whole one would spill)
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    f4 ab[DQ / 4];  // (A, B) of elements 2k and 2k + 1 of this half
+#pragma unroll
+    for (int k = 0; k < DQ / 4; ++k) ab[k] = tab[hf * DQ / 4 + k];
+    if (inter) {
+#pragma unroll
+      for (int k = 0; k < DQ / 4; ++k) {
+        const int i = hf * DQ / 2 + 2 * k;
+        const float x0 = qv[i], x1 = qv[i + 1];
+        qv[i] = rn * (x0 * ab[k][0] + x1 * ab[k][1]);
+        qv[i + 1] = rn * (x1 * ab[k][2] + x0 * ab[k][3]);
+      }
     } else {
-      const uint64_t at = at_row + kvh * D + lane * EPL;
-      const float* vsrc = p.v_new + static_cast<size_t>(row) * p.kv_dim + kvh * D + lane * EPL;
-      float vw[EPL];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) vw[e] = vsrc[e];
-      if (p.flags & SLOT_KV_FLAG_V_NORM) {  // uniform: weightless RMSNorm of the value
-        float sv = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) sv += vw[e] * vw[e];
-        const float rv = 1.0f / sqrtf(wave_sum(sv) * (1.0f / D) + p.eps);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) vw[e] *= rv;
+      for (int k = 0; k < DQ / 4; ++k) {
+        const int i = hf * DQ / 2 + 2 * k;
+        const float x0 = qv[i], x1 = qv[i + 1];
+        const float p0 = __shfl_xor(x0, 32), p1 = __shfl_xor(x1, 32);
+        qv[i] = rn * (x0 * ab[k][0] + p0 * ab[k][1]);
+        qv[i + 1] = rn * (x1 * ab[k][2] + p1 * ab[k][3]);
       }
+    }
+  }
+}
+
+// Split-K layout: lane group g holds d = 16v + 4g + e as element 4v + e
+// (v < D/16, e < 4).  With rotate-half pairs the partner d +- D/2 is element
+// 4(v +- D/32) + e of the same lane; with interleaved pairs element
+// 4v + (e ^ 1).
+template <int D>
+__device__ __forceinline__ void split_query(const PrefillParams& p, uint32_t row, uint32_t h,
+                                            uint32_t g, float (&qv)[D / 4]) {
+  constexpr int NK = D / 16;
+  const float* src = p.q + (static_cast<size_t>(row) * p.n_heads + h) * D + 4 * g;
+  const f4* tab = reinterpret_cast<const f4*>(p.rope + (static_cast<size_t>(row) * D + 4 * g) * 2);
+  f4 ab[2 * NK];  // (A, B) of elements 4v + 2m and 4v + 2m + 1 at 2v + m
+  float ss = 0.f;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        p.k_cache[at + e] = y[e];
-        p.v_cache[at + e] = vw[e];
-      }
+  for (int v = 0; v < NK; ++v) {
+    const f4 x = *reinterpret_cast<const f4*>(src + 16 * v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qv[4 * v + e] = x[e];
+      ss += x[e] * x[e];
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < NK; ++v) {
+    ab[2 * v] = tab[8 * v];
+    ab[2 * v + 1] = tab[8 * v + 1];
+  }
+  const float rn = row_rms(p, ss, D);
+  float x[D / 4];
+#pragma unroll
+  for (int e = 0; e < D / 4; ++e) x[e] = qv[e];
+  const bool inter = p.flags & SLOT_KV_FLAG_ROPE_INTERLEAVED;  // uniform
+#pragma unroll
+  for (int v = 0; v < NK; ++v) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float partner = inter ? x[4 * v + (e ^ 1)] : x[(4 * v + e + D / 8) % (D / 4)];
+      const f4 t = ab[2 * v + e / 2];
+      qv[4 * v + e] = rn * (x[4 * v + e] * t[2 * (e % 2)] + partner * t[2 * (e % 2) + 1]);
     }
   }
 }
@@ -214,18 +327,7 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) prefill_attn_kernel(const 
   const uint32_t tq = min(t, T - 1);  // rows past the last token compute on it, unused
   const uint32_t row_pos = pos0 + tq;
 
-  float qv[DQ];
-  {
-    const float* qsrc = p.qs + (static_cast<size_t>(row0 + tq) * p.n_heads + h) * D + DQ * g;
-#pragma unroll
-    for (int i = 0; i < DQ; i += 4) {
-      const f4 v = *reinterpret_cast<const f4*>(qsrc + i);
-      qv[i] = v[0];
-      qv[i + 1] = v[1];
-      qv[i + 2] = v[2];
-      qv[i + 3] = v[3];
-    }
-  }
+  float qv[DQ];  // the wave's query rows, prepared after the first fetch
   const uint64_t slot_base = a.s.slot[sq] * p.slot_stride;
   const float* kbase = p.k_cache + slot_base + j * D;
   const float* vbase = p.v_cache + slot_base + j * D;
@@ -324,15 +426,17 @@ __global__ void __launch_bounds__(kWave * kAttnWaves) prefill_attn_kernel(const 
       tile < n_tiles && wave_keys > k_lo ? min(n_blk, (wave_keys - k_lo + 15) / 16) : 0;
   fetch(stk, kbase, k_lo);
   fetch(stv, vbase, k_lo);
+  tiled_query<D>(p, row0 + tq, h, g, qv);
   stage(sh.k[0], stk);
   stage(sh.v[0], stv);
   if (n_blk > 1) {
     fetch(stk, kbase, k_lo + 16);
     stage(sh.k[1], stk);
   }
-  // The query registers are read in every pass: their loads land here, so
-  // that no wait inside the loop (where a fetch may or may not have been
-  // issued) has to wait for the loop's fetches as well.
+  // The query registers are read in every pass: their loads land (and the
+  // norm and rotation are applied) here, so that no wait inside the loop
+  // (where a fetch may or may not have been issued) has to wait for the
+  // loop's fetches as well.
 #pragma unroll
   for (int i = 0; i < DQ; ++i) asm volatile("" ::"v"(qv[i]));
   __syncthreads();
@@ -480,15 +584,7 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_eu<D>()))) split_attn_kernel(
   const uint32_t row_pos = pos0 + tq;
 
   float qv[DQ];
-  {
-    const float* qsrc = p.qs + (static_cast<size_t>(row0 + tq) * p.n_heads + h) * D + 4 * g;
-#pragma unroll
-    for (int v = 0; v < NK; ++v) {
-      const f4 x = *reinterpret_cast<const f4*>(qsrc + 16 * v);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) qv[4 * v + e] = x[e];
-    }
-  }
+  split_query<D>(p, row0 + tq, h, g, qv);
   const uint64_t slot_base = a.s.slot[sq] * p.slot_stride;
   const float* kbase = p.k_cache + slot_base + j * D;
   const float* vbase = p.v_cache + slot_base + j * D;
@@ -600,7 +696,8 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_eu<D>()))) split_attn_kernel(
     load_k(kb_, 1);
     load_v(vb, 1);
   }
-  // The query registers are read in every block: their loads land here.
+  // The query registers are read in every block: their loads land (and the
+  // norm and rotation are applied) here.
   // Left to the loop, the wait for them would sit where the loads in flight
   // are those of the next blocks, and would wait for those as well.
 #pragma unroll
@@ -794,7 +891,7 @@ template <int D>
 hipError_t launch_d(const PrefillArgs& a, uint32_t G, bool split, hipStream_t s,
                     hipEvent_t before, hipEvent_t after) {
   const uint32_t per_wg = kPrepWaves * a.p.prep_vpw;
-  const uint32_t per_row = (a.p.n_heads + a.p.n_kv_heads + per_wg - 1) / per_wg;
+  const uint32_t per_row = (a.p.n_kv_heads + per_wg - 1) / per_wg;
   hipLaunchKernelGGL((prefill_prep_kernel<D>), dim3(a.p.n_rows * per_row), dim3(kWave * kPrepWaves), 0,
                      s, a);
   hipError_t e = hipGetLastError();
