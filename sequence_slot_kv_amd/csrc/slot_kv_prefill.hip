@@ -583,8 +583,7 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_eu<D>()))) split_attn_kernel(
   const uint32_t tq = t < T ? t : T - 1;  // rows past the last token compute on it, unused
   const uint32_t row_pos = pos0 + tq;
 
-  float qv[DQ];
-  split_query<D>(p, row0 + tq, h, g, qv);
+  float qv[DQ];  // the wave's query rows, prepared with the first blocks in flight
   const uint64_t slot_base = a.s.slot[sq] * p.slot_stride;
   const float* kbase = p.k_cache + slot_base + j * D;
   const float* vbase = p.v_cache + slot_base + j * D;
@@ -696,6 +695,7 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_eu<D>()))) split_attn_kernel(
     load_k(kb_, 1);
     load_v(vb, 1);
   }
+  split_query<D>(p, row0 + tq, h, g, qv);  // with the first blocks in flight
   // The query registers are read in every block: their loads land (and the
   // norm and rotation are applied) here.
   // Left to the loop, the wait for them would sit where the loads in flight
