@@ -91,3 +91,35 @@ def test_prefill_and_verify_with_flags(flags, H, Hkv, D):
     for s_, p0, k in zip(slots, pos0, ks):
         assert_close(gk[s_, p0:p0 + k], ck[s_, p0:p0 + k], "written K")
         assert_close(gv[s_, p0:p0 + k], cv[s_, p0:p0 + k], "written V")
+
+
+@pytest.mark.parametrize("H,Hkv,D", [(8, 4, 256), (16, 4, 128)])
+def test_prefill_and_verify_flags_far_positions(H, Hkv, D):
+    """All three flags at positions past 20,000, where the RoPE angles are
+    large: a key-chunked tiled prefill (more than 64 query rows per kv head)
+    and a split-K verify, against the oracle."""
+    flags = oracle.V_NORM | oracle.ROPE_INTERLEAVED | oracle.NORM_ONE_PLUS_W
+    rng = np.random.default_rng(70 + D)
+    n_slots, slot_ctx = 3, 24576
+    L = _layer(rng, H, Hkv, D, flags, sinks=True)
+    ck, cv = _cache(rng, n_slots, slot_ctx, L.kv_dim)
+    slots, pos0, ks = [1, 2, 0], [slot_ctx - 48, 20011, 23999], [48, 4, 3]
+    rows = sum(ks)
+    q = rng.standard_normal((rows, H * D), dtype=np.float32)
+    kn = rng.standard_normal((rows, L.kv_dim), dtype=np.float32)
+    vn = rng.standard_normal((rows, L.kv_dim), dtype=np.float32)
+    kv = _handle(n_slots, slot_ctx, L, ck, cv)
+    q_d, k_d, v_d = (torch.from_numpy(x).cuda() for x in (q, kn, vn))
+    out_p = kv.prefill_attn(0, q_d[:ks[0]], k_d[:ks[0]], v_d[:ks[0]], slots[0], pos0[0]).cpu().numpy()
+    out_v = kv.verify_attn(0, q_d[ks[0]:], k_d[ks[0]:], v_d[ks[0]:], slots[1:], pos0[1:],
+                           ks[1:]).cpu().numpy()
+    written = [(kv.read_rows(0, s_, p0, k)) for s_, p0, k in zip(slots, pos0, ks)]
+    written = [(a.cpu().numpy(), c.cpu().numpy()) for a, c in written]
+    kv.close()
+    rc, ref = oracle.verify(L, ck, cv, q, kn, vn, slots, pos0, ks)
+    assert rc == 0
+    assert_close(out_p, ref[:ks[0]], f"prefill out, far positions, D={D}")
+    assert_close(out_v, ref[ks[0]:], f"verify out, far positions, D={D}")
+    for (gk, gv), s_, p0, k in zip(written, slots, pos0, ks):
+        assert_close(gk, ck[s_, p0:p0 + k], "written K")
+        assert_close(gv, cv[s_, p0:p0 + k], "written V")
