@@ -46,7 +46,17 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // The sequence holding launch row `row`: the last i with row_off[i] <= row.
 __device__ __forceinline__ uint32_t seq_of_row(const PrefillArgs& a, uint32_t row) {
-  return last_le(a.p.n_seq, row, [&](uint32_t i) { return a.s.row_off[i]; });
+  // row is wave-uniform.  Lane l tests entries l and 64 + l (both loads in
+  // flight together, always inside the table); the count of entries below
+  // n_seq at or below row (row_off rises from row_off[0] = 0) is one past
+  // the sequence.  One round trip instead of a chain of dependent loads.
+  static_assert(kMaxSeqPerLaunch <= 2 * kWave, "two entries per lane");
+  const uint32_t lane = threadIdx.x % kWave;
+  const uint32_t n = a.p.n_seq;
+  const uint32_t r0 = a.s.row_off[lane], r1 = a.s.row_off[kWave + lane];
+  const uint32_t cnt = __popcll(__ballot(lane < n && r0 <= row)) +
+                       __popcll(__ballot(kWave + lane < n && r1 <= row));
+  return __builtin_amdgcn_readfirstlane(cnt - 1);
 }
 
 // A workgroup takes 4 * prep_vpw key heads of a token row, wave w the heads
